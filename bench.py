@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark of the W1.58A8 BitLinear forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens M]
+
+A step is one pass of the per-token hot path over one batch of synthetic
+input: per-token absmax int8 quantization, load + unpack of the packed
+ternary weights, the int32 contraction, the float rescale (and ReLU^2 where
+the workload has it) for every linear of the workload.  Weights are quantized
+and packed once, before timing (offline, as the packed form is what a model
+stores); that offline pass is timed separately and reported as
+``offline_weight_quant_ms``.
+
+Default workload: the decode GEMV pair at M=1 (up 2560->6912, ReLU^2, down
+6912->2560, bf16 activations).  Its 8.85 MB of packed weights would sit in
+the 256 MB Infinity Cache, so steps rotate over enough weight copies that
+the weights stream from HBM.
+
+The K timed steps run as one HIP graph replay on torch's stream, bracketed
+by synchronizations; the JSON line carries whole-step throughput (``value``),
+the roofline of the dominant kernel (timed with HIP events around a graph of
+back-to-back launches of that kernel alone), and the CPU oracle timed on a
+bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("ternary GEMV HBM GB/s (% of peak), µs/token for all linears; "
+          "prefill int8 TOPS")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode_gemv_pair_m1")
+    p.add_argument("--tokens", type=int, default=None, help="M for multi-M workloads")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="time budget of the CPU oracle sample")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--kernel-launches", type=int, default=400,
+                   help="launches of the dominant kernel timed for the roofline")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Workload runners: allocate everything up front; step(i) only launches.
+# ---------------------------------------------------------------------------
+class Linear:
+    def __init__(self, bl, torch, dev, N, K, M, x_dtype, seed, sparse, copies):
+        self.N, self.K, self.M = N, K, M
+        gen = torch.Generator(device=dev)
+        self.packed, self.gamma = [], []
+        t0 = time.perf_counter()
+        for c in range(copies):
+            gen.manual_seed(seed * 131 + c)
+            W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+            if sparse > 0:
+                mask = torch.rand((N, K), generator=gen, device=dev) < sparse
+                W = torch.where(mask, W * 1e-3, W)
+            p, g = bl.quantize_weights(W)
+            self.packed.append(p)
+            self.gamma.append(g)
+            del W
+        torch.cuda.synchronize()
+        self.quant_s = time.perf_counter() - t0
+        gen.manual_seed(seed * 131 + 7777)
+        X = torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32)
+        self.X = X.to(x_dtype) if x_dtype is not None else X
+        self.Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = bl.workspace_bytes(M, K, N)
+        self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev) if ws > 0 else None
+
+    def bytes(self):
+        """Algorithmic bytes of one forward: packed W + X in + Y out + gamma."""
+        return (self.N * self.K // 4 + self.X.numel() * self.X.element_size()
+                + self.Y.numel() * 4 + 4)
+
+    def ops(self):
+        return 2 * self.M * self.N * self.K
+
+
+def build_runner(args, bl, torch, wl, dev):
+    wk = wl.WORKLOADS[args.workload]
+    M = args.tokens if args.tokens is not None else wk.tokens[0]
+    if M not in wk.tokens:
+        log(f"note: M={M} is not one of the workload's token counts {wk.tokens}")
+    x_dtype = torch.bfloat16 if wk.x_kind.endswith("bf16") else None
+    packed_per_step = wk.weights_per_step // 4
+    # weight copies: enough that the bytes cycled through exceed 2x the MALL
+    copies = max(1, -(-2 * MALL_BYTES // packed_per_step))
+    copies = min(copies, 64)
+    lins = []
+    for layer, li, shape in wl.step_linears(wk):
+        lins.append(Linear(bl, torch, dev, shape.N, shape.K, M, x_dtype,
+                           wl.weight_seed(wk.key, layer, li), wk.weight_sparse_frac, copies))
+    steps_in_chain = None
+    if wk.chain_relu2:
+        # up (ReLU^2) feeds down: down's input is up's float output
+        up, down = lins
+        down.X = up.Y
+
+    def step(i):
+        c = i % copies
+        if wk.chain_relu2:
+            up, down = lins
+            bl.forward(up.X, up.packed[c], up.gamma[c], up.N, epilogue="relu2", out=up.Y,
+                       workspace=up.ws)
+            bl.forward(down.X, down.packed[c], down.gamma[c], down.N, out=down.Y,
+                       workspace=down.ws)
+        else:
+            for lin in lins:
+                bl.forward(lin.X, lin.packed[c], lin.gamma[c], lin.N, out=lin.Y,
+                           workspace=lin.ws)
+
+    return wk, M, lins, copies, step
+
+
+def capture(torch, fn, count):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)  # one eager pass to settle any lazy initialisation
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(i)
+    return g
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ---------------------------------------------------------------------------
+def cpu_baseline(args, wk, M, lins_shapes, metric_kind, budget_s):
+    import numpy as np
+
+    import oracle
+    from w1_a8_matmul_amd import workloads as wl
+
+    orc = oracle.get()
+    threads = orc.max_threads()
+    rng_seed = 424242
+    # one layer's linears (the sample); weights quantized by the oracle itself
+    shapes = list(wk.linears)
+    Ms = M if metric_kind != "tops" else min(M, 16)  # prefill: a sample of token rows
+    prepared = []
+    for li, lin in enumerate(shapes):
+        W = wl.gen_weight(rng_seed + li, lin.N, lin.K, wk.weight_sparse_frac)
+        _, gc, qw = orc.quantize_weights(W)
+        del W
+        X, is_bf16 = wl.gen_acts(rng_seed + 100 + li, Ms, lin.K, wk.x_kind)
+        prepared.append((lin, qw, gc, X, is_bf16))
+
+    def one_pass():
+        if wk.chain_relu2:
+            (lu, qu, gu, Xu, bu), (ld, qd, gd, _, _) = prepared
+            y, *_ = orc.forward(Xu, qu, gu, bf16=bu)
+            h = orc.relu2(y)
+            orc.forward(h, qd, gd)
+        else:
+            for lin, qw, gc, X, is_bf16 in prepared:
+                orc.forward(X, qw, gc, bf16=is_bf16)
+
+    one_pass()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        one_pass()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 100000:
+            break
+    per_pass = el / n
+    layer_bytes = sum(lin.N * lin.K // 4 + Ms * lin.K * (2 if is_bf16 else 4) + Ms * lin.N * 4 + 4
+                      for lin, _, _, _, is_bf16 in prepared)
+    layer_ops = sum(2 * Ms * lin.N * lin.K for lin, *_ in prepared)
+    if metric_kind == "tops":
+        value, unit = layer_ops / per_pass / 1e12, "TOPS"
+    else:
+        value, unit = layer_bytes / per_pass / 1e9, "GB/s"
+    sample = (f"{n} passes over one layer's linears ({', '.join(f'{l.K}->{l.N}' for l in shapes)})"
+              f" at M={Ms}, {el:.1f} s; oracle on unpacked int8 weights, OpenMP over outputs")
+    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": sample, "us_per_layer_pass": round(per_pass * 1e6, 1)}
+
+
+def traffic_from_profile(kernel_src_hash, kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on another version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_sha1") != kernel_src_hash:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def source_hash(names):
+    h = hashlib.sha1()
+    for n in names:
+        with open(os.path.join(ROOT, "w1_a8_matmul_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; "
+                                   f"--gpus {args.gpus} is not supported (the forward is "
+                                   "single-GPU; see the sharding note in the design notes)"}))
+        sys.exit(2)
+    import torch
+
+    from w1_a8_matmul_amd import bitlinear as bl
+    from w1_a8_matmul_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    bl.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wk, M, lins, copies, step = build_runner(args, bl, torch, wl, dev)
+    quant_s = sum(l.quant_s for l in lins)
+    n_weights = sum(l.N * l.K for l in lins) * copies
+    log(f"workload {wk.key} M={M}: {len(lins)} linears, {copies} weight copies, "
+        f"offline quantization {quant_s*1e3:.1f} ms for {n_weights/1e6:.1f} M weights")
+
+    bytes_step = sum(l.bytes() for l in lins)
+    if wk.chain_relu2:
+        bytes_step -= lins[1].X.numel() * 4 * 0  # h is counted as down's input; up's output counted too
+    ops_step = sum(l.ops() for l in lins)
+    metric_kind = "tops" if M >= 128 else "hbm"
+
+    # warmup
+    if args.warmup > 0:
+        gw = capture(torch, step, args.warmup)
+        gw.replay()
+        torch.cuda.synchronize()
+        log(f"warmup {args.warmup} steps done")
+    g = capture(torch, step, args.steps)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed {args.steps} steps: wall {wall*1e3:.3f} ms, events {gpu_ms:.3f} ms")
+
+    # Dominant kernel: the linear with the most packed bytes; its launches
+    # alone, back to back, in a graph bracketed by HIP events.
+    dom = max(lins, key=lambda l: l.N * l.K)
+    epi = "relu2" if (wk.chain_relu2 and dom is lins[0]) else None
+    L = args.kernel_launches
+    dcopies = max(1, min(len(dom.packed), L))
+
+    def dom_step(i):
+        c = i % dcopies
+        bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
+                   workspace=dom.ws)
+
+    gd = capture(torch, dom_step, L)
+    gd.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gd.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    launches_per_call = 2 if dom.ws is not None else 1  # quantizer + GEMM on the large-M path
+    dom_us = e0.elapsed_time(e1) * 1e3 / L
+    if metric_kind == "tops":
+        achieved = dom.ops() / (dom_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+        kernel_key = f"gemm_q_{dom.K}x{dom.N}_m{M}"
+        src = source_hash(["gemm.hip", "common.hpp"])
+    else:
+        achieved = dom.bytes() / (dom_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        kernel_key = f"gemv_{dom.K}x{dom.N}_m{M}"
+        src = source_hash(["gemv.hip", "quant_row.hpp", "common.hpp"])
+    roof["traffic"] = traffic_from_profile(src, kernel_key)
+    roof["kernel"] = kernel_key
+    roof["kernel_us"] = round(dom_us, 3)
+    roof["launches_per_forward"] = launches_per_call
+    log(f"dominant forward {kernel_key}: {dom_us:.3f} us per call")
+
+    step_s = ms_per_step / 1e3
+    if metric_kind == "tops":
+        value, unit = ops_step / step_s / 1e12, "TOPS"
+    else:
+        value, unit = bytes_step / step_s / 1e9, "GB/s"
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args, wk, M, wk.linears, metric_kind, args.cpu_seconds)
+        log(f"cpu oracle: {cpu}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": wk.key,
+            "description": wk.description,
+            "tokens": M,
+            "linears_per_step": len(lins),
+            "weight_copies_rotated": copies,
+            "bytes_per_step": bytes_step,
+            "ops_per_step": ops_step,
+            "us_per_token": round(ms_per_step * 1e3 / M, 3),
+            "gpu_event_ms_per_step": round(gpu_ms / args.steps, 6),
+            "offline_weight_quant_ms": round(quant_s * 1e3 / copies, 3),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

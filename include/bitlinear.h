@@ -1,0 +1,177 @@
+/*
+ * bitlinear.h -- C ABI of the W1.58A8 BitLinear forward for MI355X (gfx950).
+ *
+ * What is computed (sources: "BitNet b1.58 2B4T Technical Report" paper card,
+ * ai-papers.xuzou.cn, sections "Method Adaptation" and "Compute Setup";
+ * fishai news digest on BitNet b1.58 2B4T, news.fishai.com.cn/news/3455510,
+ * the BitLinear items; dignews.cc article on BitNet b1.58 2B4T, section 2):
+ * a BitLinear layer stands in for a dense linear layer y = x W^T without
+ * bias.  Its weights are mapped to {-1, 0, +1} by an absmean scale and
+ * stored four to a byte in HBM; its input is mapped per token to 8-bit
+ * integers by an absmax scale; the product runs on integers and is scaled
+ * back.  The pages give no formulas; the readings this library implements:
+ *
+ *   gamma    = mean |W| over the whole [N][K] matrix, summed in double (each
+ *              row in column order, then the rows in row order) and rounded
+ *              once to float; gamma_c = max(gamma, 1e-5f).
+ *   q_w      = clamp(rint(W / gamma_c), -1, 1) (float division, ties to even).
+ *   per token m: a = max_k |x[m,k]|, a_c = max(a, 1e-5f), qs = 127.0f / a_c,
+ *              q_x = clamp(rint(x * qs), -127, 127), s_x[m] = a_c / 127.0f.
+ *   acc      = sum_k q_x[m,k] * q_w[n,k], exact in int32.
+ *   y[m,n]   = ((float)acc * s_x[m]) * gamma_c, two float roundings in that
+ *              order (no fused multiply-add).
+ *   ReLU^2   (optional epilogue) y <- max(y, 0)^2.
+ *
+ * All of it is reproducible bit for bit: integer work is exact and the float
+ * steps are single IEEE operations in a fixed order.
+ *
+ * Layouts.  Row-major, contiguous.  W and q_w are [N][K] (like a linear
+ * layer's weight), X is [M][K], Y is [M][N].  Packed weights: the matrix is
+ * cut into tiles of 16 rows x 256 columns; each tile is 1024 bytes; tiles
+ * are stored row-tile major, then by column block.  Inside a tile, the
+ * 16-byte chunk c (0..63) holds row (c mod 16) of the tile and its columns
+ * 64*(c div 16) .. 64*(c div 16)+63 of the block; inside a chunk, the
+ * column offset t (0..63) is stored in little-endian 32-bit word (t div 16),
+ * byte (t mod 4), bits 2f..2f+1 with f = (t mod 16) div 4, as the code
+ * q_w + 1 (0, 1 or 2; 3 never occurs).  So one 32-bit word shifted right by
+ * 2f and masked with 0x03030303 gives the codes of four consecutive columns,
+ * one per byte, and 64 lanes that each load 16 bytes read one whole tile.
+ *
+ * Conventions for every call below.
+ *   - Tensor pointers are device pointers (hipMalloc'ed or torch CUDA/HIP
+ *     tensors) owned by the caller; the library allocates no device memory
+ *     and keeps no pointer after a call returns.
+ *   - Every tensor pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it and return; no call synchronizes.  Results are ready when
+ *     the stream reaches them.
+ *   - Arguments are checked before anything is enqueued; a failed check
+ *     returns an error code and enqueues nothing.  A launch failure returns
+ *     BITLINEAR_ERR_HIP.  Device faults surface at the caller's next
+ *     synchronization.  bitlinear_last_error() gives a thread-local message
+ *     for the last failing call on that thread.
+ *   - Inputs must be finite; NaN or Inf input gives unspecified (but memory
+ *     safe) results.
+ *   - Shapes: N % 16 == 0 and K % 256 == 0 (the packed tile); M >= 0 and
+ *     M == 0 is a no-op that returns BITLINEAR_OK; N, K >= 1 otherwise.
+ *     |acc| <= 127*K must fit int32: K <= 16,908,288 (checked).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITLINEAR_ABI_VERSION 1
+
+typedef enum {
+  BITLINEAR_OK = 0,
+  BITLINEAR_ERR_NULL = 1,      /* a required pointer is NULL */
+  BITLINEAR_ERR_SHAPE = 2,     /* a size is negative or breaks N%16, K%256 */
+  BITLINEAR_ERR_ALIGN = 3,     /* a tensor pointer is not 16-byte aligned */
+  BITLINEAR_ERR_DTYPE = 4,     /* unknown bitlinear_dtype */
+  BITLINEAR_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required */
+  BITLINEAR_ERR_HIP = 6,       /* the HIP runtime reported an error */
+  BITLINEAR_ERR_ARG = 7        /* another bad argument (e.g. epilogue) */
+} bitlinear_status;
+
+typedef enum {
+  BITLINEAR_F32 = 0,  /* float32 activations */
+  BITLINEAR_BF16 = 1  /* bfloat16 activations, widened exactly to float */
+} bitlinear_dtype;
+
+typedef enum {
+  BITLINEAR_EPI_NONE = 0,  /* Y = y */
+  BITLINEAR_EPI_RELU2 = 1  /* Y = max(y, 0)^2 (the squared-ReLU FFN
+                              activation, "BitNet b1.58 2B4T Technical
+                              Report" card, Method Adaptation) */
+} bitlinear_epilogue;
+
+/* Optional extra outputs of bitlinear_forward, for checking the integer
+ * intermediates.  Each pointer may be NULL.  xq_out: int8 [M][K];
+ * xscale_out: float [M]; acc_out: int32 [M][N] (the exact sum_k q_x*q_w). */
+typedef struct {
+  int8_t* xq_out;
+  float* xscale_out;
+  int32_t* acc_out;
+} bitlinear_debug;
+
+/* Version of this ABI (BITLINEAR_ABI_VERSION). */
+int bitlinear_abi_version(void);
+
+/* Bytes of the packed form of an [N][K] ternary matrix: N*K/4.  Returns 0
+ * when N or K is negative or breaks N%16 / K%256. */
+size_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes bitlinear_quantize_weights needs for an [N][K] matrix
+ * (per-row double sums).  0 on a bad shape. */
+size_t bitlinear_weights_workspace_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes bitlinear_forward needs for M tokens x K -> N (quantized
+ * activations, scales and row sums when the large-M path runs; may be 0).
+ * Returns (size_t)-1 on a bad shape. */
+size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* Absmean ternary quantization and packing of float W [N][K] ("BitNet b1.58
+ * 2B4T Technical Report" card, Method Adaptation: absmean to {-1,0,+1}, four
+ * ternary weights per int8 in HBM).  Writes `packed`
+ * (bitlinear_packed_bytes(N,K) bytes) and gamma_c into `gamma` (one float,
+ * device memory).  `ws` holds at least bitlinear_weights_workspace_bytes(N,K)
+ * bytes; its contents on entry do not matter. */
+bitlinear_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
+                                            uint8_t* packed, float* gamma, void* ws,
+                                            size_t ws_bytes, void* stream);
+
+/* Packs already-ternary int8 q_w [N][K].  Values should be in {-1,0,1};
+ * any other value is clamped into that range before it is stored. */
+bitlinear_status bitlinear_pack_ternary(const int8_t* Wq, int64_t N, int64_t K,
+                                        uint8_t* packed, void* stream);
+
+/* Inverse of the packing: int8 q_w [N][K] from the packed bytes.  A code 3
+ * (never written by this library) unpacks as 0. */
+bitlinear_status bitlinear_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K,
+                                          int8_t* Wq, void* stream);
+
+/* Per-token absmax int8 quantization of X [M][K] (fishai digest, activation
+ * quantization item; technical-report card, Method Adaptation).  Writes Xq
+ * [M][K], x_scale [M] (= s_x) and, if x_rowsum is not NULL, the int32 row
+ * sums of Xq [M].  Here K needs only K >= 1 and K % 16 == 0. */
+bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, int64_t M,
+                                         int64_t K, int8_t* Xq, float* x_scale,
+                                         int32_t* x_rowsum, void* stream);
+
+/* The BitLinear forward: Y [M][N] (float) from X [M][K] (dtype), the packed
+ * ternary weights and gamma_c (device float, as written by
+ * bitlinear_quantize_weights).  Quantizes X per token, contracts in int32,
+ * rescales, then applies `epi`.  `dbg` may be NULL.  `ws` holds at least
+ * bitlinear_workspace_bytes(M, K, N) bytes (NULL allowed when that is 0). */
+bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t M,
+                                   int64_t K, int64_t N, const uint8_t* packed,
+                                   const float* gamma, float* Y, bitlinear_epilogue epi,
+                                   const bitlinear_debug* dbg, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* The same forward from activations already quantized by
+ * bitlinear_quantize_acts: Xq [M][K], x_scale [M], x_rowsum [M] (all three
+ * required). */
+bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
+                                     const int32_t* x_rowsum, int64_t M, int64_t K,
+                                     int64_t N, const uint8_t* packed, const float* gamma,
+                                     float* Y, bitlinear_epilogue epi, void* stream);
+
+/* Static text for a status code. */
+const char* bitlinear_status_string(bitlinear_status s);
+
+/* Thread-local detail for the last non-OK return on the calling thread
+ * ("" if none).  Valid until the next library call on that thread. */
+const char* bitlinear_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+function, and rejects bad arguments before it touches the GPU.
+
+None of these calls launches work: each one fails argument checking (which
+runs before any HIP call) or is a documented no-op, so they run without a GPU.
+Fake device addresses are never dereferenced.
+"""
+import ctypes
+
+import pytest
+
+bl = pytest.importorskip("w1_a8_matmul_amd.bitlinear")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ARG = range(8)
+A = 0x10000   # a fake, 16-byte aligned address (never dereferenced)
+U = 0x10004   # a fake misaligned address
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bl.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = bl.declared_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(L):
+    assert L.bitlinear_abi_version() == 1
+    for s in range(8):
+        assert L.bitlinear_status_string(s).decode()
+    assert L.bitlinear_status_string(99).decode() == "unknown status"
+
+
+def test_packed_and_workspace_sizes(L):
+    assert L.bitlinear_packed_bytes(6912, 2560) == 6912 * 2560 // 4
+    assert L.bitlinear_packed_bytes(16, 256) == 1024
+    assert L.bitlinear_packed_bytes(15, 256) == 0
+    assert L.bitlinear_packed_bytes(16, 128) == 0
+    assert L.bitlinear_packed_bytes(-16, 256) == 0
+    assert L.bitlinear_weights_workspace_bytes(6912, 2560) >= 6912 * 8
+    assert L.bitlinear_workspace_bytes(1, 2560, 6912) == 0
+    assert L.bitlinear_workspace_bytes(0, 2560, 6912) == 0
+    big = L.bitlinear_workspace_bytes(2048, 2560, 6912)
+    assert big >= 2048 * 2560 + 2 * 2048 * 4
+    assert L.bitlinear_workspace_bytes(-1, 2560, 6912) == ctypes.c_size_t(-1).value
+    assert L.bitlinear_workspace_bytes(4, 100, 6912) == ctypes.c_size_t(-1).value
+
+
+def _err(L):
+    return L.bitlinear_last_error().decode()
+
+
+def test_quantize_weights_validation(L):
+    qw = L.bitlinear_quantize_weights
+    assert qw(None, 16, 256, A, A, A, 1 << 20, None) == ERR_NULL
+    assert "required" in _err(L)
+    assert qw(A, 15, 256, A, A, A, 1 << 20, None) == ERR_SHAPE
+    assert qw(A, 16, 100, A, A, A, 1 << 20, None) == ERR_SHAPE
+    assert qw(A, 0, 256, A, A, A, 1 << 20, None) == ERR_SHAPE
+    assert qw(A, 16, 256 * 70000, A, A, A, 1 << 30, None) == ERR_SHAPE  # 127*K overflows int32
+    assert qw(U, 16, 256, A, A, A, 1 << 20, None) == ERR_ALIGN
+    assert qw(A, 16, 256, U, A, A, 1 << 20, None) == ERR_ALIGN
+    assert qw(A, 16, 256, A, A, None, 0, None) == ERR_WS
+    assert qw(A, 16, 256, A, A, A, 8, None) == ERR_WS
+    assert "workspace" in _err(L)
+
+
+def test_pack_unpack_validation(L):
+    assert L.bitlinear_pack_ternary(None, 16, 256, A, None) == ERR_NULL
+    assert L.bitlinear_pack_ternary(A, 16, 255, A, None) == ERR_SHAPE
+    assert L.bitlinear_pack_ternary(A, 16, 256, U, None) == ERR_ALIGN
+    assert L.bitlinear_unpack_ternary(A, 16, 256, None, None) == ERR_NULL
+    assert L.bitlinear_unpack_ternary(A, 8, 256, A, None) == ERR_SHAPE
+    assert L.bitlinear_unpack_ternary(U, 16, 256, A, None) == ERR_ALIGN
+
+
+def test_quantize_acts_validation(L):
+    qa = L.bitlinear_quantize_acts
+    assert qa(A, 7, 4, 256, A, A, A, None) == ERR_DTYPE
+    assert qa(A, 0, -1, 256, A, A, A, None) == ERR_SHAPE
+    assert qa(A, 0, 4, 100, A, A, A, None) == ERR_SHAPE
+    assert qa(None, 1, 4, 256, A, A, A, None) == ERR_NULL
+    assert qa(A, 1, 4, 256, A, None, A, None) == ERR_NULL
+    assert qa(A, 1, 4, 256, U, A, A, None) == ERR_ALIGN
+    assert qa(A, 1, 4, 256, A, A, U, None) == ERR_ALIGN
+    # M == 0 is a no-op, even with null pointers
+    assert qa(None, 1, 0, 256, None, None, None, None) == OK
+    assert _err(L) == ""
+
+
+def test_forward_validation(L):
+    f = L.bitlinear_forward
+    assert f(A, 3, 1, 256, 16, A, A, A, 0, None, None, 0, None) == ERR_DTYPE
+    assert f(A, 0, 1, 256, 16, A, A, A, 5, None, None, 0, None) == ERR_ARG
+    assert f(A, 0, -1, 256, 16, A, A, A, 0, None, None, 0, None) == ERR_SHAPE
+    assert f(A, 0, 1, 256, 24, A, A, A, 0, None, None, 0, None) == ERR_SHAPE
+    assert f(A, 0, 1, 260, 16, A, A, A, 0, None, None, 0, None) == ERR_SHAPE
+    assert f(A, 0, 1, 256, 16, None, A, A, 0, None, None, 0, None) == ERR_NULL
+    assert f(A, 0, 1, 256, 16, A, None, A, 0, None, None, 0, None) == ERR_NULL
+    assert f(A, 0, 1, 256, 16, A, A, None, 0, None, None, 0, None) == ERR_NULL
+    assert f(U, 0, 1, 256, 16, A, A, A, 0, None, None, 0, None) == ERR_ALIGN
+    dbg = bl.Debug(U, None, None)
+    assert f(A, 0, 1, 256, 16, A, A, A, 0, ctypes.byref(dbg), None, 0, None) == ERR_ALIGN
+    # the large-M path needs a workspace
+    assert f(A, 1, 2048, 2560, 6912, A, A, A, 0, None, None, 0, None) == ERR_WS
+    assert f(A, 1, 2048, 2560, 6912, A, A, A, 0, None, A, 1024, None) == ERR_WS
+    assert f(A, 1, 2048, 2560, 6912, A, A, A, 0, None, U, 1 << 30, None) == ERR_ALIGN
+    assert f(None, 1, 0, 2560, 6912, None, None, None, 0, None, None, 0, None) == OK
+
+
+def test_forward_q_validation(L):
+    f = L.bitlinear_forward_q
+    assert f(A, A, A, 4, 256, 16, A, A, A, 9, None) == ERR_ARG
+    assert f(A, A, None, 4, 256, 16, A, A, A, 0, None) == ERR_NULL
+    assert f(A, A, A, 4, 256, 17, A, A, A, 0, None) == ERR_SHAPE
+    assert f(A, A, A, 4, 256, 16, A, U, A, 0, None) == ERR_ALIGN
+    assert f(None, None, None, 0, 256, 16, None, None, None, 0, None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    with pytest.raises(bl.BitLinearError):
+        bl.quantize_acts(torch.zeros(4, 256))

@@ -1,0 +1,221 @@
+"""ctypes binding of libbitlinear.so (declared in include/bitlinear.h).
+
+Argument marshalling only: every step of the BitLinear forward runs in the
+library's HIP kernels.  torch supplies device memory (outputs and workspaces
+are allocated as torch tensors) and the stream (torch's current stream).
+If the library is not built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+from .build import LIBRARY, ROOT
+
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+OK = 0
+F32, BF16 = 0, 1
+EPI = {"none": 0, None: 0, "relu2": 1}
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class BitLinearError(RuntimeError):
+    pass
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [("xq_out", _p), ("xscale_out", _p), ("acc_out", _p)]
+
+
+_lib = None
+
+
+def declared_functions() -> list:
+    """Names of the functions include/bitlinear.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise BitLinearError(
+            f"{LIBRARY} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(LIBRARY)
+    L.bitlinear_abi_version.restype = ctypes.c_int
+    L.bitlinear_packed_bytes.argtypes = [_i64, _i64]
+    L.bitlinear_packed_bytes.restype = _sz
+    L.bitlinear_weights_workspace_bytes.argtypes = [_i64, _i64]
+    L.bitlinear_weights_workspace_bytes.restype = _sz
+    L.bitlinear_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    L.bitlinear_workspace_bytes.restype = _sz
+    L.bitlinear_quantize_weights.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
+    L.bitlinear_pack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
+    L.bitlinear_unpack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
+    L.bitlinear_quantize_acts.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
+    L.bitlinear_forward.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p,
+                                    ctypes.c_int, ctypes.POINTER(Debug), _p, _sz, _p]
+    L.bitlinear_forward_q.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p,
+                                      ctypes.c_int, _p]
+    for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
+                 "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
+                 "bitlinear_forward_q"):
+        getattr(L, name).restype = ctypes.c_int
+    L.bitlinear_status_string.argtypes = [ctypes.c_int]
+    L.bitlinear_status_string.restype = ctypes.c_char_p
+    L.bitlinear_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def check(status: int, fn: str) -> None:
+    if status != OK:
+        L = lib()
+        raise BitLinearError(f"{fn}: {L.bitlinear_status_string(status).decode()} "
+                             f"({status}): {L.bitlinear_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise BitLinearError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise BitLinearError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise BitLinearError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+# -- sizes ------------------------------------------------------------------
+def abi_version() -> int:
+    return lib().bitlinear_abi_version()
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return lib().bitlinear_packed_bytes(N, K)
+
+
+def weights_workspace_bytes(N: int, K: int) -> int:
+    return lib().bitlinear_weights_workspace_bytes(N, K)
+
+
+def workspace_bytes(M: int, K: int, N: int) -> int:
+    return lib().bitlinear_workspace_bytes(M, K, N)
+
+
+def _empty_bytes(n: int, device) -> torch.Tensor:
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+
+# -- weights ----------------------------------------------------------------
+def quantize_weights(W: torch.Tensor, packed: Optional[torch.Tensor] = None,
+                     gamma: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Absmean ternary quantization + packing of float32 W [N][K].
+
+    Returns (packed uint8 [N*K/4], gamma_c float32 [1])."""
+    N, K = W.shape
+    if W.dtype != torch.float32:
+        raise BitLinearError("W must be float32")
+    nbytes = packed_bytes(N, K)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=W.device)
+    if gamma is None:
+        gamma = torch.empty(4, dtype=torch.float32, device=W.device)[:1]
+    if workspace is None:
+        workspace = _empty_bytes(weights_workspace_bytes(N, K), W.device)
+    st = lib().bitlinear_quantize_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma),
+                                          _ptr(workspace), workspace.numel(), _stream())
+    check(st, "bitlinear_quantize_weights")
+    return packed, gamma
+
+
+def pack_ternary(Wq: torch.Tensor) -> torch.Tensor:
+    N, K = Wq.shape
+    packed = torch.empty(max(packed_bytes(N, K), 1), dtype=torch.uint8, device=Wq.device)
+    check(lib().bitlinear_pack_ternary(_ptr(Wq), N, K, _ptr(packed), _stream()),
+          "bitlinear_pack_ternary")
+    return packed
+
+
+def unpack_ternary(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
+    Wq = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    check(lib().bitlinear_unpack_ternary(_ptr(packed), N, K, _ptr(Wq), _stream()),
+          "bitlinear_unpack_ternary")
+    return Wq
+
+
+# -- activations ------------------------------------------------------------
+def quantize_acts(X: torch.Tensor):
+    """Per-token absmax int8: returns (Xq int8 [M][K], x_scale [M], x_rowsum [M])."""
+    M, K = X.shape
+    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    rs = torch.empty(M, dtype=torch.int32, device=X.device)
+    check(lib().bitlinear_quantize_acts(_ptr(X), _dtype_code(X), M, K, _ptr(Xq), _ptr(sx),
+                                        _ptr(rs), _stream()),
+          "bitlinear_quantize_acts")
+    return Xq, sx, rs
+
+
+# -- forward ----------------------------------------------------------------
+def forward(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
+            epilogue: Optional[str] = None, debug: bool = False,
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Y [M][N] float32 = BitLinear(X).  With debug=True returns
+    (Y, {"xq": int8 [M][K], "x_scale": [M], "acc": int32 [M][N]})."""
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    ws_need = workspace_bytes(M, K, N)
+    if ws_need == ctypes.c_size_t(-1).value:
+        ws_need = 0  # the call itself reports the bad shape
+    if workspace is None and ws_need > 0:
+        workspace = _empty_bytes(ws_need, X.device)
+    dbg = None
+    dbg_struct = None
+    if debug:
+        dbg = {"xq": torch.empty((M, K), dtype=torch.int8, device=X.device),
+               "x_scale": torch.empty(M, dtype=torch.float32, device=X.device),
+               "acc": torch.empty((M, N), dtype=torch.int32, device=X.device)}
+        dbg_struct = Debug(_ptr(dbg["xq"]), _ptr(dbg["x_scale"]), _ptr(dbg["acc"]))
+    st = lib().bitlinear_forward(
+        _ptr(X), _dtype_code(X), M, K, N, _ptr(packed), _ptr(gamma), _ptr(out),
+        EPI[epilogue], ctypes.byref(dbg_struct) if dbg_struct is not None else None,
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream())
+    check(st, "bitlinear_forward")
+    return (out, dbg) if debug else out
+
+
+def forward_q(Xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor,
+              packed: torch.Tensor, gamma: torch.Tensor, N: int,
+              epilogue: Optional[str] = None, out: Optional[torch.Tensor] = None):
+    M, K = Xq.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    st = lib().bitlinear_forward_q(_ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), M, K, N,
+                                   _ptr(packed), _ptr(gamma), _ptr(out), EPI[epilogue],
+                                   _stream())
+    check(st, "bitlinear_forward_q")
+    return out

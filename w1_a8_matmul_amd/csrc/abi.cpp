@@ -1,0 +1,225 @@
+// C ABI of the BitLinear library: argument checks, path choice by M, and
+// error reporting.  Declared in include/bitlinear.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/bitlinear.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+bitlinear_status fail(bitlinear_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bitlinear_status ok() {
+  g_last_error[0] = '\0';
+  return BITLINEAR_OK;
+}
+
+bitlinear_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BITLINEAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxK = 16908288;  // 127 * K must fit int32
+
+bitlinear_status check_nk(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return fail(BITLINEAR_ERR_SHAPE, "N=%lld K=%lld must be >= 1", (long long)N, (long long)K);
+  if (N % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "N=%lld is not a multiple of 16", (long long)N);
+  if (K % 256 != 0) return fail(BITLINEAR_ERR_SHAPE, "K=%lld is not a multiple of 256", (long long)K);
+  if (K > kMaxK) return fail(BITLINEAR_ERR_SHAPE, "K=%lld exceeds %lld", (long long)K, (long long)kMaxK);
+  return BITLINEAR_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the large-M path: int8 activations, scales, row sums.
+size_t q_workspace(int64_t M, int64_t K) {
+  return align256((size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+size_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || N % 16 != 0 || K % 256 != 0) return 0;
+  return (size_t)N * (size_t)K / 4;
+}
+
+size_t bitlinear_weights_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || N % 16 != 0 || K % 256 != 0) return 0;
+  return align256((size_t)N * sizeof(double));
+}
+
+size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 1 || K < 1 || N % 16 != 0 || K % 256 != 0) return (size_t)-1;
+  if (M == 0 || bl_gemv_supports(M, K)) return 0;
+  return q_workspace(M, K);
+}
+
+bitlinear_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
+                                            uint8_t* packed, float* gamma, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  if (!W || !packed || !gamma) return fail(BITLINEAR_ERR_NULL, "W, packed and gamma are required");
+  bitlinear_status st = check_nk(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (!aligned16(W) || !aligned16(packed) || !aligned16(gamma))
+    return fail(BITLINEAR_ERR_ALIGN, "W, packed and gamma must be 16-byte aligned");
+  const size_t need = bitlinear_weights_workspace_bytes(N, K);
+  if (!ws || ws_bytes < need)
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* row_sum = static_cast<double*>(ws);
+  hipError_t e = bl_launch_absmean_rows(W, N, K, row_sum, s);
+  if (e == hipSuccess) e = bl_launch_absmean_final(row_sum, N, K, gamma, s);
+  if (e == hipSuccess) e = bl_launch_quant_pack(W, N, K, gamma, packed, s);
+  return from_hip(e, "bitlinear_quantize_weights");
+}
+
+bitlinear_status bitlinear_pack_ternary(const int8_t* Wq, int64_t N, int64_t K,
+                                        uint8_t* packed, void* stream) {
+  if (!Wq || !packed) return fail(BITLINEAR_ERR_NULL, "Wq and packed are required");
+  bitlinear_status st = check_nk(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (!aligned16(Wq) || !aligned16(packed))
+    return fail(BITLINEAR_ERR_ALIGN, "Wq and packed must be 16-byte aligned");
+  return from_hip(bl_launch_pack(Wq, N, K, packed, static_cast<hipStream_t>(stream)),
+                  "bitlinear_pack_ternary");
+}
+
+bitlinear_status bitlinear_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K,
+                                          int8_t* Wq, void* stream) {
+  if (!Wq || !packed) return fail(BITLINEAR_ERR_NULL, "packed and Wq are required");
+  bitlinear_status st = check_nk(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (!aligned16(Wq) || !aligned16(packed))
+    return fail(BITLINEAR_ERR_ALIGN, "Wq and packed must be 16-byte aligned");
+  return from_hip(bl_launch_unpack(packed, N, K, Wq, static_cast<hipStream_t>(stream)),
+                  "bitlinear_unpack_ternary");
+}
+
+bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, int64_t M,
+                                         int64_t K, int8_t* Xq, float* x_scale,
+                                         int32_t* x_rowsum, void* stream) {
+  if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
+    return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (M < 0 || K < 1 || K % 16 != 0 || K > kMaxK)
+    return fail(BITLINEAR_ERR_SHAPE, "M=%lld K=%lld: need M >= 0, K >= 1, K %% 16 == 0",
+                (long long)M, (long long)K);
+  if (M > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "M=%lld too large", (long long)M);
+  if (M == 0) return ok();
+  if (!X || !Xq || !x_scale) return fail(BITLINEAR_ERR_NULL, "X, Xq and x_scale are required");
+  if (!aligned16(X) || !aligned16(Xq) || !aligned16(x_scale) ||
+      (x_rowsum && !aligned16(x_rowsum)))
+    return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  return from_hip(bl_launch_quant_acts(X, (int)dtype, M, K, Xq, x_scale, x_rowsum,
+                                       static_cast<hipStream_t>(stream)),
+                  "bitlinear_quantize_acts");
+}
+
+bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t M, int64_t K,
+                                   int64_t N, const uint8_t* packed, const float* gamma,
+                                   float* Y, bitlinear_epilogue epi, const bitlinear_debug* dbg,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
+    return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (epi != BITLINEAR_EPI_NONE && epi != BITLINEAR_EPI_RELU2)
+    return fail(BITLINEAR_ERR_ARG, "unknown epilogue %d", (int)epi);
+  if (M < 0) return fail(BITLINEAR_ERR_SHAPE, "M=%lld is negative", (long long)M);
+  bitlinear_status st = check_nk(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (M > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "M=%lld too large", (long long)M);
+  if (M == 0) return ok();
+  if (!X || !packed || !gamma || !Y)
+    return fail(BITLINEAR_ERR_NULL, "X, packed, gamma and Y are required");
+  int8_t* xq_out = dbg ? dbg->xq_out : nullptr;
+  float* xs_out = dbg ? dbg->xscale_out : nullptr;
+  int32_t* acc_out = dbg ? dbg->acc_out : nullptr;
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(gamma) || !aligned16(Y) ||
+      (xq_out && !aligned16(xq_out)) || (xs_out && !aligned16(xs_out)) ||
+      (acc_out && !aligned16(acc_out)))
+    return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const bool relu2 = epi == BITLINEAR_EPI_RELU2;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (bl_gemv_supports(M, K))
+    return from_hip(bl_launch_gemv(X, (int)dtype, M, K, N, packed, gamma, Y, relu2, xq_out,
+                                   xs_out, acc_out, s),
+                    "bitlinear_forward");
+
+  const size_t need = q_workspace(M, K);
+  if (!ws || ws_bytes < need)
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  char* base = static_cast<char*>(ws);
+  int8_t* xq = reinterpret_cast<int8_t*>(base);
+  float* sx = reinterpret_cast<float*>(base + align256((size_t)M * (size_t)K));
+  int32_t* rs = reinterpret_cast<int32_t*>(base + align256((size_t)M * (size_t)K) +
+                                           align256((size_t)M * 4));
+  hipError_t e = bl_launch_quant_acts(X, (int)dtype, M, K, xq, sx, rs, s);
+  if (e == hipSuccess && xq_out)
+    e = hipMemcpyAsync(xq_out, xq, (size_t)M * (size_t)K, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess && xs_out)
+    e = hipMemcpyAsync(xs_out, sx, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = bl_launch_gemm_q(xq, sx, rs, M, K, N, packed, gamma, Y, relu2, acc_out, s);
+  return from_hip(e, "bitlinear_forward");
+}
+
+bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
+                                     const int32_t* x_rowsum, int64_t M, int64_t K, int64_t N,
+                                     const uint8_t* packed, const float* gamma, float* Y,
+                                     bitlinear_epilogue epi, void* stream) {
+  if (epi != BITLINEAR_EPI_NONE && epi != BITLINEAR_EPI_RELU2)
+    return fail(BITLINEAR_ERR_ARG, "unknown epilogue %d", (int)epi);
+  if (M < 0) return fail(BITLINEAR_ERR_SHAPE, "M=%lld is negative", (long long)M);
+  bitlinear_status st = check_nk(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (M > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "M=%lld too large", (long long)M);
+  if (M == 0) return ok();
+  if (!Xq || !x_scale || !x_rowsum || !packed || !gamma || !Y)
+    return fail(BITLINEAR_ERR_NULL, "Xq, x_scale, x_rowsum, packed, gamma and Y are required");
+  if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(x_rowsum) || !aligned16(packed) ||
+      !aligned16(gamma) || !aligned16(Y))
+    return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  return from_hip(bl_launch_gemm_q(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
+                                   epi == BITLINEAR_EPI_RELU2, nullptr,
+                                   static_cast<hipStream_t>(stream)),
+                  "bitlinear_forward_q");
+}
+
+const char* bitlinear_status_string(bitlinear_status s) {
+  switch (s) {
+    case BITLINEAR_OK: return "ok";
+    case BITLINEAR_ERR_NULL: return "null pointer";
+    case BITLINEAR_ERR_SHAPE: return "bad shape";
+    case BITLINEAR_ERR_ALIGN: return "misaligned pointer";
+    case BITLINEAR_ERR_DTYPE: return "unknown dtype";
+    case BITLINEAR_ERR_WORKSPACE: return "workspace too small";
+    case BITLINEAR_ERR_HIP: return "HIP runtime error";
+    case BITLINEAR_ERR_ARG: return "bad argument";
+  }
+  return "unknown status";
+}
+
+const char* bitlinear_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Per-token absmax int8 quantization of activations (fishai news digest on
+// BitNet b1.58 2B4T, activation-quantization item; "BitNet b1.58 2B4T
+// Technical Report" card, Method Adaptation).  One workgroup per token.
+#include "common.hpp"
+#include "quant_row.hpp"
+
+namespace {
+
+using namespace bl;
+
+template <int DT>
+__global__ __launch_bounds__(256) void quant_acts_kernel(const void* __restrict__ X, int64_t K,
+                                                         int8_t* __restrict__ Xq,
+                                                         float* __restrict__ x_scale,
+                                                         int32_t* __restrict__ x_rowsum) {
+  __shared__ float red_f[4];
+  __shared__ int red_i[4];
+  const int64_t m = blockIdx.x;
+  const RowQuant rq = row_absmax_scale<DT, 256>(X, m, K, red_f);
+  const int sum = row_quantize_to<DT, 256>(X, m, K, rq.qs, Xq + m * K, red_i);
+  if (threadIdx.x == 0) {
+    x_scale[m] = rq.a_c / kQmax;
+    if (x_rowsum) x_rowsum[m] = sum;
+  }
+}
+
+}  // namespace
+
+hipError_t bl_launch_quant_acts(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
+                                float* x_scale, int32_t* x_rowsum, hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(quant_acts_kernel<1>, dim3((unsigned)M), dim3(256), 0, s, X, K, Xq,
+                       x_scale, x_rowsum);
+  else
+    hipLaunchKernelGGL(quant_acts_kernel<0>, dim3((unsigned)M), dim3(256), 0, s, X, K, Xq,
+                       x_scale, x_rowsum);
+  return hipGetLastError();
+}

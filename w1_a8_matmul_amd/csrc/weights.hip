@@ -1,0 +1,165 @@
+// Offline weight path: absmean scale, ternary quantization and packing into
+// the 16x256-tile layout, plus plain pack / unpack of int8 ternary values.
+//
+// Absmean to {-1, 0, +1} and four ternary weights per byte follow the
+// "BitNet b1.58 2B4T Technical Report" card, section "Method Adaptation".
+#include "common.hpp"
+
+namespace {
+
+using namespace bl;
+
+// One thread per row: sum_k |W[n,k]| in double, strictly in column order,
+// so that the result does not depend on the launch shape.
+__global__ __launch_bounds__(256) void absmean_rows_kernel(const float* __restrict__ W,
+                                                           int64_t N, int64_t K,
+                                                           double* __restrict__ row_sum) {
+  int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const float4* p = reinterpret_cast<const float4*>(W + n * K);
+  double r = 0.0;
+  for (int64_t i = 0; i < K / 4; ++i) {
+    float4 v = p[i];
+    r += fabs((double)v.x);
+    r += fabs((double)v.y);
+    r += fabs((double)v.z);
+    r += fabs((double)v.w);
+  }
+  row_sum[n] = r;
+}
+
+// A single thread adds the row sums in row order and rounds the mean once.
+__global__ void absmean_final_kernel(const double* __restrict__ row_sum, int64_t N, int64_t K,
+                                     float* __restrict__ gamma) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  double total = 0.0;
+  for (int64_t n = 0; n < N; ++n) total += row_sum[n];
+  double count = (double)N * (double)K;
+  float g = (float)(total / count);
+  *gamma = g > kEps ? g : kEps;
+}
+
+// Position of packed word w (4 bytes, 16 weights) in the matrix: the tile is
+// w / 256; inside it chunk (w % 256) / 4 and word w % 4.  Returns the row and
+// the first of the 16 consecutive columns the word holds.
+__device__ __forceinline__ void word_origin(int64_t w, int64_t K, int64_t& n, int64_t& k0) {
+  const int64_t kblocks = K / kTileCols;
+  const int64_t tile = w >> 8;
+  const int within = (int)(w & 255);
+  const int chunk = within >> 2, word = within & 3;
+  const int64_t tile_row = tile / kblocks, kblock = tile - tile_row * kblocks;
+  n = tile_row * kTileRows + (chunk & 15);
+  k0 = kblock * kTileCols + (chunk >> 4) * 64 + word * 16;
+}
+
+// Column offset 4f + e of a word lives in byte e, bits 2f..2f+1.
+__global__ __launch_bounds__(256) void quant_pack_kernel(const float* __restrict__ W,
+                                                         int64_t N, int64_t K,
+                                                         const float* __restrict__ gamma_p,
+                                                         uint32_t* __restrict__ out) {
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (w >= N * K / 16) return;
+  const float gamma = *gamma_p;
+  int64_t n, k0;
+  word_origin(w, K, n, k0);
+  const float4* src = reinterpret_cast<const float4*>(W + n * K + k0);
+  uint32_t word = 0;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const float4 v = src[f];
+    const float vals[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float q = __builtin_rintf(vals[e] / gamma);
+      q = fminf(fmaxf(q, -1.0f), 1.0f);
+      word |= (uint32_t)((int)q + 1) << (8 * e + 2 * f);
+    }
+  }
+  out[w] = word;
+}
+
+__global__ __launch_bounds__(256) void pack_kernel(const int8_t* __restrict__ Wq, int64_t N,
+                                                   int64_t K, uint32_t* __restrict__ out) {
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (w >= N * K / 16) return;
+  int64_t n, k0;
+  word_origin(w, K, n, k0);
+  const uint4 v = *reinterpret_cast<const uint4*>(Wq + n * K + k0);
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  uint32_t word = 0;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int q = (int)(int8_t)(d[f] >> (8 * e));
+      q = q < -1 ? -1 : (q > 1 ? 1 : q);
+      word |= (uint32_t)(q + 1) << (8 * e + 2 * f);
+    }
+  }
+  out[w] = word;
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ in, int64_t N,
+                                                     int64_t K, int8_t* __restrict__ Wq) {
+  const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (w >= N * K / 16) return;
+  int64_t n, k0;
+  word_origin(w, K, n, k0);
+  const uint32_t word = in[w];
+  uint32_t d[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t code = (word >> (8 * e + 2 * f)) & 3u;
+      const int q = code == 3u ? 0 : (int)code - 1;
+      out |= ((uint32_t)q & 0xffu) << (8 * e);
+    }
+    d[f] = out;
+  }
+  *reinterpret_cast<uint4*>(Wq + n * K + k0) = make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+inline unsigned grid_for(int64_t items, int block) {
+  return (unsigned)((items + block - 1) / block);
+}
+
+}  // namespace
+
+hipError_t bl_launch_absmean_rows(const float* W, int64_t N, int64_t K, double* row_sum,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(absmean_rows_kernel, dim3(grid_for(N, 256)), dim3(256), 0, s, W, N, K,
+                     row_sum);
+  return hipGetLastError();
+}
+
+hipError_t bl_launch_absmean_final(const double* row_sum, int64_t N, int64_t K, float* gamma,
+                                   hipStream_t s) {
+  hipLaunchKernelGGL(absmean_final_kernel, dim3(1), dim3(64), 0, s, row_sum, N, K, gamma);
+  return hipGetLastError();
+}
+
+hipError_t bl_launch_quant_pack(const float* W, int64_t N, int64_t K, const float* gamma,
+                                uint8_t* packed, hipStream_t s) {
+  const int64_t words = N * K / 16;
+  hipLaunchKernelGGL(quant_pack_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s, W, N, K,
+                     gamma, reinterpret_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t bl_launch_pack(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packed,
+                          hipStream_t s) {
+  const int64_t words = N * K / 16;
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s, Wq, N, K,
+                     reinterpret_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t bl_launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
+                            hipStream_t s) {
+  const int64_t words = N * K / 16;
+  hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(packed), N, K, Wq);
+  return hipGetLastError();
+}
