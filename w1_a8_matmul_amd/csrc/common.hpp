@@ -18,21 +18,65 @@ constexpr int kTileCols = 256;
 constexpr int kTileBytes = 1024;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [p, p + bytes): loads at offsets at or past
+// `bytes` return zero and do not touch memory, so loads need no branches.
+// The third descriptor word is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16-byte load at byte offset voff (per lane) + soff (wave-uniform).
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                            uint32_t soff) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+// DPP lane moves inside each 16-lane row: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror.  After the four steps every lane
+// of a row holds the row's reduction.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, __int_as_float(dpp<0xb1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<0x4e>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<0x141>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<0x140>(__float_as_int(v))));
   return v;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+__device__ __forceinline__ int row_sum16(int v) {
+  v += dpp<0xb1>(v);
+  v += dpp<0x4e>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
   return v;
+}
+
+// Whole-wave reductions (all 64 lanes active); the result is wave-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max16(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+  v = row_sum16(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
 // rint(v) clamped to [-127, 127] as an int; v is x * qs.
