@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-launches", type=int, default=400,
                    help="launches of the dominant kernel timed for the roofline")
+    p.add_argument("--grouped", action="store_true",
+                   help="run all linears of a step as one grouped forward (M <= 4)")
     return p.parse_args()
 
 
@@ -111,14 +113,23 @@ def build_runner(args, bl, torch, wl, dev):
     for layer, li, shape in wl.step_linears(wk):
         lins.append(Linear(bl, torch, dev, shape.N, shape.K, M, x_dtype,
                            wl.weight_seed(wk.key, layer, li), wk.weight_sparse_frac, copies))
-    steps_in_chain = None
     if wk.chain_relu2:
         # up (ReLU^2) feeds down: down's input is up's float output
         up, down = lins
         down.X = up.Y
 
+    groups = None
+    if args.grouped:
+        if wk.chain_relu2:
+            raise SystemExit("--grouped needs independent linears")
+        groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, None, l.Y) for l in lins])
+                  for c in range(copies)]
+
     def step(i):
         c = i % copies
+        if groups is not None:
+            groups[c].forward()
+            return
         if wk.chain_relu2:
             up, down = lins
             bl.forward(up.X, up.packed[c], up.gamma[c], up.N, epilogue="relu2", out=up.Y,
@@ -130,7 +141,7 @@ def build_runner(args, bl, torch, wl, dev):
                 bl.forward(lin.X, lin.packed[c], lin.gamma[c], lin.N, out=lin.Y,
                            workspace=lin.ws)
 
-    return wk, M, lins, copies, step
+    return wk, M, lins, copies, step, groups
 
 
 def capture(torch, fn, count):
@@ -145,6 +156,68 @@ def capture(torch, fn, count):
         for i in range(count):
             fn(i)
     return g
+
+
+def time_graph(torch, fn, count):
+    """Microseconds per call of fn(i), i < count, replayed as one graph."""
+    g = capture(torch, fn, count)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / count
+
+
+def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
+    """The linear with the most packed bytes, launched alone back to back
+    (rotating its weight copies) in a graph bracketed by HIP events."""
+    dom = max(lins, key=lambda l: l.N * l.K)
+    epi = "relu2" if (wk.chain_relu2 and dom is lins[0]) else None
+    n = args.kernel_launches
+    copies = len(dom.packed)
+
+    def dom_step(i):
+        c = i % copies
+        bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
+                   workspace=dom.ws)
+
+    us = time_graph(torch, dom_step, n)
+    if metric_kind == "tops":
+        achieved = dom.ops() / (us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+        key = f"gemm_q_{dom.K}x{dom.N}_m{M}"
+        src = source_hash(["gemm.hip", "common.hpp"])
+    else:
+        achieved = dom.bytes() / (us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        key = f"gemv_{dom.K}x{dom.N}_m{M}"
+        src = source_hash(["gemv.hip", "quant_row.hpp", "common.hpp"])
+    roof["traffic"] = traffic_from_profile(src, key)
+    roof["kernel"] = key
+    roof["kernel_us"] = round(us, 3)
+    roof["launches_per_forward"] = 2 if dom.ws is not None else 1
+    log(f"dominant forward {key}: {us:.3f} us per call")
+    return roof
+
+
+def roofline_grouped(args, torch, step, bytes_step, wk, M, n_lin):
+    """The grouped forward of a whole step (its quantizer launch included)."""
+    n = max(4, args.kernel_launches // 20)
+    us = time_graph(torch, step, n)
+    achieved = bytes_step / (us * 1e-6) / 1e9
+    key = f"group_gemv_{wk.key}_m{M}"
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(
+                source_hash(["group.hip", "group.hpp", "quant_row.hpp", "common.hpp"]), key),
+            "kernel": key, "kernel_us": round(us, 3), "launches_per_forward": 2}
+    log(f"grouped forward: {us:.3f} us per step ({n_lin} linears)")
+    return roof
 
 
 # ---------------------------------------------------------------------------
@@ -242,15 +315,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wk, M, lins, copies, step = build_runner(args, bl, torch, wl, dev)
+    wk, M, lins, copies, step, groups = build_runner(args, bl, torch, wl, dev)
     quant_s = sum(l.quant_s for l in lins)
     n_weights = sum(l.N * l.K for l in lins) * copies
     log(f"workload {wk.key} M={M}: {len(lins)} linears, {copies} weight copies, "
         f"offline quantization {quant_s*1e3:.1f} ms for {n_weights/1e6:.1f} M weights")
 
+    # In the ReLU^2 chain the hidden vector h counts twice: written by the up
+    # projection and read by the down projection, as it is on the device.
     bytes_step = sum(l.bytes() for l in lins)
-    if wk.chain_relu2:
-        bytes_step -= lins[1].X.numel() * 4 * 0  # h is counted as down's input; up's output counted too
     ops_step = sum(l.ops() for l in lins)
     metric_kind = "tops" if M >= 128 else "hbm"
 
@@ -273,45 +346,10 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     log(f"timed {args.steps} steps: wall {wall*1e3:.3f} ms, events {gpu_ms:.3f} ms")
 
-    # Dominant kernel: the linear with the most packed bytes; its launches
-    # alone, back to back, in a graph bracketed by HIP events.
-    dom = max(lins, key=lambda l: l.N * l.K)
-    epi = "relu2" if (wk.chain_relu2 and dom is lins[0]) else None
-    L = args.kernel_launches
-    dcopies = max(1, min(len(dom.packed), L))
-
-    def dom_step(i):
-        c = i % dcopies
-        bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
-                   workspace=dom.ws)
-
-    gd = capture(torch, dom_step, L)
-    gd.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    gd.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    launches_per_call = 2 if dom.ws is not None else 1  # quantizer + GEMM on the large-M path
-    dom_us = e0.elapsed_time(e1) * 1e3 / L
-    if metric_kind == "tops":
-        achieved = dom.ops() / (dom_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-        kernel_key = f"gemm_q_{dom.K}x{dom.N}_m{M}"
-        src = source_hash(["gemm.hip", "common.hpp"])
+    if groups is not None:
+        roof = roofline_grouped(args, torch, step, bytes_step, wk, M, len(lins))
     else:
-        achieved = dom.bytes() / (dom_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        kernel_key = f"gemv_{dom.K}x{dom.N}_m{M}"
-        src = source_hash(["gemv.hip", "quant_row.hpp", "common.hpp"])
-    roof["traffic"] = traffic_from_profile(src, kernel_key)
-    roof["kernel"] = kernel_key
-    roof["kernel_us"] = round(dom_us, 3)
-    roof["launches_per_forward"] = launches_per_call
-    log(f"dominant forward {kernel_key}: {dom_us:.3f} us per call")
+        roof = roofline_single(args, torch, bl, wk, M, lins, metric_kind)
 
     step_s = ms_per_step / 1e3
     if metric_kind == "tops":
@@ -348,6 +386,7 @@ def main():
             "us_per_token": round(ms_per_step * 1e3 / M, 3),
             "gpu_event_ms_per_step": round(gpu_ms / args.steps, 6),
             "offline_weight_quant_ms": round(quant_s * 1e3 / copies, 3),
+            "grouped": groups is not None,
         },
         "roofline": roof,
         "cpu_baseline": cpu,

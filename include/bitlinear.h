@@ -163,6 +163,47 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      int64_t N, const uint8_t* packed, const float* gamma,
                                      float* Y, bitlinear_epilogue epi, void* stream);
 
+/* ---- Grouped decode forward ------------------------------------------------
+ * Many independent BitLinear layers that share the token count M (1..4), run
+ * as one activation-quantization launch plus one persistent launch that
+ * streams the packed weights of all layers back to back.  Each layer's result
+ * is bit-identical to bitlinear_forward on the same arguments.  Intended for
+ * decode, where one launch per layer of a few megabytes is dominated by the
+ * launch's start-up and drain. */
+typedef struct {
+  const void* X;          /* [M][K] activations, device, 16-byte aligned */
+  bitlinear_dtype dtype;  /* BITLINEAR_F32 or BITLINEAR_BF16 */
+  bitlinear_epilogue epi; /* BITLINEAR_EPI_NONE or BITLINEAR_EPI_RELU2 */
+  int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 12288 */
+  const uint8_t* packed;  /* packed weights of this layer */
+  const float* gamma;     /* gamma_c of this layer (device float) */
+  float* Y;               /* [M][N] output; must not overlap any layer's input */
+} bitlinear_group_op;
+
+/* Opaque host-side handle of a planned group (host memory only). */
+typedef struct bitlinear_group bitlinear_group;
+
+/* Device workspace bytes for a group of n_ops layers at M tokens (the layer
+ * table, the tile schedule and the quantized activations).  Returns 0 on a
+ * bad argument; needs no GPU. */
+size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops, int64_t M);
+
+/* Checks every layer, plans the tile schedule for the current device and
+ * writes the layer table into `ws` with a synchronous copy (so call it
+ * outside stream capture).  `ws` must hold bitlinear_group_workspace_bytes
+ * bytes and must stay allocated, and the layers' buffers valid, for as long
+ * as the group is used.  *out receives a handle to free with
+ * bitlinear_group_destroy. */
+bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops, int64_t M,
+                                        void* ws, size_t ws_bytes, bitlinear_group** out);
+
+/* Runs every layer of the group on `stream` (two launches; capturable in a
+ * HIP graph).  Calls that overlap on one workspace race. */
+bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream);
+
+/* Frees the handle (not the workspace).  NULL is allowed. */
+void bitlinear_group_destroy(bitlinear_group* g);
+
 /* Static text for a status code. */
 const char* bitlinear_status_string(bitlinear_status s);
 

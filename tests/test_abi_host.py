@@ -23,7 +23,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = bl.declared_functions()
-    assert len(names) == 12
+    assert len(names) >= 16
     for n in names:
         assert hasattr(L, n), n
 
@@ -126,3 +126,29 @@ def test_binding_refuses_cpu_tensors():
 
     with pytest.raises(bl.BitLinearError):
         bl.quantize_acts(torch.zeros(4, 256))
+
+
+def _gop(X=A, dtype=1, epi=0, K=2560, N=256, packed=A, gamma=A, Y=A):
+    return bl.GroupOp(X, dtype, epi, K, N, packed, gamma, Y)
+
+
+def test_group_validation(L):
+    arr = (bl.GroupOp * 2)(_gop(), _gop(K=6912, N=2560))
+    need = L.bitlinear_group_workspace_bytes(arr, 2, 1)
+    assert need >= 2560 + 6912 + 2 * 64
+    assert L.bitlinear_group_workspace_bytes(arr, 2, 5) == 0      # M > 4
+    assert L.bitlinear_group_workspace_bytes(arr, 0, 1) == 0
+    h = ctypes.c_void_p()
+    assert L.bitlinear_group_create(arr, 2, 1, A, need, None) == ERR_NULL
+    assert L.bitlinear_group_create(None, 2, 1, A, need, ctypes.byref(h)) == ERR_NULL
+    assert L.bitlinear_group_create(arr, 2, 0, A, need, ctypes.byref(h)) == ERR_SHAPE
+    assert L.bitlinear_group_create(arr, 2, 1, A, need - 1, ctypes.byref(h)) == ERR_WS
+    assert L.bitlinear_group_create(arr, 2, 1, U, need, ctypes.byref(h)) == ERR_ALIGN
+    bad = [(_gop(dtype=5), ERR_DTYPE), (_gop(epi=3), ERR_ARG), (_gop(N=24), ERR_SHAPE),
+           (_gop(K=12288 + 256), ERR_SHAPE), (_gop(Y=None), ERR_NULL), (_gop(X=U), ERR_ALIGN)]
+    for op, code in bad:
+        one = (bl.GroupOp * 1)(op)
+        assert L.bitlinear_group_create(one, 1, 1, A, 1 << 30, ctypes.byref(h)) == code
+        assert h.value is None
+    assert L.bitlinear_group_forward(None, None) == ERR_NULL
+    L.bitlinear_group_destroy(None)

@@ -289,3 +289,67 @@ def test_7b_linears(dev, bl, orc, M, li):
         rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M + li).integers(0, M, 14)]))
     _check_forward(dev, bl, orc, M, lin.K, lin.N, "student_t3_bf16", wl.weight_seed(key, 0, li),
                    sparse=0.3, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# grouped decode forward
+# ---------------------------------------------------------------------------
+GROUP_SHAPES = [(256, 16, "normal_f32", None), (2560, 272, "normal_bf16", "relu2"),
+                (6912, 2560, "normal_bf16", None), (768, 48, "normal_f32", "relu2"),
+                (4096, 512, "student_t3_bf16", None), (11008, 64, "normal_bf16", None),
+                (12288, 32, "normal_bf16", None)]
+
+
+def _group_layers(dev, bl, orc, M, shapes, seed0):
+    layers, refs = [], []
+    for i, (K, N, kind, epi) in enumerate(shapes):
+        W = wl.gen_weight(seed0 + 2 * i, N, K)
+        X, is_bf16 = wl.gen_acts(seed0 + 2 * i + 1, M, K, kind)
+        packed, gamma, qw, gc = _quantize_both(bl, orc, W, dev)
+        Xt = _acts_gpu(X, is_bf16, dev)
+        y_ref, *_ = orc.forward(X, qw, gc, bf16=is_bf16)
+        if epi == "relu2":
+            y_ref = orc.relu2(y_ref)
+        layers.append((Xt, packed, gamma, N, epi, None))
+        refs.append(y_ref)
+    return layers, refs
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_group_forward_matches_oracle(dev, bl, orc, M):
+    layers, refs = _group_layers(dev, bl, orc, M, GROUP_SHAPES, 7000 + 100 * M)
+    g = bl.Group(layers)
+    outs = [y.clone() for y in g.forward()]
+    torch.cuda.synchronize()
+    for (Xt, packed, gamma, N, epi, _), y, y_ref in zip(layers, outs, refs):
+        assert np.array_equal(y.cpu().numpy(), y_ref)
+        single = bl.forward(Xt, packed, gamma, N, epilogue=epi)
+        assert torch.equal(single, y)
+    again = g.forward()
+    for y, y2 in zip(outs, again):
+        assert torch.equal(y, y2)
+
+
+def test_group_2b_layer_graph_replay(dev, bl, orc):
+    shapes = [(l.K, l.N, "normal_bf16", None) for l in wl.LAYER_2B]
+    layers, refs = _group_layers(dev, bl, orc, 1, shapes, 7900)
+    g = bl.Group(layers)
+    g.forward()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g.forward()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        g.forward()
+    for rep in range(3):
+        for y in g.outputs:
+            y.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for y, y_ref in zip(g.outputs, refs):
+            assert np.array_equal(y.cpu().numpy(), y_ref), f"replay {rep}"

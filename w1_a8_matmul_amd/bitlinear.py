@@ -35,6 +35,11 @@ class Debug(ctypes.Structure):
     _fields_ = [("xq_out", _p), ("xscale_out", _p), ("acc_out", _p)]
 
 
+class GroupOp(ctypes.Structure):
+    _fields_ = [("X", _p), ("dtype", ctypes.c_int), ("epi", ctypes.c_int), ("K", _i64),
+                ("N", _i64), ("packed", _p), ("gamma", _p), ("Y", _p)]
+
+
 _lib = None
 
 
@@ -71,6 +76,15 @@ def lib() -> ctypes.CDLL:
                  "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
                  "bitlinear_forward_q"):
         getattr(L, name).restype = ctypes.c_int
+    L.bitlinear_group_workspace_bytes.argtypes = [ctypes.POINTER(GroupOp), ctypes.c_int, _i64]
+    L.bitlinear_group_workspace_bytes.restype = _sz
+    L.bitlinear_group_create.argtypes = [ctypes.POINTER(GroupOp), ctypes.c_int, _i64, _p, _sz,
+                                         ctypes.POINTER(_p)]
+    L.bitlinear_group_create.restype = ctypes.c_int
+    L.bitlinear_group_forward.argtypes = [_p, _p]
+    L.bitlinear_group_forward.restype = ctypes.c_int
+    L.bitlinear_group_destroy.argtypes = [_p]
+    L.bitlinear_group_destroy.restype = None
     L.bitlinear_status_string.argtypes = [ctypes.c_int]
     L.bitlinear_status_string.restype = ctypes.c_char_p
     L.bitlinear_last_error.restype = ctypes.c_char_p
@@ -219,3 +233,50 @@ def forward_q(Xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor,
                                    _stream())
     check(st, "bitlinear_forward_q")
     return out
+
+
+# -- grouped decode forward ----------------------------------------------------
+class Group:
+    """Independent BitLinear layers sharing M (1..4), run in two launches.
+
+    layers: list of (X, packed, gamma, N, epilogue, Y) with X [M][K] on the
+    GPU and Y [M][N] float32 (allocated when None).  The tensors must stay
+    alive while the group is used; ``forward()`` enqueues on torch's stream."""
+
+    def __init__(self, layers):
+        L = lib()
+        arr = (GroupOp * len(layers))()
+        self.keep = []
+        self.outputs = []
+        M = None
+        for i, (X, packed, gamma, N, epilogue, Y) in enumerate(layers):
+            m, K = X.shape
+            M = m if M is None else M
+            if m != M:
+                raise BitLinearError("all layers of a group need the same M")
+            if Y is None:
+                Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+            arr[i] = GroupOp(_ptr(X), _dtype_code(X), EPI[epilogue], K, N, _ptr(packed),
+                             _ptr(gamma), _ptr(Y))
+            self.keep += [X, packed, gamma]
+            self.outputs.append(Y)
+        self.M = M
+        need = L.bitlinear_group_workspace_bytes(arr, len(layers), M)
+        if need == 0:
+            check(L.bitlinear_group_create(arr, len(layers), M, None, 0, ctypes.byref(_p())),
+                  "bitlinear_group_workspace_bytes")
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=layers[0][0].device)
+        handle = _p()
+        check(L.bitlinear_group_create(arr, len(layers), M, _ptr(self.workspace), need,
+                                       ctypes.byref(handle)), "bitlinear_group_create")
+        self.handle = handle
+
+    def forward(self):
+        check(lib().bitlinear_group_forward(self.handle, _stream()), "bitlinear_group_forward")
+        return self.outputs
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _lib is not None:
+            _lib.bitlinear_group_destroy(h)
+            self.handle = None

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libbitlinear.so")
 
-SOURCES = ["abi.cpp", "weights.hip", "acts.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "weights.hip", "acts.hip", "gemv.hip", "gemm.hip", "group.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -6,8 +6,12 @@
 #include <cstdio>
 #include <cstring>
 
+#include <new>
+#include <vector>
+
 #include "../../include/bitlinear.h"
 #include "common.hpp"
+#include "group.hpp"
 
 namespace {
 
@@ -50,7 +54,67 @@ size_t q_workspace(int64_t M, int64_t K) {
   return align256((size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
 }
 
+// Grouped forward: device workspace layout.
+constexpr int kGroupMaxWG = 1024;
+constexpr int kGroupMaxK = 12288;
+
+struct GroupLayout {
+  size_t table, wg_begin, xq, sx, rs, total;
+};
+
+GroupLayout group_layout(const bitlinear_group_op* ops, int n_ops, int64_t M) {
+  GroupLayout L;
+  size_t off = 0;
+  L.table = off;
+  off += align256((size_t)n_ops * sizeof(GroupOp));
+  L.wg_begin = off;
+  off += align256((size_t)(kGroupMaxWG + 1) * sizeof(int));
+  L.xq = off;
+  for (int i = 0; i < n_ops; ++i) off += align256((size_t)M * (size_t)ops[i].K);
+  L.sx = off;
+  off += align256((size_t)n_ops * (size_t)M * 4);
+  L.rs = off;
+  off += align256((size_t)n_ops * (size_t)M * 4);
+  L.total = off;
+  return L;
+}
+
+bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M) {
+  if (!ops) return fail(BITLINEAR_ERR_NULL, "ops is required");
+  if (n_ops < 1 || n_ops > 65536) return fail(BITLINEAR_ERR_ARG, "n_ops=%d out of range", n_ops);
+  if (M < 1 || M > 4) return fail(BITLINEAR_ERR_SHAPE, "grouped forward needs 1 <= M <= 4, got %lld", (long long)M);
+  int64_t items = 0;
+  for (int i = 0; i < n_ops; ++i) {
+    const bitlinear_group_op& o = ops[i];
+    if (o.dtype != BITLINEAR_F32 && o.dtype != BITLINEAR_BF16)
+      return fail(BITLINEAR_ERR_DTYPE, "op %d: unknown dtype %d", i, (int)o.dtype);
+    if (o.epi != BITLINEAR_EPI_NONE && o.epi != BITLINEAR_EPI_RELU2)
+      return fail(BITLINEAR_ERR_ARG, "op %d: unknown epilogue %d", i, (int)o.epi);
+    bitlinear_status st = check_nk(o.N, o.K);
+    if (st != BITLINEAR_OK) return st;
+    if (o.K > kGroupMaxK) return fail(BITLINEAR_ERR_SHAPE, "op %d: K=%lld exceeds %d", i, (long long)o.K, kGroupMaxK);
+    if (!o.X || !o.packed || !o.gamma || !o.Y) return fail(BITLINEAR_ERR_NULL, "op %d: X, packed, gamma and Y are required", i);
+    if (!aligned16(o.X) || !aligned16(o.packed) || !aligned16(o.gamma) || !aligned16(o.Y))
+      return fail(BITLINEAR_ERR_ALIGN, "op %d: tensor pointers must be 16-byte aligned", i);
+    items += o.N / 16;
+  }
+  if (items > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "too many output tiles");
+  return BITLINEAR_OK;
+}
+
 }  // namespace
+
+struct bitlinear_group {
+  int n_ops;
+  int M;
+  int G;
+  int max_k;
+  GroupOp* ops;
+  int* wg_begin;
+  int8_t* xq;
+  float* sx;
+  int32_t* rs;
+};
 
 extern "C" {
 
@@ -205,6 +269,102 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                    static_cast<hipStream_t>(stream)),
                   "bitlinear_forward_q");
 }
+
+size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops, int64_t M) {
+  if (check_group(ops, n_ops, M) != BITLINEAR_OK) return 0;
+  return group_layout(ops, n_ops, M).total;
+}
+
+bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops, int64_t M,
+                                        void* ws, size_t ws_bytes, bitlinear_group** out) {
+  if (!out) return fail(BITLINEAR_ERR_NULL, "out is required");
+  *out = nullptr;
+  bitlinear_status st = check_group(ops, n_ops, M);
+  if (st != BITLINEAR_OK) return st;
+  const GroupLayout L = group_layout(ops, n_ops, M);
+  if (!ws || ws_bytes < L.total)
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
+  // Two workgroups per compute unit: each holds one layer's int8 activations
+  // (at most 4 x 12288 bytes) in LDS.
+  int G = 2 * (cus > 0 ? cus : 1);
+  if (G > kGroupMaxWG) G = kGroupMaxWG;
+
+  std::vector<GroupOp> table((size_t)n_ops);
+  std::vector<int64_t> weight_before;  // cumulative 1 KiB blocks before each tile
+  int64_t item = 0, xq_off = 0, total_blocks = 0;
+  int max_k = 0;
+  for (int i = 0; i < n_ops; ++i) {
+    const bitlinear_group_op& o = ops[i];
+    GroupOp& t = table[(size_t)i];
+    t.X = o.X;
+    t.packed = o.packed;
+    t.gamma = o.gamma;
+    t.Y = o.Y;
+    t.xq_off = xq_off;
+    t.K = (int32_t)o.K;
+    t.N = (int32_t)o.N;
+    t.dtype = (int32_t)o.dtype;
+    t.relu2 = o.epi == BITLINEAR_EPI_RELU2 ? 1 : 0;
+    t.item_begin = (int32_t)item;
+    const int kblocks = (int)(o.K / 256);
+    const int nc = (kblocks + 11) / 12;
+    t.chunk = (kblocks + nc - 1) / nc;
+    item += o.N / 16;
+    total_blocks += (o.N / 16) * kblocks;
+    xq_off += (int64_t)align256((size_t)M * (size_t)o.K);
+    if (o.K > max_k) max_k = (int)o.K;
+  }
+  // Byte-balanced contiguous tile ranges: workgroup g starts at the first
+  // tile whose preceding weight reaches g/G of the total.
+  std::vector<int> wg_begin((size_t)G + 1);
+  {
+    int g = 0;
+    int64_t before = 0, it = 0;
+    for (int i = 0; i < n_ops && g <= G; ++i) {
+      const int64_t tiles = ops[i].N / 16, kblocks = ops[i].K / 256;
+      for (int64_t t = 0; t < tiles; ++t, ++it) {
+        while (g <= G && before * G >= (int64_t)g * total_blocks) wg_begin[(size_t)g++] = (int)it;
+        before += kblocks;
+      }
+    }
+    while (g <= G) wg_begin[(size_t)g++] = (int)item;
+  }
+  char* base = static_cast<char*>(ws);
+  e = hipMemcpy(base + L.table, table.data(), table.size() * sizeof(GroupOp), hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(base + L.wg_begin, wg_begin.data(), wg_begin.size() * sizeof(int),
+                  hipMemcpyHostToDevice);
+  if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
+  bitlinear_group* g = new (std::nothrow) bitlinear_group;
+  if (!g) return fail(BITLINEAR_ERR_ARG, "out of host memory");
+  g->n_ops = n_ops;
+  g->M = (int)M;
+  g->G = G;
+  g->max_k = max_k;
+  g->ops = reinterpret_cast<GroupOp*>(base + L.table);
+  g->wg_begin = reinterpret_cast<int*>(base + L.wg_begin);
+  g->xq = reinterpret_cast<int8_t*>(base + L.xq);
+  g->sx = reinterpret_cast<float*>(base + L.sx);
+  g->rs = reinterpret_cast<int32_t*>(base + L.rs);
+  *out = g;
+  return ok();
+}
+
+bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream) {
+  if (!g) return fail(BITLINEAR_ERR_NULL, "group handle is required");
+  return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k, g->xq,
+                                  g->sx, g->rs, static_cast<hipStream_t>(stream)),
+                  "bitlinear_group_forward");
+}
+
+void bitlinear_group_destroy(bitlinear_group* g) { delete g; }
 
 const char* bitlinear_status_string(bitlinear_status s) {
   switch (s) {
