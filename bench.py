@@ -59,6 +59,9 @@ def parse():
                    help="launches of the dominant kernel timed for the roofline")
     p.add_argument("--grouped", action="store_true",
                    help="run all linears of a step as one grouped forward (M <= 4)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only time a plain 1 GiB device-to-device copy (achievable HBM "
+                        "bandwidth, and the known-size kernel for counter calibration)")
     return p.parse_args()
 
 
@@ -298,6 +301,25 @@ def source_hash(names):
     return h.hexdigest()
 
 
+def copy_probe(torch, nbytes=1 << 30, reps=10):
+    """A plain device copy of known size: reads and writes nbytes each."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"probe": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "ms": round(ms, 4), "GBps_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -311,6 +333,9 @@ def main():
     from w1_a8_matmul_amd import workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     bl.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

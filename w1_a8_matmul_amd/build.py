@@ -29,7 +29,7 @@ CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-command-line-argument",
+    "-Wall", "-Wno-unused-command-line-argument", "-Wno-inline-asm",
 ]
 
 

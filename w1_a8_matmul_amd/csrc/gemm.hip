@@ -1,29 +1,169 @@
 // BitLinear forward from int8 activations on the CDNA4 int8 matrix cores
-// (v_mfma_i32_16x16x64_i8): for larger M the ternary x int8 product is a
-// dense contraction, so the packed tiles are unpacked in registers into
-// MFMA B operands and multiplied against int8 activation tiles.
+// (v_mfma_i32_16x16x64_i8).  For larger M the ternary x int8 product is a
+// dense contraction (prefill), so the 2-bit codes are unpacked into MFMA B
+// operands and multiplied against int8 activation tiles.
+//
+// A workgroup of WM x WN waves computes a (16*TM*WM) x (16*TN*WN) output
+// tile, walking K in steps of 128 columns (half of a packed 256-column
+// block).  Each step's int8 activation rows (A) and packed weight chunks (B,
+// still 2 bits per weight) are copied into LDS by direct-to-LDS buffer
+// loads (buffer_load_dwordx4 ... lds: no register staging), into a ring of
+// three stages, two steps ahead of the multiply.  Each wave reads its A
+// fragments (16 bytes per lane from XOR-swizzled rows, so eight lanes hit
+// eight distinct bank groups) and one 16-byte chunk of packed codes per B
+// fragment pair, unpacks the codes in registers and issues TM*TN*2 MFMAs per step.
+// Codes
+// are q+1 in {0,1,2}; the activation row sums turn sum(code*x) into
+// sum(q*x) exactly in the epilogue.
+//
+// The load/unpack/multiply order follows the kernel outline of the "BitNet
+// b1.58 2B4T Technical Report" card, section "Method Adaptation"; the tiling
+// is this library's own, for gfx950.
 #include "common.hpp"
 
 namespace {
 
 using namespace bl;
 
-constexpr int kThreads = 256;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Wave tile: TM x TN blocks of 16x16 outputs; 2x2 waves per workgroup.
-template <int TM, int TN, bool RELU2, bool DEBUG>
-__global__ __launch_bounds__(kThreads) void gemm_q_kernel(
+// Raw buffer descriptor (gfx9 layout: 48-bit base, stride 0, byte range,
+// raw-buffer format word) for the copies below.
+__device__ __forceinline__ v4i rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// One wave-wide direct-to-LDS copy: lane j's 16 bytes at voff land at
+// lds + 16*j (lds is wave-uniform).  Offsets at or past the range read zeros
+// without touching memory.  Written as inline asm so that the compiler does
+// not track these LDS writes itself: it can follow only one outstanding
+// copy per LDS object and would otherwise wait for the next step's copies
+// before reading the current step.  The kernel orders the copies with
+// explicit vmcnt waits and barriers.  M0 holds the LDS base (read when the
+// instruction issues; one wait state after writing it); no other code in the
+// kernel uses M0.
+__device__ __forceinline__ void copy16(v4i rs, uint32_t voff, void* lds) {
+  const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(la), "s"(rs) : "memory", "m0");
+}
+
+constexpr int kStepCols = 128;  // K columns per pipeline step
+constexpr int kStages = 3;      // LDS ring depth (two steps in flight)
+
+template <int WM, int WN, int TM, int TN>
+struct Tile {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BM = 16 * TM * WM;
+  static constexpr int BN = 16 * TN * WN;
+  static constexpr int kBTiles = BN / kTileRows;                // weight tiles per workgroup
+  static constexpr int kABytes = BM * kStepCols;                // A bytes per step
+  static constexpr int kAInstr = kABytes / 1024;                // 1 KiB per wave DMA
+  static constexpr int kBInstrUsed = kBTiles / 2;               // 2 tiles' halves each
+  // Every wave issues the same number of copies per step (the waits count
+  // them): B is padded with copies that read zeros into a spare area.
+  static constexpr int kAPerWave = kAInstr / kWaves;
+  static constexpr int kBPerWave = (kBInstrUsed + kWaves - 1) / kWaves;
+  static constexpr int kBBytes = kBPerWave * kWaves * 1024;     // B bytes per step (padded)
+  static constexpr int kStageBytes = kABytes + kBBytes;
+  static_assert(kAInstr % kWaves == 0 && kBTiles % 2 == 0, "stage sizes");
+  static_assert(kStages * kStageBytes <= 160 * 1024, "LDS ring must fit 160 KiB");
+};
+
+// vmcnt <= N, other counters unconstrained (gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads() (which would
+// wait for every outstanding copy).  The s_barrier intrinsic alone does not
+// order memory accesses for the compiler, so empty asm statements with a
+// memory clobber keep LDS reads and copies on their side of it; they emit
+// no instructions.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int WM, int WN, int TM, int TN, bool DEBUG>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ x_rowsum, int64_t M, int64_t K, int64_t N,
+    const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
-    float* __restrict__ Y, int32_t* __restrict__ acc_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m_base = ((int64_t)blockIdx.y * 2 + wm) * (16 * TM);
-  const int64_t ntile_base = ((int64_t)blockIdx.x * 2 + wn) * TN;  // in 16-row tiles
-  const int64_t ntiles = N / kTileRows;
-  const int64_t kblocks = K / kTileCols;
-  const int r16 = lane & 15, grp = lane >> 4;
+    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tiles_n,
+    int tiles_total) {
+  using T = Tile<WM, WN, TM, TN>;
+  // Separate arrays (not one indexed ring): with compile-time stage indices
+  // the compiler can tell which copies a read depends on and waits for
+  // those only.
+  __shared__ __align__(1024) int8_t ring0[T::kStageBytes];
+  __shared__ __align__(1024) int8_t ring1[T::kStageBytes];
+  __shared__ __align__(1024) int8_t ring2[T::kStageBytes];
+  auto stage_ptr = [&](int slot) -> int8_t* {
+    return slot == 0 ? ring0 : slot == 1 ? ring1 : ring2;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Consecutive workgroup ids go to different XCDs; give each XCD a
+  // contiguous run of tiles (row-major), so tiles that share activation rows
+  // share that XCD's L2.
+  int tile = blockIdx.x;
+  if (tiles_total % 8 == 0) tile = (blockIdx.x % 8) * (tiles_total / 8) + blockIdx.x / 8;
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const int m0 = tm * T::BM;
+  const int nt0 = tn * T::kBTiles;  // first 16-row weight tile
+  const int ntiles = N / kTileRows;
+  const int kblocks = K / kTileCols;
+  const int nsteps = K / kStepCols;
+
+  // Buffer ranges: rows past M and weight tiles past N read as zero.
+  const int rows_here = min(T::BM, M - m0);
+  const v4i a_rsrc = rsrc_words(Xq + (int64_t)m0 * K, (uint32_t)rows_here * (uint32_t)K);
+  const int tiles_here = min(T::kBTiles, ntiles - nt0);
+  const v4i b_rsrc = rsrc_words(packed + (int64_t)nt0 * kblocks * kTileBytes,
+                                (uint32_t)tiles_here * (uint32_t)kblocks * kTileBytes);
+
+  // DMA of step kh into ring slot `slot`.  A: wave instruction q writes rows
+  // 8q..8q+7 (128 bytes each); lane j fills row 8q + j/8, 16-byte slot j%8,
+  // loading activation column (j%8) ^ (row & 7) -- the XOR swizzle.
+  // B: instruction q writes weight tiles 2q, 2q+1 (their half for this step,
+  // 512 bytes each).
+  // Steps past the end are issued too, with offsets moved out of the buffer
+  // range (so they read zeros without touching memory): a branch around the
+  // copies would make the compiler wait for all of them before LDS reads.
+  auto dma = [&](int kh, int slot) {
+    int8_t* base = stage_ptr(slot);
+    const uint32_t past = kh < nsteps ? 0u : 0x80000000u;
+#pragma unroll
+    for (int p = 0; p < T::kAPerWave; ++p) {
+      const int q = wave + p * T::kWaves;
+      const int r = 8 * q + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      const uint32_t voff =
+          ((uint32_t)r * (uint32_t)K + (uint32_t)(kh * kStepCols + c * 16)) | past;
+      copy16(a_rsrc, voff, base + q * 1024);
+    }
+#pragma unroll
+    for (int p = 0; p < T::kBPerWave; ++p) {
+      const int q = wave + p * T::kWaves;
+      const int t = 2 * q + (lane >> 5);
+      const uint32_t pad = q < T::kBInstrUsed ? 0u : 0x80000000u;
+      const uint32_t voff = (uint32_t)((t * kblocks + (kh >> 1)) * kTileBytes +
+                                       (kh & 1) * (kTileBytes / 2) + (lane & 31) * 16) |
+                            past | pad;
+      copy16(b_rsrc, voff, base + T::kABytes + q * 1024);
+    }
+  };
+  // Copies this wave issues per step.
+  constexpr int kMyDma = T::kAPerWave + T::kBPerWave;
 
   v4i acc[TM][TN];
 #pragma unroll
@@ -31,43 +171,63 @@ __global__ __launch_bounds__(kThreads) void gemm_q_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  for (int64_t b = 0; b < kblocks; ++b) {
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) dma(s, s);
+
+  const int r16 = lane & 15, grp = lane >> 4;
+  auto step = [&](int kh, int slot) {
+    // This wave's copies of step kh have landed once at most the copies of
+    // the later step are outstanding; the barrier then makes
+    // every wave's copies visible and frees the slot of step kh-1.
+    // (Not __syncthreads(): its workgroup fence would wait for every
+    // outstanding copy, emptying the pipeline.  The LDS traffic to order is
+    // the copies, waited for by count here, and the reads of step kh-1,
+    // whose results the MFMAs have already consumed.)
+    wait_vmcnt<(kStages - 2) * kMyDma>();
+    lds_barrier();
+    dma(kh + kStages - 1, (slot + kStages - 1) % kStages);
+
+    const int8_t* sa = stage_ptr(slot);
+    const int8_t* sb = sa + T::kABytes;
+    // Lane group grp takes sub-block (grp & 1) of this half and, in MFMA t,
+    // word 2*(grp >> 1) + t of that 64-column chunk: columns
+    // 64*(grp & 1) + 16*(2*(grp >> 1) + t) .. +15 of the step.  The B words a
+    // lane needs for t = 0, 1 sit in one 16-byte chunk; the lane reads the
+    // whole chunk (16-byte LDS reads are never merged into paired reads,
+    // which would make the compiler wait for every outstanding copy).
     uint4 bw[TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int64_t nt = ntile_base + j;
-      bw[j] = nt < ntiles ? reinterpret_cast<const uint4*>(
-                                packed + (nt * kblocks + b) * kTileBytes)[lane]
-                          : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-    }
-    v4i a[TM][4];
+    for (int j = 0; j < TN; ++j)
+      bw[j] = *reinterpret_cast<const uint4*>(
+          sb + (wn * TN + j) * (kTileBytes / 2) + ((grp & 1) * 16 + r16) * 16);
+    const bool hi = (grp >> 1) != 0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m_base + i * 16 + r16;
-      if (m < M) {
-        const v4i* p = reinterpret_cast<const v4i*>(Xq + m * K + b * kTileCols + grp * 64);
+    for (int t = 0; t < 2; ++t) {
+      v4i a[TM];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) a[i][g] = p[g];
-      } else {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) a[i][g] = v4i{0, 0, 0, 0};
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * 16 * TM + i * 16 + r16;
+        const int c = (4 * (grp & 1) + 2 * (grp >> 1) + t) ^ (r & 7);
+        a[i] = *reinterpret_cast<const v4i*>(sa + r * kStepCols + c * 16);
       }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      v4i bop[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint32_t w = g == 0 ? bw[j].x : g == 1 ? bw[j].y : g == 2 ? bw[j].z : bw[j].w;
-        bop[j] = v4i{(int)codes(w, 0), (int)codes(w, 1), (int)codes(w, 2), (int)codes(w, 3)};
+        const uint32_t w = t == 0 ? (hi ? bw[j].z : bw[j].x) : (hi ? bw[j].w : bw[j].y);
+        const v4i b = v4i{(int)codes(w, 0), (int)codes(w, 1), (int)codes(w, 2), (int)codes(w, 3)};
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i][g], bop[j], acc[i][j], 0, 0, 0);
     }
+  };
+  int kh = 0;
+  for (; kh + kStages <= nsteps; kh += kStages) {
+    step(kh, 0);
+    step(kh + 1, 1);
+    step(kh + 2, 2);
   }
+  if (kh < nsteps) step(kh, 0);
+  if (kh + 1 < nsteps) step(kh + 1, 1);
 
   // D layout of a 16x16 int32 MFMA tile: lane holds column (lane % 16) and
   // rows 4*(lane / 16) + r, r = 0..3.
@@ -76,51 +236,53 @@ __global__ __launch_bounds__(kThreads) void gemm_q_kernel(
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t m = m_base + i * 16 + grp * 4 + r;
+      const int m = m0 + wm * 16 * TM + i * 16 + grp * 4 + r;
       if (m >= M) continue;
       const float sx = x_scale[m];
       const int rs = x_rowsum[m];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int64_t nt = ntile_base + j;
+        const int nt = nt0 + wn * TN + j;
         if (nt >= ntiles) continue;
-        const int64_t n = nt * kTileRows + r16;
+        const int64_t n = (int64_t)nt * kTileRows + r16;
         const int v = acc[i][j][r] - rs;
-        Y[m * N + n] = rescale(v, sx, gamma, RELU2);
-        if constexpr (DEBUG) acc_out[m * N + n] = v;
+        Y[(int64_t)m * N + n] = rescale(v, sx, gamma, relu2 != 0);
+        if constexpr (DEBUG) acc_out[(int64_t)m * N + n] = v;
       }
     }
   }
 }
 
-constexpr int kTM = 4, kTN = 4;
-
-template <bool RELU2, bool DEBUG>
-hipError_t launch(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M, int64_t K,
-                  int64_t N, const uint8_t* packed, const float* gamma, float* Y,
-                  int32_t* acc_out, hipStream_t s) {
-  const int64_t rows_per_wg = 2 * 16 * kTM;
-  const int64_t ntiles_per_wg = 2 * kTN;
-  const dim3 grid((unsigned)((N / kTileRows + ntiles_per_wg - 1) / ntiles_per_wg),
-                  (unsigned)((M + rows_per_wg - 1) / rows_per_wg));
-  hipLaunchKernelGGL((gemm_q_kernel<kTM, kTN, RELU2, DEBUG>), grid, dim3(kThreads), 0, s, Xq,
-                     sx, rs, M, K, N, packed, gamma, Y, acc_out);
+template <int WM, int WN, int TM, int TN>
+hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M,
+                      int64_t K, int64_t N, const uint8_t* packed, const float* gamma, float* Y,
+                      bool relu2, int32_t* acc_out, hipStream_t s) {
+  using T = Tile<WM, WN, TM, TN>;
+  const int tiles_m = (int)((M + T::BM - 1) / T::BM);
+  const int tiles_n = (int)((N + T::BN - 1) / T::BN);
+  const int total = tiles_m * tiles_n;
+  if (acc_out)
+    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, true>), dim3(total), dim3(T::kThreads), 0,
+                       s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y, relu2 ? 1 : 0,
+                       acc_out, tiles_n, total);
+  else
+    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, false>), dim3(total), dim3(T::kThreads), 0,
+                       s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y, relu2 ? 1 : 0,
+                       acc_out, tiles_n, total);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile choice: measured on MI355X over the prefill shapes (M = 512, 2048;
+// K = 2560..11008; N = 2560..22016), 64x128 tiles (4 waves of 32x64, up to
+// four workgroups per compute unit) beat 128x128, 128x160 and 128x256 on
+// every shape: this kernel is bound by latency hiding (waves per SIMD), not
+// by LDS bandwidth.
 hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                             const float* gamma, float* Y, bool relu2, int32_t* acc_out,
                             hipStream_t s) {
-  if (relu2)
-    return acc_out ? launch<true, true>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
-                                        acc_out, s)
-                   : launch<true, false>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
-                                         acc_out, s);
-  return acc_out ? launch<false, true>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
-                                       acc_out, s)
-                 : launch<false, false>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
-                                        acc_out, s);
+  return launch_cfg<2, 2, 2, 4>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
+                                acc_out, s);
 }
