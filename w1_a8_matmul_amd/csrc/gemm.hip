@@ -10,8 +10,8 @@
 // loads (buffer_load_dwordx4 ... lds: no register staging), into a ring of
 // three stages, two steps ahead of the multiply.  Each wave reads its A
 // fragments (16 bytes per lane from XOR-swizzled rows, so eight lanes hit
-// eight distinct bank groups) and one 16-byte chunk of packed codes per B
-// fragment pair, unpacks the codes in registers and issues TM*TN*2 MFMAs per step.
+// eight distinct bank groups) and 8 bytes of packed codes per B fragment
+// pair, unpacks the codes in registers and issues TM*TN*2 MFMAs per step.
 // Codes
 // are q+1 in {0,1,2}; the activation row sums turn sum(code*x) into
 // sum(q*x) exactly in the epilogue.
@@ -50,10 +50,10 @@ __device__ __forceinline__ void copy16(v4i rs, uint32_t voff, void* lds) {
 }
 
 constexpr int kStepCols = 128;  // K columns per pipeline step
-constexpr int kStages = 3;      // LDS ring depth (two steps in flight)
 
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, int S>
 struct Tile {
+  static constexpr int kStages = S;  // LDS ring depth (S-1 steps in flight)
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BM = 16 * TM * WM;
@@ -69,14 +69,17 @@ struct Tile {
   static constexpr int kBBytes = kBPerWave * kWaves * 1024;     // B bytes per step (padded)
   static constexpr int kStageBytes = kABytes + kBBytes;
   static_assert(kAInstr % kWaves == 0 && kBTiles % 2 == 0, "stage sizes");
-  static_assert(kStages * kStageBytes <= 160 * 1024, "LDS ring must fit 160 KiB");
+  static_assert(S >= 2 && S * kStageBytes <= 160 * 1024, "LDS ring must fit 160 KiB");
 };
 
-// vmcnt <= N, other counters unconstrained (gfx9 s_waitcnt encoding).
+// vmcnt <= N and lgkmcnt == 0 (gfx9 s_waitcnt encoding): this wave's
+// copies older than the last N have landed, and its LDS reads have returned
+// -- the compiler may otherwise leave reads of the previous step in flight
+// across the next barrier, after which other waves refill that slot.
 template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
+__device__ __forceinline__ void wait_copies_and_reads() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
 }
 
 // Workgroup barrier without the memory fence of __syncthreads() (which would
@@ -90,23 +93,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int WM, int WN, int TM, int TN, bool DEBUG>
+template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
     float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tiles_n,
     int tiles_total) {
-  using T = Tile<WM, WN, TM, TN>;
-  // Separate arrays (not one indexed ring): with compile-time stage indices
-  // the compiler can tell which copies a read depends on and waits for
-  // those only.
-  __shared__ __align__(1024) int8_t ring0[T::kStageBytes];
-  __shared__ __align__(1024) int8_t ring1[T::kStageBytes];
-  __shared__ __align__(1024) int8_t ring2[T::kStageBytes];
-  auto stage_ptr = [&](int slot) -> int8_t* {
-    return slot == 0 ? ring0 : slot == 1 ? ring1 : ring2;
-  };
+  using T = Tile<WM, WN, TM, TN, S>;
+  constexpr int kStages = S;
+  __shared__ __align__(1024) int8_t ring[kStages][T::kStageBytes];
+  auto stage_ptr = [&](int slot) -> int8_t* { return &ring[slot][0]; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -177,13 +174,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
   const int r16 = lane & 15, grp = lane >> 4;
   auto step = [&](int kh, int slot) {
     // This wave's copies of step kh have landed once at most the copies of
-    // the later step are outstanding; the barrier then makes
-    // every wave's copies visible and frees the slot of step kh-1.
+    // the later steps are outstanding; the barrier then makes every wave's
+    // copies visible and, with every wave's reads of step kh-1 returned,
+    // frees that step's slot for the copy issued next.
     // (Not __syncthreads(): its workgroup fence would wait for every
     // outstanding copy, emptying the pipeline.  The LDS traffic to order is
     // the copies, waited for by count here, and the reads of step kh-1,
     // whose results the MFMAs have already consumed.)
-    wait_vmcnt<(kStages - 2) * kMyDma>();
+    wait_copies_and_reads<(kStages - 2) * kMyDma>();
     lds_barrier();
     dma(kh + kStages - 1, (slot + kStages - 1) % kStages);
 
@@ -192,15 +190,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
     // Lane group grp takes sub-block (grp & 1) of this half and, in MFMA t,
     // word 2*(grp >> 1) + t of that 64-column chunk: columns
     // 64*(grp & 1) + 16*(2*(grp >> 1) + t) .. +15 of the step.  The B words a
-    // lane needs for t = 0, 1 sit in one 16-byte chunk; the lane reads the
-    // whole chunk (16-byte LDS reads are never merged into paired reads,
-    // which would make the compiler wait for every outstanding copy).
-    uint4 bw[TN];
+    // lane needs for t = 0, 1 are adjacent: one 8-byte read serves both.
+    uint2 bw[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bw[j] = *reinterpret_cast<const uint4*>(
-          sb + (wn * TN + j) * (kTileBytes / 2) + ((grp & 1) * 16 + r16) * 16);
-    const bool hi = (grp >> 1) != 0;
+      bw[j] = *reinterpret_cast<const uint2*>(
+          sb + (wn * TN + j) * (kTileBytes / 2) + ((grp & 1) * 16 + r16) * 16 + (grp >> 1) * 8);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       v4i a[TM];
@@ -212,7 +207,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint32_t w = t == 0 ? (hi ? bw[j].z : bw[j].x) : (hi ? bw[j].w : bw[j].y);
+        const uint32_t w = t == 0 ? bw[j].x : bw[j].y;
         const v4i b = v4i{(int)codes(w, 0), (int)codes(w, 1), (int)codes(w, 2), (int)codes(w, 3)};
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -220,14 +215,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
       }
     }
   };
-  int kh = 0;
-  for (; kh + kStages <= nsteps; kh += kStages) {
-    step(kh, 0);
-    step(kh + 1, 1);
-    step(kh + 2, 2);
+  // Unrolled by the ring depth so that every slot index is a constant, and
+  // padded to a whole number of rounds instead of a remainder loop (a
+  // second loop makes the compiler shuffle the accumulators every
+  // iteration).  Padding steps read zero activations (their copies are out
+  // of range), so they add nothing.
+  const int nrounds = (nsteps + kStages - 1) / kStages;
+  for (int rd = 0; rd < nrounds; ++rd) {
+#pragma unroll
+    for (int u = 0; u < kStages; ++u) step(rd * kStages + u, u);
   }
-  if (kh < nsteps) step(kh, 0);
-  if (kh + 1 < nsteps) step(kh + 1, 1);
 
   // D layout of a 16x16 int32 MFMA tile: lane holds column (lane % 16) and
   // rows 4*(lane / 16) + r, r = 0..3.
@@ -253,20 +250,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
   }
 }
 
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, int S>
 hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M,
                       int64_t K, int64_t N, const uint8_t* packed, const float* gamma, float* Y,
                       bool relu2, int32_t* acc_out, hipStream_t s) {
-  using T = Tile<WM, WN, TM, TN>;
+  using T = Tile<WM, WN, TM, TN, S>;
   const int tiles_m = (int)((M + T::BM - 1) / T::BM);
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
   const int total = tiles_m * tiles_n;
   if (acc_out)
-    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, true>), dim3(total), dim3(T::kThreads), 0,
+    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, S, true>), dim3(total), dim3(T::kThreads), 0,
                        s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y, relu2 ? 1 : 0,
                        acc_out, tiles_n, total);
   else
-    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, false>), dim3(total), dim3(T::kThreads), 0,
+    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, S, false>), dim3(total), dim3(T::kThreads), 0,
                        s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y, relu2 ? 1 : 0,
                        acc_out, tiles_n, total);
   return hipGetLastError();
@@ -283,6 +280,6 @@ hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                             const float* gamma, float* Y, bool relu2, int32_t* acc_out,
                             hipStream_t s) {
-  return launch_cfg<2, 2, 2, 4>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
-                                acc_out, s);
+  return launch_cfg<2, 2, 2, 4, 3>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
+                                   acc_out, s);
 }
