@@ -7,8 +7,9 @@
 // tile, walking K in steps of 128 columns (half of a packed 256-column
 // block).  Each step's int8 activation rows (A) and packed weight chunks (B,
 // still 2 bits per weight) are copied into LDS by direct-to-LDS buffer
-// loads (buffer_load_dwordx4 ... lds: no register staging), into a ring of
-// three stages, two steps ahead of the multiply.  Each wave reads its A
+// loads (buffer_load_dwordx4 ... lds: no register staging) into a ring of
+// S stages, up to S steps ahead of the multiply; each wave reads a step's
+// fragments into registers one step before its MFMAs use them.  Each wave reads its A
 // fragments (16 bytes per lane from XOR-swizzled rows, so eight lanes hit
 // eight distinct bank groups) and 8 bytes of packed codes per B fragment
 // pair, unpacks the codes in registers and issues TM*TN*2 MFMAs per step.
@@ -70,6 +71,7 @@ struct Tile {
   static constexpr int kStageBytes = kABytes + kBBytes;
   static_assert(kAInstr % kWaves == 0 && kBTiles % 2 == 0, "stage sizes");
   static_assert(S >= 2 && S * kStageBytes <= 160 * 1024, "LDS ring must fit 160 KiB");
+  static_assert((S - 1) * (kAPerWave + kBPerWave) < 64, "vmcnt range");
 };
 
 // vmcnt <= N and lgkmcnt == 0 (gfx9 s_waitcnt encoding): this wave's
@@ -168,63 +170,85 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) dma(s, s);
-
+  // Fragments of one step, read from LDS into registers one step ahead of
+  // their MFMAs.  Lane group grp takes sub-block (grp & 1) of the step's
+  // half block and, in MFMA t, word 2*(grp >> 1) + t of that 64-column
+  // chunk: columns 64*(grp & 1) + 16*(2*(grp >> 1) + t) .. +15 of the step.
+  // The B words a lane needs for t = 0, 1 are adjacent (one 8-byte read).
+  struct Frag {
+    v4i a[2][TM];
+    uint2 b[TN];
+  };
   const int r16 = lane & 15, grp = lane >> 4;
-  auto step = [&](int kh, int slot) {
-    // This wave's copies of step kh have landed once at most the copies of
-    // the later steps are outstanding; the barrier then makes every wave's
-    // copies visible and, with every wave's reads of step kh-1 returned,
-    // frees that step's slot for the copy issued next.
-    // (Not __syncthreads(): its workgroup fence would wait for every
-    // outstanding copy, emptying the pipeline.  The LDS traffic to order is
-    // the copies, waited for by count here, and the reads of step kh-1,
-    // whose results the MFMAs have already consumed.)
-    wait_copies_and_reads<(kStages - 2) * kMyDma>();
-    lds_barrier();
-    dma(kh + kStages - 1, (slot + kStages - 1) % kStages);
-
+  auto read_frags = [&](int slot, Frag& f) {
     const int8_t* sa = stage_ptr(slot);
     const int8_t* sb = sa + T::kABytes;
-    // Lane group grp takes sub-block (grp & 1) of this half and, in MFMA t,
-    // word 2*(grp >> 1) + t of that 64-column chunk: columns
-    // 64*(grp & 1) + 16*(2*(grp >> 1) + t) .. +15 of the step.  The B words a
-    // lane needs for t = 0, 1 are adjacent: one 8-byte read serves both.
-    uint2 bw[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bw[j] = *reinterpret_cast<const uint2*>(
+      f.b[j] = *reinterpret_cast<const uint2*>(
           sb + (wn * TN + j) * (kTileBytes / 2) + ((grp & 1) * 16 + r16) * 16 + (grp >> 1) * 8);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      v4i a[TM];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * 16 * TM + i * 16 + r16;
         const int c = (4 * (grp & 1) + 2 * (grp >> 1) + t) ^ (r & 7);
-        a[i] = *reinterpret_cast<const v4i*>(sa + r * kStepCols + c * 16);
+        f.a[t][i] = *reinterpret_cast<const v4i*>(sa + r * kStepCols + c * 16);
       }
+  };
+  auto compute = [&](const Frag& f) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint32_t w = t == 0 ? bw[j].x : bw[j].y;
+        const uint32_t w = t == 0 ? f.b[j].x : f.b[j].y;
         const v4i b = v4i{(int)codes(w, 0), (int)codes(w, 1), (int)codes(w, 2), (int)codes(w, 3)};
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[t][i], b, acc[i][j], 0, 0, 0);
       }
-    }
   };
-  // Unrolled by the ring depth so that every slot index is a constant, and
-  // padded to a whole number of rounds instead of a remainder loop (a
-  // second loop makes the compiler shuffle the accumulators every
-  // iteration).  Padding steps read zero activations (their copies are out
-  // of range), so they add nothing.
-  const int nrounds = (nsteps + kStages - 1) / kStages;
+
+  // Prologue: copies of steps 0..S-1 into every slot; fragments of step 0.
+#pragma unroll
+  for (int st = 0; st < kStages; ++st) dma(st, st);
+  wait_copies_and_reads<(kStages - 1) * kMyDma>();
+  lds_barrier();
+  Frag f0, f1;
+  read_frags(0, f0);
+
+  // Step kh: its fragments are in registers (cur).  Wait until this wave's
+  // copies of step kh+1 have landed (at most those of the S-2 later steps
+  // outstanding) and its reads of step kh have returned; after the barrier
+  // every wave's copies of kh+1 are visible and nobody reads step kh's slot
+  // any more, so it takes the copies of step kh+S.  Then read step kh+1's
+  // fragments (nxt) and run step kh's MFMAs while those reads are in
+  // flight.  (Not __syncthreads(): its workgroup fence would wait for every
+  // outstanding copy, emptying the pipeline.)
+  auto step = [&](int kh, int slot, Frag& cur, Frag& nxt) {
+    wait_copies_and_reads<(kStages - 2) * kMyDma>();
+    lds_barrier();
+    dma(kh + kStages, slot);
+    read_frags((slot + 1) % kStages, nxt);
+    compute(cur);
+  };
+  // Unrolled so that slot and fragment-buffer indices are constants, and
+  // padded to whole rounds instead of a remainder loop (a second loop makes
+  // the compiler shuffle the accumulators every iteration).  Padding steps
+  // read zero activations (their copies are out of range) and add nothing.
+  constexpr int kUnroll = (kStages % 2 == 0) ? kStages : 2 * kStages;
+  const int nrounds = (nsteps + kUnroll - 1) / kUnroll;
   for (int rd = 0; rd < nrounds; ++rd) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) step(rd * kStages + u, u);
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u % 2 == 0)
+        step(rd * kUnroll + u, u % kStages, f0, f1);
+      else
+        step(rd * kUnroll + u, u % kStages, f1, f0);
+    }
   }
+  // No copy may still be writing LDS when the workgroup exits.
+  wait_copies_and_reads<0>();
 
   // D layout of a 16x16 int32 MFMA tile: lane holds column (lane % 16) and
   // rows 4*(lane / 16) + r, r = 0..3.
