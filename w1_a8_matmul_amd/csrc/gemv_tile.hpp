@@ -1,0 +1,193 @@
+// Building blocks of the small-M (decode) forward of one 16-row output tile,
+// (used by the one-linear decode kernel).
+//
+// A workgroup of NT threads (W = NT/64 waves) owns a tile.  Wave w streams
+// the tile's column blocks w, w+W, ... (each 16-byte lane load of a wave is
+// one whole 1 KiB packed block), unpacks the 2-bit codes in registers and
+// contracts them with the int8 activations in LDS using v_dot4; partial sums
+// are folded across lanes and waves through LDS.
+#pragma once
+
+#include "common.hpp"
+
+namespace bl {
+
+constexpr int kPreloadRegs = 64;   // VGPRs allowed for activations loaded early
+
+// Codes of a packed word, kept at their bit positions where that still fits
+// a signed byte: field 0 as is, field 1 times 4, fields 2 and 3 times 16.
+// Three accumulators at scales 1, 4 and 16 then give the exact sum
+// acc0 + acc1/4 + acc2/16 (each accumulator is an exact multiple of its
+// scale).  Five bit operations unpack 16 codes.
+__device__ __forceinline__ void dot_word(uint32_t w, const int* x4, int& a0, int& a1, int& a2) {
+  a0 = __builtin_amdgcn_sdot4((int)(w & 0x03030303u), x4[0], a0, false);
+  a1 = __builtin_amdgcn_sdot4((int)(w & 0x0c0c0c0cu), x4[1], a1, false);
+  a2 = __builtin_amdgcn_sdot4((int)(w & 0x30303030u), x4[2], a2, false);
+  a2 = __builtin_amdgcn_sdot4((int)((w >> 2) & 0x30303030u), x4[3], a2, false);
+}
+
+// Raw activation chunk: 8 consecutive elements (bf16: one uint4; f32: two).
+template <int DT>
+struct Chunk {
+  uint4 a, b;
+};
+
+// Loads of one activation row go through a buffer resource over that row,
+// so chunks past its end read as zero without a branch (branches around
+// loads make the compiler wait for them early) and without memory traffic.
+template <int DT, int NT, int KCH>
+__device__ __forceinline__ void load_row(const void* __restrict__ X, int m, int K,
+                                         Chunk<DT> ch[KCH]) {
+  constexpr uint32_t elt = DT == 1 ? 2 : 4;
+  const auto r = make_rsrc(reinterpret_cast<const char*>(X) + (int64_t)m * K * elt, K * elt);
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    const uint32_t off = (threadIdx.x + c * NT) * 8 * elt;
+    ch[c].a = buf_load16(r, off, 0);
+    ch[c].b = DT == 1 ? make_uint4(0, 0, 0, 0) : buf_load16(r, off + 16, 0);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void widen(const Chunk<DT>& c, float v[8]) {
+  if constexpr (DT == 1) {
+    const uint32_t d[4] = {c.a.x, c.a.y, c.a.z, c.a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_float(d[i] & 0xffffu);
+      v[2 * i + 1] = bf16_bits_to_float(d[i] >> 16);
+    }
+  } else {
+    v[0] = __uint_as_float(c.a.x); v[1] = __uint_as_float(c.a.y);
+    v[2] = __uint_as_float(c.a.z); v[3] = __uint_as_float(c.a.w);
+    v[4] = __uint_as_float(c.b.x); v[5] = __uint_as_float(c.b.y);
+    v[6] = __uint_as_float(c.b.z); v[7] = __uint_as_float(c.b.w);
+  }
+}
+
+// Quantizes one row held in registers into xs[0..K); the scale and row sum
+// go to s_scale / s_rowsum.  All NT threads take part.
+template <int DT, int NT, int KCH>
+__device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int8_t* xs,
+                                             float* red_f, int* red_i, float* s_scale,
+                                             int* s_rowsum) {
+  constexpr int W = NT / kWave;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Every chunk is used unconditionally (chunks past the row are zeros and
+  // cannot raise the max), so the compiler keeps their loads where they
+  // were issued instead of sinking them past the weight loads.
+  float v[KCH][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    widen<DT>(ch[c], v[c]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+  }
+  amax = wave_max(amax);
+  if (lane == 0) red_f[wave] = amax;
+  __syncthreads();
+  float a = red_f[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) a = fmaxf(a, red_f[w]);
+  const float a_c = a > kEps ? a : kEps;
+  const float qs = kQmax / a_c;
+  int sum = 0;
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    const int k = (tid + c * NT) * 8;
+    if (k < K) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = quant_i8(v[c][i] * qs);
+        sum += q;
+        if (i < 4)
+          lo |= ((uint32_t)q & 0xffu) << (8 * i);
+        else
+          hi |= ((uint32_t)q & 0xffu) << (8 * (i - 4));
+      }
+      *reinterpret_cast<uint2*>(xs + k) = make_uint2(lo, hi);
+    }
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red_i[wave] = sum;
+  __syncthreads();  // also keeps the next row's red_f write after the reads above
+  if (tid == 0) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) t += red_i[w];
+    *s_scale = a_c / kQmax;
+    *s_rowsum = t;
+  }
+}
+
+// Issues every packed-weight load of this lane for 16-row tile `tile`
+// (kblocks <= L*W column blocks; wave w takes blocks w, w+W, ...).  Blocks
+// past the tile's end read as zero through the buffer range check.  L is
+// the exact number of loads the shape needs: out-of-range loads return zeros
+// but still occupy the address and data paths.
+template <int W, int L>
+__device__ __forceinline__ void load_tile_weights(const uint8_t* __restrict__ packed,
+                                                  int64_t tile, int kblocks, int wave,
+                                                  int lane, uint4 (&wv)[L]) {
+  const auto wr = make_rsrc(packed + tile * (int64_t)kblocks * kTileBytes,
+                            (uint32_t)kblocks * kTileBytes);
+#pragma unroll
+  for (int i = 0; i < L; ++i)
+    wv[i] = buf_load16(wr, lane * 16, (uint32_t)(wave + W * i) * kTileBytes);
+}
+
+// Unpacks this lane's weights and contracts them with the int8 activations
+// xs [M][K] in LDS.  Returns, per token, the lane's partial sum of code * x
+// over its blocks for row (lane mod 16) of the tile.
+template <int M, int W, int L>
+__device__ __forceinline__ void contract_tile(const uint4 (&wv)[L], const int8_t* xs,
+                                              int K, int kblocks, int wave, int lane,
+                                              int (&part)[M]) {
+  int a0[M], a1[M], a2[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) a0[m] = a1[m] = a2[m] = 0;
+  const int sub = lane >> 4;  // 64-column quarter of the 256-column block
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int b = wave + W * i;
+    if (b < kblocks) {
+      const uint32_t words[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int4* xp = reinterpret_cast<const int4*>(xs + m * K + b * kTileCols + sub * 64);
+        const int4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+        const int xd[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                            x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dot_word(words[g], xd + 4 * g, a0[m], a1[m], a2[m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) part[m] = a0[m] + (a1[m] >> 2) + (a2[m] >> 4);
+}
+
+// Folds the lanes' partial sums of all W waves through LDS (partial is
+// [M][W][64] ints).  Afterwards thread t < M*16 holds in *acc the exact
+// sum_k code*x of token t/16, row t%16 of the tile, and returns true.
+template <int M, int W>
+__device__ __forceinline__ bool fold_tile(const int (&part)[M], int (*partial)[W][kWave],
+                                          int wave, int lane, int* acc) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) partial[m][wave][lane] = part[m];
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid >= M * kTileRows) return false;
+  const int m = tid / kTileRows, i = tid % kTileRows;
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += partial[m][w][q * 16 + i];
+  *acc = s;
+  return true;
+}
+
+}  // namespace bl
