@@ -59,6 +59,10 @@ def parse():
                    help="launches of the dominant kernel timed for the roofline")
     p.add_argument("--grouped", action="store_true",
                    help="run all linears of a step as one grouped forward (M <= 4)")
+    p.add_argument("--probes", action="store_true",
+                   help="only run the context probes: streaming-read bandwidth (1 GiB, a "
+                        "2B decode step's 521 MB, one 4.4 MB GEMV's worth) and the int8 "
+                        "matrix-core rate (both MFMA shapes)")
     p.add_argument("--copy-probe", action="store_true",
                    help="only time a plain 1 GiB device-to-device copy (achievable HBM "
                         "bandwidth, and the known-size kernel for counter calibration)")
@@ -320,6 +324,64 @@ def copy_probe(torch, nbytes=1 << 30, reps=10):
           flush=True)
 
 
+def context_probes(torch):
+    """Achievable streaming-read bandwidth and int8 MFMA rate on this GPU.
+
+    Context for the roofline fractions (which use the published peaks)."""
+    import ctypes
+
+    from w1_a8_matmul_amd.build import PROBES_LIBRARY
+
+    L = ctypes.CDLL(PROBES_LIBRARY)
+    L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_void_p]
+    L.probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    st = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+    out = {"probe": "context", "compute_units": cus}
+
+    # streaming read: sizes x buffer copies (copies rotate so that the small
+    # sizes stream from HBM rather than the 256 MB Infinity Cache)
+    for label, nbytes, copies in (("1GiB", 1 << 30, 1), ("2b_step_521MB", 521011200, 1),
+                                  ("gemv_4.4MB", 4423680, 61)):
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+        best = None
+        for wg_per_cu in (2, 4, 8):
+            grid = wg_per_cu * cus
+
+            def fn(i):
+                b = bufs[i % copies]
+                rc = L.probe_stream_read(b.data_ptr(), nbytes, sink.data_ptr(), grid, st())
+                assert rc == 0, rc
+
+            us = time_graph(torch, fn, 4 if copies == 1 else 200)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            if best is None or gbs > best[0]:
+                best = (round(gbs, 1), round(us, 3), wg_per_cu)
+        out[f"read_{label}"] = {"GBps": best[0], "us": best[1], "wg_per_cu": best[2]}
+        del bufs
+    # int8 matrix cores, random operand bytes
+    src = torch.randint(-2**31, 2**31 - 1, (4096,), dtype=torch.int32, device="cuda")
+    for shape, label, macs in ((0, "mfma_i32_16x16x64_i8", 8 * 16 * 16 * 64),
+                               (1, "mfma_i32_32x32x32_i8", 4 * 32 * 32 * 32)):
+        best = None
+        for wg_per_cu in (1, 2, 4):
+            grid, iters = wg_per_cu * cus, 2000
+
+            def fn(i):
+                rc = L.probe_mfma_i8(shape, src.data_ptr(), iters, sink.data_ptr(), grid, st())
+                assert rc == 0, rc
+
+            us = time_graph(torch, fn, 5)
+            tops = 2 * macs * iters * grid * 4 / (us * 1e-6) / 1e12
+            if best is None or tops > best[0]:
+                best = (round(tops, 1), wg_per_cu * 4)
+        out[label] = {"TOPS": best[0], "waves_per_cu": best[1]}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,6 +397,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_probe:
         copy_probe(torch)
+        return
+    if args.probes:
+        context_probes(torch)
         return
     bl.lib()
     dev = torch.device("cuda:0")

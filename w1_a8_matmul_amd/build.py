@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libbitlinear.so")
+# Measurement-only probes (streaming read, int8 matrix-core loop) for bench.py.
+PROBES_LIBRARY = os.path.join(PKG, "libbitlinear_probes.so")
+PROBES_SOURCES = ["probes.hip"]
 
 SOURCES = ["abi.cpp", "weights.hip", "acts.hip", "gemv.hip", "gemm.hip", "group.hip"]
 
@@ -46,16 +49,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build_library(jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIBRARY + ".tmp"
+def _link(objs, target: str) -> None:
+    tmp = target + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIBRARY)
+    os.replace(tmp, target)
+
+
+def build_library(jobs: int = 8) -> str:
+    """Builds libbitlinear.so and the probe library; returns the former's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBES_SOURCES
+    with ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIBRARY)
+    _link(objs[len(SOURCES):], PROBES_LIBRARY)
     return LIBRARY
 
 
