@@ -213,7 +213,7 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
 
 
 def roofline_grouped(args, torch, step, bytes_step, wk, M, n_lin):
-    """The grouped forward of a whole step (its quantizer launch included)."""
+    """The grouped forward of a whole step (one launch, quantization included)."""
     n = max(4, args.kernel_launches // 20)
     us = time_graph(torch, step, n)
     achieved = bytes_step / (us * 1e-6) / 1e9
@@ -222,7 +222,7 @@ def roofline_grouped(args, torch, step, bytes_step, wk, M, n_lin):
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(
                 source_hash(["group.hip", "group.hpp", "quant_row.hpp", "common.hpp"]), key),
-            "kernel": key, "kernel_us": round(us, 3), "launches_per_forward": 2}
+            "kernel": key, "kernel_us": round(us, 3), "launches_per_forward": 1}
     log(f"grouped forward: {us:.3f} us per step ({n_lin} linears)")
     return roof
 

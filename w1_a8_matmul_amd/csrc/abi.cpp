@@ -54,27 +54,20 @@ size_t q_workspace(int64_t M, int64_t K) {
   return align256((size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
 }
 
-// Grouped forward: device workspace layout.
-constexpr int kGroupMaxWG = 1024;
-constexpr int kGroupMaxK = 12288;
+// Grouped forward: device workspace layout (layer table, tile schedule).
+constexpr int kGroupMaxWG = 2048;
 
 struct GroupLayout {
-  size_t table, wg_begin, xq, sx, rs, total;
+  size_t table, wg_begin, total;
 };
 
-GroupLayout group_layout(const bitlinear_group_op* ops, int n_ops, int64_t M) {
+GroupLayout group_layout(int n_ops) {
   GroupLayout L;
   size_t off = 0;
   L.table = off;
   off += align256((size_t)n_ops * sizeof(GroupOp));
   L.wg_begin = off;
   off += align256((size_t)(kGroupMaxWG + 1) * sizeof(int));
-  L.xq = off;
-  for (int i = 0; i < n_ops; ++i) off += align256((size_t)M * (size_t)ops[i].K);
-  L.sx = off;
-  off += align256((size_t)n_ops * (size_t)M * 4);
-  L.rs = off;
-  off += align256((size_t)n_ops * (size_t)M * 4);
   L.total = off;
   return L;
 }
@@ -111,9 +104,6 @@ struct bitlinear_group {
   int max_k;
   GroupOp* ops;
   int* wg_begin;
-  int8_t* xq;
-  float* sx;
-  int32_t* rs;
 };
 
 extern "C" {
@@ -272,7 +262,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
 
 size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   if (check_group(ops, n_ops, M) != BITLINEAR_OK) return 0;
-  return group_layout(ops, n_ops, M).total;
+  return group_layout(n_ops).total;
 }
 
 bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops, int64_t M,
@@ -281,7 +271,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   *out = nullptr;
   bitlinear_status st = check_group(ops, n_ops, M);
   if (st != BITLINEAR_OK) return st;
-  const GroupLayout L = group_layout(ops, n_ops, M);
+  const GroupLayout L = group_layout(n_ops);
   if (!ws || ws_bytes < L.total)
     return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 ws ? ws_bytes : (size_t)0);
@@ -291,36 +281,34 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
-  // Two workgroups per compute unit: each holds one layer's int8 activations
-  // (at most 4 x 12288 bytes) in LDS.
-  int G = 2 * (cus > 0 ? cus : 1);
-  if (G > kGroupMaxWG) G = kGroupMaxWG;
-
   std::vector<GroupOp> table((size_t)n_ops);
-  std::vector<int64_t> weight_before;  // cumulative 1 KiB blocks before each tile
-  int64_t item = 0, xq_off = 0, total_blocks = 0;
+  int64_t item = 0, total_blocks = 0;
   int max_k = 0;
   for (int i = 0; i < n_ops; ++i) {
     const bitlinear_group_op& o = ops[i];
     GroupOp& t = table[(size_t)i];
+    t = GroupOp{};
     t.X = o.X;
     t.packed = o.packed;
     t.gamma = o.gamma;
     t.Y = o.Y;
-    t.xq_off = xq_off;
     t.K = (int32_t)o.K;
     t.N = (int32_t)o.N;
     t.dtype = (int32_t)o.dtype;
     t.relu2 = o.epi == BITLINEAR_EPI_RELU2 ? 1 : 0;
     t.item_begin = (int32_t)item;
-    const int kblocks = (int)(o.K / 256);
-    const int nc = (kblocks + 11) / 12;
-    t.chunk = (kblocks + nc - 1) / nc;
     item += o.N / 16;
-    total_blocks += (o.N / 16) * kblocks;
-    xq_off += (int64_t)align256((size_t)M * (size_t)o.K);
+    total_blocks += (o.N / 16) * (o.K / 256);
     if (o.K > max_k) max_k = (int)o.K;
   }
+  // As many workgroups as fit on the chip at once (each holds one layer's
+  // int8 activations in LDS), at most four per compute unit: the weights are
+  // split into that many contiguous streams.
+  int per_cu = bl_group_blocks_per_cu((int)M, max_k);
+  if (per_cu > 4) per_cu = 4;
+  int G = per_cu * (cus > 0 ? cus : 1);
+  if (G > kGroupMaxWG) G = kGroupMaxWG;
+
   // Byte-balanced contiguous tile ranges: workgroup g starts at the first
   // tile whose preceding weight reaches g/G of the total.
   std::vector<int> wg_begin((size_t)G + 1);
@@ -350,17 +338,14 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->max_k = max_k;
   g->ops = reinterpret_cast<GroupOp*>(base + L.table);
   g->wg_begin = reinterpret_cast<int*>(base + L.wg_begin);
-  g->xq = reinterpret_cast<int8_t*>(base + L.xq);
-  g->sx = reinterpret_cast<float*>(base + L.sx);
-  g->rs = reinterpret_cast<int32_t*>(base + L.rs);
   *out = g;
   return ok();
 }
 
 bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream) {
   if (!g) return fail(BITLINEAR_ERR_NULL, "group handle is required");
-  return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k, g->xq,
-                                  g->sx, g->rs, static_cast<hipStream_t>(stream)),
+  return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k,
+                                  static_cast<hipStream_t>(stream)),
                   "bitlinear_group_forward");
 }
 

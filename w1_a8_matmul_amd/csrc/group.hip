@@ -1,58 +1,37 @@
 // Grouped decode forward: many independent BitLinear layers (same token
-// count M <= 4) in two launches instead of one per layer.
+// count M <= 4) in one persistent launch instead of one launch per layer.
 //
-// Launch 1 quantizes every layer's activation rows per token (absmax, int8)
-// into a workspace.  Launch 2 is persistent: each workgroup owns a
-// contiguous, byte-balanced range of 16-row output tiles taken from the
-// concatenation of all layers, stages the int8 activations of the layer it
-// is working on in LDS, and its waves stream their tiles' packed weights
-// (double-buffered chunks of 16-byte lane loads, one 1 KiB tile per wave
-// load), unpack the 2-bit codes in registers and contract them with v_dot4.
-// One launch then keeps HBM busy across layer boundaries, where one launch
-// per layer pays its start-up and drain for every few megabytes.
+// Each workgroup owns a contiguous, byte-balanced range of 16-row output
+// tiles taken from the concatenation of all layers.  Whenever it starts on a
+// layer, the workgroup quantizes that layer's activation rows per token
+// (absmax, int8) into LDS itself -- a few kilobytes read from L2, cheaper
+// than a separate quantization launch -- while its waves' first weight
+// loads are already in flight.  Its waves then stream their tiles' packed
+// weights in chunks of 16-byte lane loads (one 1 KiB block
+// per wave load, two chunks per round), unpack the 2-bit codes in registers
+// and contract them with v_dot4.  One launch keeps HBM busy across layer boundaries, where one
+// launch per layer pays its start-up and drain for every few megabytes.
 //
 // The per-layer arithmetic is that of the single-layer forward: absmean
 // ternary weights and per-token absmax int8 activations ("BitNet b1.58 2B4T
 // Technical Report" card, section "Method Adaptation"), exact int32 sums,
 // ((float)acc * s_x) * gamma.
 #include "common.hpp"
+#include "gemv_tile.hpp"
 #include "group.hpp"
-#include "quant_row.hpp"
 
 namespace {
 
 using namespace bl;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kGroupThreads;
 constexpr int kWaves = kThreads / kWave;
-
-__global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restrict__ ops, int M,
-                                                          int8_t* __restrict__ xq,
-                                                          float* __restrict__ sx,
-                                                          int32_t* __restrict__ rs) {
-  __shared__ float red_f[4];
-  __shared__ int red_i[4];
-  const int op = blockIdx.x / M, m = blockIdx.x % M;
-  const GroupOp o = ops[op];
-  int8_t* dst = xq + o.xq_off + (int64_t)m * o.K;
-  RowQuant q;
-  int sum;
-  if (o.dtype == 1) {
-    q = row_absmax_scale<1, 256>(o.X, m, o.K, red_f);
-    sum = row_quantize_to<1, 256>(o.X, m, o.K, q.qs, dst, red_i);
-  } else {
-    q = row_absmax_scale<0, 256>(o.X, m, o.K, red_f);
-    sum = row_quantize_to<0, 256>(o.X, m, o.K, q.qs, dst, red_i);
-  }
-  if (threadIdx.x == 0) {
-    sx[op * M + m] = q.a_c / kQmax;
-    rs[op * M + m] = sum;
-  }
-}
+constexpr int kChunk = 6;        // column blocks per streamed chunk
+constexpr int kSegTiles = 64;    // tiles whose outputs are held in LDS at once
 
 // Unpack and contract one 16-byte lane chunk (64 columns of one row) with
-// the matching 64 int8 activations of every token; see the single-layer
-// kernel for the scale-1/4/16 accumulator trick.
+// the matching 64 int8 activations of every token (scale-1/4/16
+// accumulators, as in dot_word).
 template <int M>
 __device__ __forceinline__ void dot_chunk(const uint4 w, const int8_t* xs, int K, int col,
                                           int (&a0)[M], int (&a1)[M], int (&a2)[M]) {
@@ -64,160 +43,229 @@ __device__ __forceinline__ void dot_chunk(const uint4 w, const int8_t* xs, int K
     const int xd[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
                         x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t wd = words[g];
-      a0[m] = __builtin_amdgcn_sdot4((int)(wd & 0x03030303u), xd[4 * g + 0], a0[m], false);
-      a1[m] = __builtin_amdgcn_sdot4((int)(wd & 0x0c0c0c0cu), xd[4 * g + 1], a1[m], false);
-      a2[m] = __builtin_amdgcn_sdot4((int)(wd & 0x30303030u), xd[4 * g + 2], a2[m], false);
-      a2[m] = __builtin_amdgcn_sdot4((int)((wd >> 2) & 0x30303030u), xd[4 * g + 3], a2[m], false);
-    }
+    for (int g = 0; g < 4; ++g) dot_word(words[g], xd + 4 * g, a0[m], a1[m], a2[m]);
   }
 }
 
-// One wave works through tiles first, first+stride, ... < last of layer o.
-// Each tile is cut into chunks of C column blocks; the loads of the next
-// chunk are in flight while the current one is contracted.  Chunks past the
-// end use an empty buffer range and read zeros.
-template <int M, int C>
-__device__ __forceinline__ void run_tiles(const GroupOp& o, int first, int last, int stride,
-                                          const int8_t* xs, const float* s_sx, const int* s_rs,
-                                          int lane) {
+struct Smem {
+  float red_f[kWaves];
+  int red_i[kWaves];
+};
+
+// One layer segment: tiles first, first+stride, ... < last of layer o for
+// this wave.  Each tile is cut into chunks of kChunk column blocks.
+// Chunks past the end of a tile or of the wave's work use an empty or short
+// buffer range and read zeros.
+template <int M, int KCH, int DT>
+__device__ __forceinline__ void run_segment(const GroupOp& o, int first, int last, bool quantize,
+                                            int8_t* xs, float* s_sx, int* s_rs, float* s_y,
+                                            Smem& sm, int wave, int lane) {
+  constexpr int C = kChunk;
   const int K = o.K;
   const int kblocks = K / kTileCols;
   const int nc = (kblocks + C - 1) / C;
-  const int n_mine = first < last ? (last - first + stride - 1) / stride : 0;
+  const int stride = kWaves;
+  const int mine = first + wave;
+  const int n_mine = mine < last ? (last - mine + stride - 1) / stride : 0;
   const int total = n_mine * nc;
-  if (total == 0) return;
-  const float gamma = *o.gamma;
   const int sub = lane >> 4;
 
-  auto issue = [&](uint4 (&buf)[C], int j) {
+  // Chunk cursors (tile, chunk within the tile) advance with selects only:
+  // a branch here, or a division the compiler skips with one, would make it
+  // wait for every outstanding load where the paths join.
+  struct Cursor {
+    int it, c;
+  };
+  auto advance = [&](Cursor& q) {
+    const bool wrap = q.c + 1 == nc;
+    q.it = wrap ? q.it + stride : q.it;
+    q.c = wrap ? 0 : q.c + 1;
+  };
+  auto issue = [&](uint4 (&buf)[C], int j, const Cursor& q) {
     const bool valid = j < total;
-    const int it = first + (j / nc) * stride;
-    const int c = j % nc;
-    const int64_t tr = it - o.item_begin;
-    const auto r = make_rsrc(o.packed + (valid ? tr * (int64_t)kblocks * kTileBytes : 0),
+    const int tr = valid ? q.it - o.item_begin : 0;
+    const auto r = make_rsrc(o.packed + (int64_t)tr * kblocks * kTileBytes,
                              valid ? (uint32_t)kblocks * kTileBytes : 0u);
 #pragma unroll
-    for (int i = 0; i < C; ++i) buf[i] = buf_load16(r, lane * 16, (uint32_t)(c * C + i) * kTileBytes);
+    for (int i = 0; i < C; ++i)
+      buf[i] = buf_load16(r, lane * 16, (uint32_t)(q.c * C + i) * kTileBytes);
   };
 
+  // Activation row 0 first, then the first weight chunk, then the
+  // quantization (which waits for the row but not for the weights).
+  uint4 bufA[C], bufB[C];
+  Cursor qi{mine, 0};  // next chunk to issue
+  Cursor qc{mine, 0};  // next chunk to consume
+  if (quantize) {
+    Chunk<DT> ch[KCH];
+    load_row<DT, kThreads, KCH>(o.X, 0, K, ch);
+    issue(bufA, 0, qi);
+    quantize_row<DT, kThreads, KCH>(ch, K, xs, sm.red_f, sm.red_i, s_sx, s_rs);
+#pragma unroll
+    for (int m = 1; m < M; ++m) {
+      Chunk<DT> chm[KCH];
+      load_row<DT, kThreads, KCH>(o.X, m, K, chm);
+      quantize_row<DT, kThreads, KCH>(chm, K, xs + m * K, sm.red_f, sm.red_i, s_sx + m,
+                                      s_rs + m);
+    }
+  } else {
+    issue(bufA, 0, qi);
+  }
+  advance(qi);
+  __syncthreads();
+
+  const float gamma = *o.gamma;
   int a0[M], a1[M], a2[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) a0[m] = a1[m] = a2[m] = 0;
 
-  auto consume = [&](const uint4 (&buf)[C], int j) {
-    const int c = j % nc;
+  auto consume = [&](const uint4 (&buf)[C], int j, Cursor& q) {
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-      const int b = min(c * C + i, kblocks - 1);  // past the end: zero codes, any x
+      const int b = min(q.c * C + i, kblocks - 1);  // past the end: zero codes, any x
       dot_chunk<M>(buf[i], xs, K, b * kTileCols + sub * 64, a0, a1, a2);
     }
-    if (c == nc - 1) {
-      const int it = first + (j / nc) * stride;
-      const int64_t tr = it - o.item_begin;
+    if (q.c == nc - 1) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         int v = a0[m] + (a1[m] >> 2) + (a2[m] >> 4);
         v += __shfl_xor(v, 16, kWave);
         v += __shfl_xor(v, 32, kWave);
-        if (lane < kTileRows && j < total) {
-          const int64_t n = tr * kTileRows + lane;
-          o.Y[m * (int64_t)o.N + n] = rescale(v - s_rs[m], s_sx[m], gamma, o.relu2 != 0);
-        }
+        if (lane < kTileRows && j < total)
+          s_y[(m * kSegTiles + (q.it - first)) * kTileRows + lane] =
+              rescale(v - s_rs[m], s_sx[m], gamma, o.relu2 != 0);
         a0[m] = a1[m] = a2[m] = 0;
       }
     }
+    advance(q);
   };
 
-  uint4 bufA[C], bufB[C];
-  issue(bufA, 0);
-  for (int j = 0; j < total; j += 2) {
-    issue(bufB, j + 1);
-    consume(bufA, j);
-    issue(bufA, j + 2);
-    consume(bufB, j + 1);
+  // Rounds of four chunks through two buffers: while one chunk is
+  // contracted the next is in flight.  Every load is consumed within its
+  // round: a load whose result crosses a loop's back edge, or a branch
+  // around loads, makes the compiler wait for every outstanding load before
+  // the first use, which would serialize the chunks.  The first round (chunk
+  // 0 already in flight since before the quantization) runs
+  // unconditionally; a wave with no tiles reads zeros and stores nothing.
+  auto rest_of_round = [&](int j) {
+    issue(bufB, j + 1, qi);
+    advance(qi);
+    consume(bufA, j, qc);
+    issue(bufA, j + 2, qi);
+    advance(qi);
+    consume(bufB, j + 1, qc);
+    issue(bufB, j + 3, qi);
+    advance(qi);
+    consume(bufA, j + 2, qc);
+    consume(bufB, j + 3, qc);
+  };
+  rest_of_round(0);
+  for (int j = 4; j < total; j += 4) {
+    issue(bufA, j, qi);
+    advance(qi);
+    rest_of_round(j);
+  }
+
+  // Outputs of the segment's tiles, from LDS, in row order.  Stores are kept
+  // out of the streaming loop: with loads and stores outstanding together the
+  // compiler can no longer count loads in order and waits for all of them.
+  __syncthreads();
+  const int rows = (last - first) * kTileRows;
+  const int64_t n0 = (int64_t)(first - o.item_begin) * kTileRows;
+  for (int i = threadIdx.x; i < M * rows; i += kThreads) {
+    const int m = i / rows, r = i - m * rows;
+    o.Y[m * (int64_t)o.N + n0 + r] = s_y[m * kSegTiles * kTileRows + r];
   }
 }
 
-template <int M, int C>
-__device__ void run_tiles_c(const GroupOp& o, int first, int last, const int8_t* xs,
-                            const float* s_sx, const int* s_rs, int wave, int lane) {
-  run_tiles<M, C>(o, first + wave, last, kWaves, xs, s_sx, s_rs, lane);
-}
-
-template <int M>
-__global__ __launch_bounds__(kThreads) void group_gemv_kernel(
-    const GroupOp* __restrict__ ops, int n_ops, const int* __restrict__ wg_begin,
-    const int8_t* __restrict__ xq, const float* __restrict__ sx, const int* __restrict__ rs) {
+template <int M, int KCH>
+__global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restrict__ ops,
+                                                         int n_ops,
+                                                         const int* __restrict__ wg_begin) {
   extern __shared__ __align__(16) int8_t xs[];  // [M][K] of the current layer
   __shared__ float s_sx[M];
   __shared__ int s_rs[M];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ float s_y[M * kSegTiles * kTileRows];
+  __shared__ Smem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int item = wg_begin[blockIdx.x];
   const int end = wg_begin[blockIdx.x + 1];
   int op = 0;
   while (op + 1 < n_ops && ops[op + 1].item_begin <= item) ++op;
 
+  // Segments: runs of at most kSegTiles tiles of one layer.  The activations
+  // are quantized when a segment starts a new layer.
+  int quantized_op = -1;
   while (item < end) {
     const GroupOp o = ops[op];
-    const int seg_end = min(end, o.item_begin + o.N / kTileRows);
-    // Stage this layer's int8 activations (M*K bytes, a multiple of 256).
-    const int bytes = M * o.K;
-    const uint4* src = reinterpret_cast<const uint4*>(xq + o.xq_off);
-    for (int i = tid; i < bytes / 16; i += kThreads) reinterpret_cast<uint4*>(xs)[i] = src[i];
-    if (tid < M) {
-      s_sx[tid] = sx[op * M + tid];
-      s_rs[tid] = rs[op * M + tid];
-    }
-    __syncthreads();
-    switch (o.chunk) {
-      case 1: run_tiles_c<M, 1>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 2: run_tiles_c<M, 2>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 3: run_tiles_c<M, 3>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 4: run_tiles_c<M, 4>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 5: run_tiles_c<M, 5>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 6: run_tiles_c<M, 6>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 7: run_tiles_c<M, 7>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 8: run_tiles_c<M, 8>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 9: run_tiles_c<M, 9>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 10: run_tiles_c<M, 10>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      case 11: run_tiles_c<M, 11>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-      default: run_tiles_c<M, 12>(o, item, seg_end, xs, s_sx, s_rs, wave, lane); break;
-    }
-    __syncthreads();  // before the next layer overwrites xs
+    const int op_end = o.item_begin + o.N / kTileRows;
+    const int seg_end = min(min(end, op_end), item + kSegTiles);
+    const bool quantize = quantized_op != op;
+    if (o.dtype == 1)
+      run_segment<M, KCH, 1>(o, item, seg_end, quantize, xs, s_sx, s_rs, s_y, sm, wave, lane);
+    else
+      run_segment<M, KCH, 0>(o, item, seg_end, quantize, xs, s_sx, s_rs, s_y, sm, wave, lane);
+    __syncthreads();  // before the next segment overwrites xs, the scales or s_y
+    quantized_op = op;
     item = seg_end;
-    ++op;
+    if (item == op_end) ++op;
   }
+}
+
+// Activation chunks per thread: 2, 4 or 6 cover rows of up to 4096, 8192
+// and 12288 elements.
+template <int M>
+const void* kernel_for(int max_k) {
+  if (max_k <= 4096) return reinterpret_cast<const void*>(&group_kernel<M, 2>);
+  if (max_k <= 8192) return reinterpret_cast<const void*>(&group_kernel<M, 4>);
+  return reinterpret_cast<const void*>(&group_kernel<M, 6>);
+}
+
+const void* kernel_for_m(int M, int max_k) {
+  switch (M) {
+    case 1: return kernel_for<1>(max_k);
+    case 2: return kernel_for<2>(max_k);
+    case 3: return kernel_for<3>(max_k);
+    default: return kernel_for<4>(max_k);
+  }
+}
+
+template <int M, int KCH>
+void launch(const GroupOp* ops, int n_ops, const int* wg_begin, int G, size_t lds,
+            hipStream_t s) {
+  hipLaunchKernelGGL((group_kernel<M, KCH>), dim3(G), dim3(kThreads), lds, s, ops, n_ops,
+                     wg_begin);
+}
+
+template <int M>
+void launch_m(const GroupOp* ops, int n_ops, const int* wg_begin, int G, int max_k,
+              hipStream_t s) {
+  const size_t lds = bl_group_lds_bytes(M, max_k);
+  if (max_k <= 4096)
+    launch<M, 2>(ops, n_ops, wg_begin, G, lds, s);
+  else if (max_k <= 8192)
+    launch<M, 4>(ops, n_ops, wg_begin, G, lds, s);
+  else
+    launch<M, 6>(ops, n_ops, wg_begin, G, lds, s);
 }
 
 }  // namespace
 
+int bl_group_blocks_per_cu(int M, int max_k) {
+  int blocks = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &blocks, kernel_for_m(M, max_k), kThreads, bl_group_lds_bytes(M, max_k));
+  return (e == hipSuccess && blocks > 0) ? blocks : 1;
+}
+
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
-                           int max_k, int8_t* xq, float* sx, int32_t* rs, hipStream_t s) {
-  hipLaunchKernelGGL(group_quant_kernel, dim3((unsigned)(n_ops * M)), dim3(256), 0, s, ops, M,
-                     xq, sx, rs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t lds = (size_t)M * (size_t)max_k;
+                           int max_k, hipStream_t s) {
   switch (M) {
-    case 1:
-      hipLaunchKernelGGL(group_gemv_kernel<1>, dim3(G), dim3(kThreads), lds, s, ops, n_ops,
-                         wg_begin, xq, sx, rs);
-      break;
-    case 2:
-      hipLaunchKernelGGL(group_gemv_kernel<2>, dim3(G), dim3(kThreads), lds, s, ops, n_ops,
-                         wg_begin, xq, sx, rs);
-      break;
-    case 3:
-      hipLaunchKernelGGL(group_gemv_kernel<3>, dim3(G), dim3(kThreads), lds, s, ops, n_ops,
-                         wg_begin, xq, sx, rs);
-      break;
-    default:
-      hipLaunchKernelGGL(group_gemv_kernel<4>, dim3(G), dim3(kThreads), lds, s, ops, n_ops,
-                         wg_begin, xq, sx, rs);
-      break;
+    case 1: launch_m<1>(ops, n_ops, wg_begin, G, max_k, s); break;
+    case 2: launch_m<2>(ops, n_ops, wg_begin, G, max_k, s); break;
+    case 3: launch_m<3>(ops, n_ops, wg_begin, G, max_k, s); break;
+    default: launch_m<4>(ops, n_ops, wg_begin, G, max_k, s); break;
   }
   return hipGetLastError();
 }
