@@ -164,7 +164,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      float* Y, bitlinear_epilogue epi, void* stream);
 
 /* ---- Grouped decode forward ------------------------------------------------
- * Many independent BitLinear layers that share the token count M (1..4), run
+ * Many independent BitLinear layers that share the token count M (1..16), run
  * as one persistent launch that streams the packed weights of all layers
  * back to back (each workgroup quantizes the activations of the layers it
  * works on itself).  Each layer's result is bit-identical to
@@ -175,7 +175,8 @@ typedef struct {
   const void* X;          /* [M][K] activations, device, 16-byte aligned */
   bitlinear_dtype dtype;  /* BITLINEAR_F32 or BITLINEAR_BF16 */
   bitlinear_epilogue epi; /* BITLINEAR_EPI_NONE or BITLINEAR_EPI_RELU2 */
-  int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 12288 */
+  int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 12288, and
+                             M * (max K + 16) + M * 2048 <= 160 KiB */
   const uint8_t* packed;  /* packed weights of this layer */
   const float* gamma;     /* gamma_c of this layer (device float) */
   float* Y;               /* [M][N] output; must not overlap any layer's input */

@@ -315,7 +315,7 @@ def _group_layers(dev, bl, orc, M, shapes, seed0):
     return layers, refs
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11])
 def test_group_forward_matches_oracle(dev, bl, orc, M):
     layers, refs = _group_layers(dev, bl, orc, M, GROUP_SHAPES, 7000 + 100 * M)
     g = bl.Group(layers)
@@ -328,6 +328,18 @@ def test_group_forward_matches_oracle(dev, bl, orc, M):
     again = g.forward()
     for y, y2 in zip(outs, again):
         assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_group_2b_layer(dev, bl, orc, M):
+    # one 2B-shape layer (QKV, O, gate+up, down) at the decode step's token counts
+    shapes = [(l.K, l.N, "normal_bf16", None) for l in wl.LAYER_2B]
+    layers, refs = _group_layers(dev, bl, orc, M, shapes, 7800 + M)
+    g = bl.Group(layers)
+    outs = g.forward()
+    torch.cuda.synchronize()
+    for y, y_ref in zip(outs, refs):
+        assert np.array_equal(y.cpu().numpy(), y_ref)
 
 
 def test_group_2b_layer_graph_replay(dev, bl, orc):

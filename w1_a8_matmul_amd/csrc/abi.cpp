@@ -75,7 +75,8 @@ GroupLayout group_layout(int n_ops) {
 bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   if (!ops) return fail(BITLINEAR_ERR_NULL, "ops is required");
   if (n_ops < 1 || n_ops > 65536) return fail(BITLINEAR_ERR_ARG, "n_ops=%d out of range", n_ops);
-  if (M < 1 || M > 4) return fail(BITLINEAR_ERR_SHAPE, "grouped forward needs 1 <= M <= 4, got %lld", (long long)M);
+  if (M < 1 || M > kGroupMaxM)
+    return fail(BITLINEAR_ERR_SHAPE, "grouped forward needs 1 <= M <= %d, got %lld", kGroupMaxM, (long long)M);
   int64_t items = 0;
   for (int i = 0; i < n_ops; ++i) {
     const bitlinear_group_op& o = ops[i];
@@ -92,6 +93,12 @@ bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M
     items += o.N / 16;
   }
   if (items > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "too many output tiles");
+  int64_t max_k = 0;
+  for (int i = 0; i < n_ops; ++i) max_k = ops[i].K > max_k ? ops[i].K : max_k;
+  if (bl_group_lds_bytes((int)M, (int)max_k) > kGroupMaxLds)
+    return fail(BITLINEAR_ERR_SHAPE,
+                "M=%lld tokens of K=%lld activations do not fit in LDS (M * (K + 16) + M * 2048 "
+                "bytes must stay within %zu)", (long long)M, (long long)max_k, kGroupMaxLds);
   return BITLINEAR_OK;
 }
 
@@ -304,6 +311,8 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   // As many workgroups as fit on the chip at once (each holds one layer's
   // int8 activations in LDS), at most four per compute unit: the weights are
   // split into that many contiguous streams.
+  e = bl_group_prepare((int)M, max_k);
+  if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   int per_cu = bl_group_blocks_per_cu((int)M, max_k);
   if (per_cu > 4) per_cu = 4;
   int G = per_cu * (cus > 0 ? cus : 1);

@@ -1,5 +1,5 @@
 // Grouped decode forward: many independent BitLinear layers (same token
-// count M <= 4) in one persistent launch instead of one launch per layer.
+// count M <= 16) in one persistent launch instead of one launch per layer.
 //
 // Each workgroup owns a contiguous, byte-balanced range of 16-row output
 // tiles taken from the concatenation of all layers.  Whenever it starts on a
@@ -27,23 +27,27 @@ using namespace bl;
 constexpr int kThreads = kGroupThreads;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 6;        // column blocks per streamed chunk
-constexpr int kSegTiles = 64;    // tiles whose outputs are held in LDS at once
+constexpr int kSegTiles = 32;    // tiles whose outputs are held in LDS at once
 
-// Unpack and contract one 16-byte lane chunk (64 columns of one row) with
-// the matching 64 int8 activations of every token (scale-1/4/16
-// accumulators, as in dot_word).
-template <int M>
-__device__ __forceinline__ void dot_chunk(const uint4 w, const int8_t* xs, int K, int col,
-                                          int (&a0)[M], int (&a1)[M], int (&a2)[M]) {
+// One 1 KiB block of a 16-row tile on the matrix cores.  Lane l loaded
+// row l%16 of the tile, columns 64q .. 64q+63 of the block (q = l/16), as
+// four words; word w holds the codes of columns 64q + 16w .. +15.  MFMA w
+// contracts, for every lane, those 16 columns of tile row l%16 (B) with the
+// same 16 columns of token row l%16 (A, 16 bytes from LDS): the four MFMAs
+// together cover the block's 256 columns for all 16 x 16 (token, row)
+// pairs.  Two accumulators halve the dependent chain.
+__device__ __forceinline__ void mfma_block(const uint4 w, const int8_t* xa, v4i& acc0,
+                                           v4i& acc1) {
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int4* xp = reinterpret_cast<const int4*>(xs + m * K + col);
-    const int4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
-    const int xd[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                        x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-#pragma unroll
-    for (int g = 0; g < 4; ++g) dot_word(words[g], xd + 4 * g, a0[m], a1[m], a2[m]);
+  for (int k = 0; k < 4; ++k) {
+    const v4i a = *reinterpret_cast<const v4i*>(xa + 16 * k);
+    const uint32_t wd = words[k];
+    const v4i b = v4i{(int)codes(wd, 0), (int)codes(wd, 1), (int)codes(wd, 2), (int)codes(wd, 3)};
+    if (k % 2 == 0)
+      acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc0, 0, 0, 0);
+    else
+      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc1, 0, 0, 0);
   }
 }
 
@@ -56,10 +60,11 @@ struct Smem {
 // this wave.  Each tile is cut into chunks of kChunk column blocks.
 // Chunks past the end of a tile or of the wave's work use an empty or short
 // buffer range and read zeros.
-template <int M, int KCH, int DT>
-__device__ __forceinline__ void run_segment(const GroupOp& o, int first, int last, bool quantize,
-                                            int8_t* xs, float* s_sx, int* s_rs, float* s_y,
-                                            Smem& sm, int wave, int lane) {
+template <int KCH, int DT>
+__device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, int last,
+                                            bool quantize, int8_t* xs, int xstride,
+                                            float* s_sx, int* s_rs, float* s_y, Smem& sm,
+                                            int wave, int lane) {
   constexpr int C = kChunk;
   const int K = o.K;
   const int kblocks = K / kTileCols;
@@ -68,7 +73,8 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int first, int las
   const int mine = first + wave;
   const int n_mine = mine < last ? (last - mine + stride - 1) / stride : 0;
   const int total = n_mine * nc;
-  const int sub = lane >> 4;
+  const int q16 = lane >> 4;                     // 64-column quarter held by this lane
+  const int arow = min(lane & 15, M - 1);        // token row of this lane's A operand
 
   // Chunk cursors (tile, chunk within the tile) advance with selects only:
   // a branch here, or a division the compiler skips with one, would make it
@@ -101,11 +107,10 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int first, int las
     load_row<DT, kThreads, KCH>(o.X, 0, K, ch);
     issue(bufA, 0, qi);
     quantize_row<DT, kThreads, KCH>(ch, K, xs, sm.red_f, sm.red_i, s_sx, s_rs);
-#pragma unroll
     for (int m = 1; m < M; ++m) {
       Chunk<DT> chm[KCH];
       load_row<DT, kThreads, KCH>(o.X, m, K, chm);
-      quantize_row<DT, kThreads, KCH>(chm, K, xs + m * K, sm.red_f, sm.red_i, s_sx + m,
+      quantize_row<DT, kThreads, KCH>(chm, K, xs + m * xstride, sm.red_f, sm.red_i, s_sx + m,
                                       s_rs + m);
     }
   } else {
@@ -115,27 +120,27 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int first, int las
   __syncthreads();
 
   const float gamma = *o.gamma;
-  int a0[M], a1[M], a2[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) a0[m] = a1[m] = a2[m] = 0;
+  const int8_t* xrow = xs + arow * xstride + q16 * 64;
+  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
 
+  // D layout: lane l holds tile row l%16 and tokens 4*(l/16) + r, r = 0..3.
   auto consume = [&](const uint4 (&buf)[C], int j, Cursor& q) {
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int b = min(q.c * C + i, kblocks - 1);  // past the end: zero codes, any x
-      dot_chunk<M>(buf[i], xs, K, b * kTileCols + sub * 64, a0, a1, a2);
+      mfma_block(buf[i], xrow + b * kTileCols, acc0, acc1);
     }
     if (q.c == nc - 1) {
+      const v4i d = acc0 + acc1;
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        int v = a0[m] + (a1[m] >> 2) + (a2[m] >> 4);
-        v += __shfl_xor(v, 16, kWave);
-        v += __shfl_xor(v, 32, kWave);
-        if (lane < kTileRows && j < total)
-          s_y[(m * kSegTiles + (q.it - first)) * kTileRows + lane] =
-              rescale(v - s_rs[m], s_sx[m], gamma, o.relu2 != 0);
-        a0[m] = a1[m] = a2[m] = 0;
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * q16 + r;
+        if (m < M && j < total)
+          s_y[(m * kSegTiles + (q.it - first)) * kTileRows + (lane & 15)] =
+              rescale(d[r] - s_rs[m], s_sx[m], gamma, o.relu2 != 0);
       }
+      acc0 = v4i{0, 0, 0, 0};
+      acc1 = v4i{0, 0, 0, 0};
     }
     advance(q);
   };
@@ -178,14 +183,19 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int first, int las
   }
 }
 
-template <int M, int KCH>
+template <int KCH>
 __global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restrict__ ops,
-                                                         int n_ops,
+                                                         int n_ops, int M, int max_k,
                                                          const int* __restrict__ wg_begin) {
-  extern __shared__ __align__(16) int8_t xs[];  // [M][K] of the current layer
-  __shared__ float s_sx[M];
-  __shared__ int s_rs[M];
-  __shared__ float s_y[M * kSegTiles * kTileRows];
+  // Dynamic LDS: int8 activations [M][max_k + 16] of the current layer (rows
+  // padded by 16 bytes so that the 16 token rows of an A-operand read fall in
+  // distinct banks), then the segment's outputs [M][kSegTiles][16] floats.
+  extern __shared__ __align__(16) int8_t dyn[];
+  const int xstride = max_k + 16;
+  int8_t* xs = dyn;
+  float* s_y = reinterpret_cast<float*>(dyn + (size_t)M * xstride);
+  __shared__ float s_sx[kGroupMaxM];
+  __shared__ int s_rs[kGroupMaxM];
   __shared__ Smem sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -203,9 +213,11 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restri
     const int seg_end = min(min(end, op_end), item + kSegTiles);
     const bool quantize = quantized_op != op;
     if (o.dtype == 1)
-      run_segment<M, KCH, 1>(o, item, seg_end, quantize, xs, s_sx, s_rs, s_y, sm, wave, lane);
+      run_segment<KCH, 1>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm, wave,
+                          lane);
     else
-      run_segment<M, KCH, 0>(o, item, seg_end, quantize, xs, s_sx, s_rs, s_y, sm, wave, lane);
+      run_segment<KCH, 0>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm, wave,
+                          lane);
     __syncthreads();  // before the next segment overwrites xs, the scales or s_y
     quantized_op = op;
     item = seg_end;
@@ -215,57 +227,43 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restri
 
 // Activation chunks per thread: 2, 4 or 6 cover rows of up to 4096, 8192
 // and 12288 elements.
-template <int M>
 const void* kernel_for(int max_k) {
-  if (max_k <= 4096) return reinterpret_cast<const void*>(&group_kernel<M, 2>);
-  if (max_k <= 8192) return reinterpret_cast<const void*>(&group_kernel<M, 4>);
-  return reinterpret_cast<const void*>(&group_kernel<M, 6>);
-}
-
-const void* kernel_for_m(int M, int max_k) {
-  switch (M) {
-    case 1: return kernel_for<1>(max_k);
-    case 2: return kernel_for<2>(max_k);
-    case 3: return kernel_for<3>(max_k);
-    default: return kernel_for<4>(max_k);
-  }
-}
-
-template <int M, int KCH>
-void launch(const GroupOp* ops, int n_ops, const int* wg_begin, int G, size_t lds,
-            hipStream_t s) {
-  hipLaunchKernelGGL((group_kernel<M, KCH>), dim3(G), dim3(kThreads), lds, s, ops, n_ops,
-                     wg_begin);
-}
-
-template <int M>
-void launch_m(const GroupOp* ops, int n_ops, const int* wg_begin, int G, int max_k,
-              hipStream_t s) {
-  const size_t lds = bl_group_lds_bytes(M, max_k);
-  if (max_k <= 4096)
-    launch<M, 2>(ops, n_ops, wg_begin, G, lds, s);
-  else if (max_k <= 8192)
-    launch<M, 4>(ops, n_ops, wg_begin, G, lds, s);
-  else
-    launch<M, 6>(ops, n_ops, wg_begin, G, lds, s);
+  if (max_k <= 4096) return reinterpret_cast<const void*>(&group_kernel<2>);
+  if (max_k <= 8192) return reinterpret_cast<const void*>(&group_kernel<4>);
+  return reinterpret_cast<const void*>(&group_kernel<6>);
 }
 
 }  // namespace
 
+size_t bl_group_lds_bytes(int M, int max_k) {
+  return (size_t)M * (size_t)(max_k + 16) + (size_t)M * kSegTiles * kTileRows * sizeof(float);
+}
+
+hipError_t bl_group_prepare(int M, int max_k) {
+  const size_t lds = bl_group_lds_bytes(M, max_k);
+  if (lds <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(kernel_for(max_k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
+}
+
 int bl_group_blocks_per_cu(int M, int max_k) {
   int blocks = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks, kernel_for_m(M, max_k), kThreads, bl_group_lds_bytes(M, max_k));
+      &blocks, kernel_for(max_k), kThreads, bl_group_lds_bytes(M, max_k));
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
                            int max_k, hipStream_t s) {
-  switch (M) {
-    case 1: launch_m<1>(ops, n_ops, wg_begin, G, max_k, s); break;
-    case 2: launch_m<2>(ops, n_ops, wg_begin, G, max_k, s); break;
-    case 3: launch_m<3>(ops, n_ops, wg_begin, G, max_k, s); break;
-    default: launch_m<4>(ops, n_ops, wg_begin, G, max_k, s); break;
-  }
+  const size_t lds = bl_group_lds_bytes(M, max_k);
+  if (max_k <= 4096)
+    hipLaunchKernelGGL((group_kernel<2>), dim3(G), dim3(kThreads), lds, s, ops, n_ops, M, max_k,
+                       wg_begin);
+  else if (max_k <= 8192)
+    hipLaunchKernelGGL((group_kernel<4>), dim3(G), dim3(kThreads), lds, s, ops, n_ops, M, max_k,
+                       wg_begin);
+  else
+    hipLaunchKernelGGL((group_kernel<6>), dim3(G), dim3(kThreads), lds, s, ops, n_ops, M, max_k,
+                       wg_begin);
   return hipGetLastError();
 }

@@ -17,12 +17,20 @@ struct GroupOp {
 };
 static_assert(sizeof(GroupOp) == 64, "GroupOp must stay 64 bytes");
 
-// Largest K of a grouped layer, and the kernel's workgroup size.
+// Largest K of a grouped layer, largest token count, and the kernel's
+// workgroup size.
 constexpr int kGroupMaxK = 12288;
+constexpr int kGroupMaxM = 16;
 constexpr int kGroupThreads = 256;
 
 // Dynamic LDS bytes of the grouped kernel for M tokens and largest K.
-inline size_t bl_group_lds_bytes(int M, int max_k) { return (size_t)M * (size_t)max_k; }
+size_t bl_group_lds_bytes(int M, int max_k);
+
+// LDS available to one workgroup.
+constexpr size_t kGroupMaxLds = 160 * 1024;
+
+// Allows the kernel the dynamic LDS this group needs (above the default).
+hipError_t bl_group_prepare(int M, int max_k);
 
 // Workgroups of the grouped kernel that fit on one compute unit at once.
 int bl_group_blocks_per_cu(int M, int max_k);
