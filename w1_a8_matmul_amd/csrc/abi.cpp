@@ -109,6 +109,7 @@ struct bitlinear_group {
   int M;
   int G;
   int max_k;
+  int threads;
   GroupOp* ops;
   int* wg_begin;
 };
@@ -311,9 +312,9 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   // As many workgroups as fit on the chip at once (each holds one layer's
   // int8 activations in LDS), at most four per compute unit: the weights are
   // split into that many contiguous streams.
-  e = bl_group_prepare((int)M, max_k);
+  int threads = 256, per_cu = 1;
+  e = bl_group_plan((int)M, max_k, &threads, &per_cu);
   if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
-  int per_cu = bl_group_blocks_per_cu((int)M, max_k);
   if (per_cu > 4) per_cu = 4;
   int G = per_cu * (cus > 0 ? cus : 1);
   if (G > kGroupMaxWG) G = kGroupMaxWG;
@@ -345,6 +346,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->M = (int)M;
   g->G = G;
   g->max_k = max_k;
+  g->threads = threads;
   g->ops = reinterpret_cast<GroupOp*>(base + L.table);
   g->wg_begin = reinterpret_cast<int*>(base + L.wg_begin);
   *out = g;
@@ -354,7 +356,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
 bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream) {
   if (!g) return fail(BITLINEAR_ERR_NULL, "group handle is required");
   return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k,
-                                  static_cast<hipStream_t>(stream)),
+                                  g->threads, static_cast<hipStream_t>(stream)),
                   "bitlinear_group_forward");
 }
 

@@ -24,8 +24,6 @@ namespace {
 
 using namespace bl;
 
-constexpr int kThreads = kGroupThreads;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 6;        // column blocks per streamed chunk
 constexpr int kSegTiles = 32;    // tiles whose outputs are held in LDS at once
 
@@ -51,20 +49,23 @@ __device__ __forceinline__ void mfma_block(const uint4 w, const int8_t* xa, v4i&
   }
 }
 
+template <int NT>
 struct Smem {
-  float red_f[kWaves];
-  int red_i[kWaves];
+  float red_f[NT / kWave];
+  int red_i[NT / kWave];
 };
 
 // One layer segment: tiles first, first+stride, ... < last of layer o for
 // this wave.  Each tile is cut into chunks of kChunk column blocks.
 // Chunks past the end of a tile or of the wave's work use an empty or short
 // buffer range and read zeros.
-template <int KCH, int DT>
+template <int NT, int KCH, int DT>
 __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, int last,
                                             bool quantize, int8_t* xs, int xstride,
-                                            float* s_sx, int* s_rs, float* s_y, Smem& sm,
+                                            float* s_sx, int* s_rs, float* s_y, Smem<NT>& sm,
                                             int wave, int lane) {
+  constexpr int kThreads = NT;
+  constexpr int kWaves = NT / kWave;
   constexpr int C = kChunk;
   const int K = o.K;
   const int kblocks = K / kTileCols;
@@ -183,8 +184,8 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   }
 }
 
-template <int KCH>
-__global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restrict__ ops,
+template <int NT, int KCH>
+__global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops,
                                                          int n_ops, int M, int max_k,
                                                          const int* __restrict__ wg_begin) {
   // Dynamic LDS: int8 activations [M][max_k + 16] of the current layer (rows
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restri
   float* s_y = reinterpret_cast<float*>(dyn + (size_t)M * xstride);
   __shared__ float s_sx[kGroupMaxM];
   __shared__ int s_rs[kGroupMaxM];
-  __shared__ Smem sm;
+  __shared__ Smem<NT> sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int item = wg_begin[blockIdx.x];
@@ -213,11 +214,11 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restri
     const int seg_end = min(min(end, op_end), item + kSegTiles);
     const bool quantize = quantized_op != op;
     if (o.dtype == 1)
-      run_segment<KCH, 1>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm, wave,
-                          lane);
+      run_segment<NT, KCH, 1>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm,
+                              wave, lane);
     else
-      run_segment<KCH, 0>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm, wave,
-                          lane);
+      run_segment<NT, KCH, 0>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm,
+                              wave, lane);
     __syncthreads();  // before the next segment overwrites xs, the scales or s_y
     quantized_op = op;
     item = seg_end;
@@ -225,12 +226,37 @@ __global__ __launch_bounds__(kThreads) void group_kernel(const GroupOp* __restri
   }
 }
 
-// Activation chunks per thread: 2, 4 or 6 cover rows of up to 4096, 8192
-// and 12288 elements.
+// Activation chunks per thread: each covers NT * 8 elements of a row.
+template <int NT>
 const void* kernel_for(int max_k) {
-  if (max_k <= 4096) return reinterpret_cast<const void*>(&group_kernel<2>);
-  if (max_k <= 8192) return reinterpret_cast<const void*>(&group_kernel<4>);
-  return reinterpret_cast<const void*>(&group_kernel<6>);
+  if (max_k <= NT * 8 * 2) return reinterpret_cast<const void*>(&group_kernel<NT, 2>);
+  if (max_k <= NT * 8 * 4) return reinterpret_cast<const void*>(&group_kernel<NT, 4>);
+  return reinterpret_cast<const void*>(&group_kernel<NT, 6>);
+}
+
+const void* kernel_for(int threads, int max_k) {
+  return threads == 512 ? kernel_for<512>(max_k) : kernel_for<256>(max_k);
+}
+
+template <int NT>
+void launch(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G, int max_k,
+            size_t lds, hipStream_t s) {
+  if (max_k <= NT * 8 * 2)
+    hipLaunchKernelGGL((group_kernel<NT, 2>), dim3(G), dim3(NT), lds, s, ops, n_ops, M, max_k,
+                       wg_begin);
+  else if (max_k <= NT * 8 * 4)
+    hipLaunchKernelGGL((group_kernel<NT, 4>), dim3(G), dim3(NT), lds, s, ops, n_ops, M, max_k,
+                       wg_begin);
+  else
+    hipLaunchKernelGGL((group_kernel<NT, 6>), dim3(G), dim3(NT), lds, s, ops, n_ops, M, max_k,
+                       wg_begin);
+}
+
+int blocks_per_cu(int threads, size_t lds, int max_k) {
+  int blocks = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &blocks, kernel_for(threads, max_k), threads, lds);
+  return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 }  // namespace
@@ -239,31 +265,35 @@ size_t bl_group_lds_bytes(int M, int max_k) {
   return (size_t)M * (size_t)(max_k + 16) + (size_t)M * kSegTiles * kTileRows * sizeof(float);
 }
 
-hipError_t bl_group_prepare(int M, int max_k) {
+hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
-  if (lds <= 64 * 1024) return hipSuccess;
-  return hipFuncSetAttribute(kernel_for(max_k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)lds);
-}
-
-int bl_group_blocks_per_cu(int M, int max_k) {
-  int blocks = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks, kernel_for(max_k), kThreads, bl_group_lds_bytes(M, max_k));
-  return (e == hipSuccess && blocks > 0) ? blocks : 1;
+  for (int nt : {256, 512}) {
+    if (lds > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(
+          kernel_for(nt, max_k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+  }
+  // Four-wave workgroups while at least two fit on a compute unit (more,
+  // shorter weight streams); eight-wave ones when the activations take so
+  // much LDS that only one does.
+  const int b256 = blocks_per_cu(256, lds, max_k);
+  if (b256 >= 2) {
+    *threads = 256;
+    *per_cu = b256;
+  } else {
+    *threads = 512;
+    *per_cu = blocks_per_cu(512, lds, max_k);
+  }
+  return hipSuccess;
 }
 
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
-                           int max_k, hipStream_t s) {
+                           int max_k, int threads, hipStream_t s) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
-  if (max_k <= 4096)
-    hipLaunchKernelGGL((group_kernel<2>), dim3(G), dim3(kThreads), lds, s, ops, n_ops, M, max_k,
-                       wg_begin);
-  else if (max_k <= 8192)
-    hipLaunchKernelGGL((group_kernel<4>), dim3(G), dim3(kThreads), lds, s, ops, n_ops, M, max_k,
-                       wg_begin);
+  if (threads == 512)
+    launch<512>(ops, n_ops, M, wg_begin, G, max_k, lds, s);
   else
-    hipLaunchKernelGGL((group_kernel<6>), dim3(G), dim3(kThreads), lds, s, ops, n_ops, M, max_k,
-                       wg_begin);
+    launch<256>(ops, n_ops, M, wg_begin, G, max_k, lds, s);
   return hipGetLastError();
 }

@@ -17,25 +17,22 @@ struct GroupOp {
 };
 static_assert(sizeof(GroupOp) == 64, "GroupOp must stay 64 bytes");
 
-// Largest K of a grouped layer, largest token count, and the kernel's
-// workgroup size.
+// Largest K of a grouped layer and largest token count.
 constexpr int kGroupMaxK = 12288;
 constexpr int kGroupMaxM = 16;
-constexpr int kGroupThreads = 256;
-
-// Dynamic LDS bytes of the grouped kernel for M tokens and largest K.
-size_t bl_group_lds_bytes(int M, int max_k);
 
 // LDS available to one workgroup.
 constexpr size_t kGroupMaxLds = 160 * 1024;
 
-// Allows the kernel the dynamic LDS this group needs (above the default).
-hipError_t bl_group_prepare(int M, int max_k);
+// Dynamic LDS bytes of the grouped kernel for M tokens and largest K.
+size_t bl_group_lds_bytes(int M, int max_k);
 
-// Workgroups of the grouped kernel that fit on one compute unit at once.
-int bl_group_blocks_per_cu(int M, int max_k);
+// Chooses the workgroup size (256 or 512 threads) and reports how many
+// workgroups fit on one compute unit; also allows the kernel the dynamic
+// LDS it needs.
+hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu);
 
 // Grouped forward: one launch.  wg_begin[g]..wg_begin[g+1] is workgroup g's
-// tile range; G workgroups; max_k the largest K of the group.
+// tile range; G workgroups of `threads` threads; max_k the largest K.
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
-                           int max_k, hipStream_t s);
+                           int max_k, int threads, hipStream_t s);
