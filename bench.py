@@ -222,7 +222,8 @@ def roofline_grouped(args, torch, step, bytes_step, wk, M, n_lin):
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(
                 source_hash(["group.hip", "group.hpp", "quant_row.hpp", "common.hpp"]), key),
-            "kernel": key, "kernel_us": round(us, 3), "launches_per_forward": 1}
+            "kernel": key, "kernel_us": round(us, 3),
+            "launches_per_forward": 1 if M <= 4 else 2}
     log(f"grouped forward: {us:.3f} us per step ({n_lin} linears)")
     return roof
 

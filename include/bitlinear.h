@@ -166,8 +166,9 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
 /* ---- Grouped decode forward ------------------------------------------------
  * Many independent BitLinear layers that share the token count M (1..16), run
  * as one persistent launch that streams the packed weights of all layers
- * back to back (each workgroup quantizes the activations of the layers it
- * works on itself).  Each layer's result is bit-identical to
+ * back to back.  Up to 4 tokens each workgroup quantizes the activations of
+ * the layers it works on itself; above, one more launch quantizes them first
+ * into the workspace.  Each layer's result is bit-identical to
  * bitlinear_forward on the same arguments.  Intended for decode, where one
  * launch per layer of a few megabytes is dominated by the launch's start-up
  * and drain. */
@@ -186,7 +187,8 @@ typedef struct {
 typedef struct bitlinear_group bitlinear_group;
 
 /* Device workspace bytes for a group of n_ops layers at M tokens (the layer
- * table and the tile schedule).  Returns 0 on a bad argument; needs no GPU. */
+ * table, the tile schedule and, for M > 4, the quantized activations).
+ * Returns 0 on a bad argument; needs no GPU. */
 size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops, int64_t M);
 
 /* Checks every layer, plans the tile schedule for the current device and
@@ -198,9 +200,8 @@ size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops,
 bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops, int64_t M,
                                         void* ws, size_t ws_bytes, bitlinear_group** out);
 
-/* Runs every layer of the group on `stream` (one launch; capturable in a
- * HIP graph).  The workspace is only read by the launch; calls that overlap
- * write the same outputs and race on them. */
+/* Runs every layer of the group on `stream` (one launch, two for M > 4;
+ * capturable in a HIP graph).  Calls that overlap on one group race. */
 bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream);
 
 /* Frees the handle (not the workspace).  NULL is allowed. */

@@ -58,16 +58,26 @@ size_t q_workspace(int64_t M, int64_t K) {
 constexpr int kGroupMaxWG = 2048;
 
 struct GroupLayout {
-  size_t table, wg_begin, total;
+  size_t table, wg_begin, xq, sx, rs, total;
 };
 
-GroupLayout group_layout(int n_ops) {
+// The quantized activations, scales and row sums exist only for token
+// counts whose activations are quantized by a launch of their own.
+GroupLayout group_layout(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   GroupLayout L;
   size_t off = 0;
   L.table = off;
   off += align256((size_t)n_ops * sizeof(GroupOp));
   L.wg_begin = off;
   off += align256((size_t)(kGroupMaxWG + 1) * sizeof(int));
+  L.xq = L.sx = L.rs = off;
+  if (bl_group_prequantizes((int)M)) {
+    for (int i = 0; i < n_ops; ++i) off += align256((size_t)M * (size_t)ops[i].K);
+    L.sx = off;
+    off += align256((size_t)n_ops * (size_t)M * sizeof(float));
+    L.rs = off;
+    off += align256((size_t)n_ops * (size_t)M * sizeof(int));
+  }
   L.total = off;
   return L;
 }
@@ -112,6 +122,9 @@ struct bitlinear_group {
   int threads;
   GroupOp* ops;
   int* wg_begin;
+  int8_t* xq;
+  float* sx;
+  int* rs;
 };
 
 extern "C" {
@@ -270,7 +283,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
 
 size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   if (check_group(ops, n_ops, M) != BITLINEAR_OK) return 0;
-  return group_layout(n_ops).total;
+  return group_layout(ops, n_ops, M).total;
 }
 
 bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops, int64_t M,
@@ -279,7 +292,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   *out = nullptr;
   bitlinear_status st = check_group(ops, n_ops, M);
   if (st != BITLINEAR_OK) return st;
-  const GroupLayout L = group_layout(n_ops);
+  const GroupLayout L = group_layout(ops, n_ops, M);
   if (!ws || ws_bytes < L.total)
     return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 ws ? ws_bytes : (size_t)0);
@@ -290,7 +303,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   std::vector<GroupOp> table((size_t)n_ops);
-  int64_t item = 0, total_blocks = 0;
+  int64_t item = 0, total_blocks = 0, xq_off = 0;
   int max_k = 0;
   for (int i = 0; i < n_ops; ++i) {
     const bitlinear_group_op& o = ops[i];
@@ -305,6 +318,8 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     t.dtype = (int32_t)o.dtype;
     t.relu2 = o.epi == BITLINEAR_EPI_RELU2 ? 1 : 0;
     t.item_begin = (int32_t)item;
+    t.xq_off = xq_off;
+    xq_off += (int64_t)align256((size_t)M * (size_t)o.K);
     item += o.N / 16;
     total_blocks += (o.N / 16) * (o.K / 256);
     if (o.K > max_k) max_k = (int)o.K;
@@ -349,6 +364,9 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->threads = threads;
   g->ops = reinterpret_cast<GroupOp*>(base + L.table);
   g->wg_begin = reinterpret_cast<int*>(base + L.wg_begin);
+  g->xq = reinterpret_cast<int8_t*>(base + L.xq);
+  g->sx = reinterpret_cast<float*>(base + L.sx);
+  g->rs = reinterpret_cast<int*>(base + L.rs);
   *out = g;
   return ok();
 }
@@ -356,7 +374,8 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
 bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream) {
   if (!g) return fail(BITLINEAR_ERR_NULL, "group handle is required");
   return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k,
-                                  g->threads, static_cast<hipStream_t>(stream)),
+                                  g->threads, g->xq, g->sx, g->rs,
+                                  static_cast<hipStream_t>(stream)),
                   "bitlinear_group_forward");
 }
 

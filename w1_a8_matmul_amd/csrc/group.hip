@@ -19,6 +19,7 @@
 #include "common.hpp"
 #include "gemv_tile.hpp"
 #include "group.hpp"
+#include "quant_row.hpp"
 
 namespace {
 
@@ -59,11 +60,16 @@ struct Smem {
 // this wave.  Each tile is cut into chunks of kChunk column blocks.
 // Chunks past the end of a tile or of the wave's work use an empty or short
 // buffer range and read zeros.
-template <int NT, int KCH, int DT>
+// PREQ: the activations were quantized by the separate launch; the
+// segment copies its layer's int8 rows, scales and row sums into LDS instead.
+template <int NT, int KCH, int DT, bool PREQ>
 __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, int last,
                                             bool quantize, int8_t* xs, int xstride,
                                             float* s_sx, int* s_rs, float* s_y, Smem<NT>& sm,
-                                            int wave, int lane) {
+                                            const int8_t* __restrict__ xq,
+                                            const float* __restrict__ sx,
+                                            const int* __restrict__ rs, int op, int wave,
+                                            int lane) {
   constexpr int kThreads = NT;
   constexpr int kWaves = NT / kWave;
   constexpr int C = kChunk;
@@ -99,11 +105,26 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   };
 
   // Activation row 0 first, then the first weight chunk, then the
-  // quantization (which waits for the row but not for the weights).
+  // quantization (which waits for the row but not for the weights); or the
+  // first weight chunk, then the copy of the quantized rows.
   uint4 bufA[C], bufB[C];
   Cursor qi{mine, 0};  // next chunk to issue
   Cursor qc{mine, 0};  // next chunk to consume
-  if (quantize) {
+  if (PREQ) {
+    issue(bufA, 0, qi);
+    if (quantize) {
+      const int row16 = K / 16;  // 16-byte pieces per row
+      const uint4* src = reinterpret_cast<const uint4*>(xq + o.xq_off);
+      for (int i = threadIdx.x; i < M * row16; i += kThreads) {
+        const int m = i / row16, c = i - m * row16;
+        *reinterpret_cast<uint4*>(xs + m * xstride + c * 16) = src[i];
+      }
+      if ((int)threadIdx.x < M) {
+        s_sx[threadIdx.x] = sx[op * M + threadIdx.x];
+        s_rs[threadIdx.x] = rs[op * M + threadIdx.x];
+      }
+    }
+  } else if (quantize) {
     Chunk<DT> ch[KCH];
     load_row<DT, kThreads, KCH>(o.X, 0, K, ch);
     issue(bufA, 0, qi);
@@ -184,10 +205,13 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   }
 }
 
-template <int NT, int KCH>
-__global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops,
-                                                         int n_ops, int M, int max_k,
-                                                         const int* __restrict__ wg_begin) {
+template <int NT, int KCH, bool PREQ>
+__global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops, int n_ops,
+                                                   int M, int max_k,
+                                                   const int* __restrict__ wg_begin,
+                                                   const int8_t* __restrict__ xq,
+                                                   const float* __restrict__ sx,
+                                                   const int* __restrict__ rs) {
   // Dynamic LDS: int8 activations [M][max_k + 16] of the current layer (rows
   // padded by 16 bytes so that the 16 token rows of an A-operand read fall in
   // distinct banks), then the segment's outputs [M][kSegTiles][16] floats.
@@ -213,12 +237,15 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
     const int op_end = o.item_begin + o.N / kTileRows;
     const int seg_end = min(min(end, op_end), item + kSegTiles);
     const bool quantize = quantized_op != op;
-    if (o.dtype == 1)
-      run_segment<NT, KCH, 1>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm,
-                              wave, lane);
+    if (PREQ)
+      run_segment<NT, KCH, 0, true>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y,
+                                    sm, xq, sx, rs, op, wave, lane);
+    else if (o.dtype == 1)
+      run_segment<NT, KCH, 1, false>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y,
+                                     sm, xq, sx, rs, op, wave, lane);
     else
-      run_segment<NT, KCH, 0>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y, sm,
-                              wave, lane);
+      run_segment<NT, KCH, 0, false>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y,
+                                     sm, xq, sx, rs, op, wave, lane);
     __syncthreads();  // before the next segment overwrites xs, the scales or s_y
     quantized_op = op;
     item = seg_end;
@@ -226,40 +253,69 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
   }
 }
 
+// Per-token quantization of every layer's activations (one workgroup per
+// layer and token) into the workspace, for the larger token counts.
+__global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restrict__ ops, int M,
+                                                          int8_t* __restrict__ xq,
+                                                          float* __restrict__ sx,
+                                                          int* __restrict__ rs) {
+  __shared__ float red_f[4];
+  __shared__ int red_i[4];
+  const int op = blockIdx.x / M, m = blockIdx.x % M;
+  const GroupOp o = ops[op];
+  int8_t* dst = xq + o.xq_off + (int64_t)m * o.K;
+  RowQuant q;
+  int sum;
+  if (o.dtype == 1) {
+    q = row_absmax_scale<1, 256>(o.X, m, o.K, red_f);
+    sum = row_quantize_to<1, 256>(o.X, m, o.K, q.qs, dst, red_i);
+  } else {
+    q = row_absmax_scale<0, 256>(o.X, m, o.K, red_f);
+    sum = row_quantize_to<0, 256>(o.X, m, o.K, q.qs, dst, red_i);
+  }
+  if (threadIdx.x == 0) {
+    sx[op * M + m] = q.a_c / kQmax;
+    rs[op * M + m] = sum;
+  }
+}
+
 // Activation chunks per thread: each covers NT * 8 elements of a row.
-template <int NT>
+template <int NT, bool PREQ>
 const void* kernel_for(int max_k) {
-  if (max_k <= NT * 8 * 2) return reinterpret_cast<const void*>(&group_kernel<NT, 2>);
-  if (max_k <= NT * 8 * 4) return reinterpret_cast<const void*>(&group_kernel<NT, 4>);
-  return reinterpret_cast<const void*>(&group_kernel<NT, 6>);
+  if (max_k <= NT * 8 * 2) return reinterpret_cast<const void*>(&group_kernel<NT, 2, PREQ>);
+  if (max_k <= NT * 8 * 4) return reinterpret_cast<const void*>(&group_kernel<NT, 4, PREQ>);
+  return reinterpret_cast<const void*>(&group_kernel<NT, 6, PREQ>);
 }
 
-const void* kernel_for(int threads, int max_k) {
-  return threads == 512 ? kernel_for<512>(max_k) : kernel_for<256>(max_k);
+const void* kernel_for(int threads, bool preq, int max_k) {
+  if (threads == 512) return preq ? kernel_for<512, true>(max_k) : kernel_for<512, false>(max_k);
+  return preq ? kernel_for<256, true>(max_k) : kernel_for<256, false>(max_k);
 }
 
-template <int NT>
+template <int NT, bool PREQ>
 void launch(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G, int max_k,
-            size_t lds, hipStream_t s) {
+            size_t lds, const int8_t* xq, const float* sx, const int* rs, hipStream_t s) {
   if (max_k <= NT * 8 * 2)
-    hipLaunchKernelGGL((group_kernel<NT, 2>), dim3(G), dim3(NT), lds, s, ops, n_ops, M, max_k,
-                       wg_begin);
+    hipLaunchKernelGGL((group_kernel<NT, 2, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
+                       max_k, wg_begin, xq, sx, rs);
   else if (max_k <= NT * 8 * 4)
-    hipLaunchKernelGGL((group_kernel<NT, 4>), dim3(G), dim3(NT), lds, s, ops, n_ops, M, max_k,
-                       wg_begin);
+    hipLaunchKernelGGL((group_kernel<NT, 4, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
+                       max_k, wg_begin, xq, sx, rs);
   else
-    hipLaunchKernelGGL((group_kernel<NT, 6>), dim3(G), dim3(NT), lds, s, ops, n_ops, M, max_k,
-                       wg_begin);
+    hipLaunchKernelGGL((group_kernel<NT, 6, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
+                       max_k, wg_begin, xq, sx, rs);
 }
 
-int blocks_per_cu(int threads, size_t lds, int max_k) {
+int blocks_per_cu(int threads, bool preq, size_t lds, int max_k) {
   int blocks = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks, kernel_for(threads, max_k), threads, lds);
+      &blocks, kernel_for(threads, preq, max_k), threads, lds);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 }  // namespace
+
+bool bl_group_prequantizes(int M) { return M > kGroupInlineQuantMaxM; }
 
 size_t bl_group_lds_bytes(int M, int max_k) {
   return (size_t)M * (size_t)(max_k + 16) + (size_t)M * kSegTiles * kTileRows * sizeof(float);
@@ -267,33 +323,44 @@ size_t bl_group_lds_bytes(int M, int max_k) {
 
 hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
+  const bool preq = bl_group_prequantizes(M);
   for (int nt : {256, 512}) {
     if (lds > 64 * 1024) {
       const hipError_t e = hipFuncSetAttribute(
-          kernel_for(nt, max_k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+          kernel_for(nt, preq, max_k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
   }
   // Four-wave workgroups while at least two fit on a compute unit (more,
   // shorter weight streams); eight-wave ones when the activations take so
   // much LDS that only one does.
-  const int b256 = blocks_per_cu(256, lds, max_k);
+  const int b256 = blocks_per_cu(256, preq, lds, max_k);
   if (b256 >= 2) {
     *threads = 256;
     *per_cu = b256;
   } else {
     *threads = 512;
-    *per_cu = blocks_per_cu(512, lds, max_k);
+    *per_cu = blocks_per_cu(512, preq, lds, max_k);
   }
   return hipSuccess;
 }
 
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
-                           int max_k, int threads, hipStream_t s) {
+                           int max_k, int threads, int8_t* xq, float* sx, int* rs,
+                           hipStream_t s) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
+  const bool preq = bl_group_prequantizes(M);
+  if (preq) {
+    hipLaunchKernelGGL(group_quant_kernel, dim3((unsigned)(n_ops * M)), dim3(256), 0, s, ops, M,
+                       xq, sx, rs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (threads == 512)
-    launch<512>(ops, n_ops, M, wg_begin, G, max_k, lds, s);
+    preq ? launch<512, true>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s)
+         : launch<512, false>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s);
   else
-    launch<256>(ops, n_ops, M, wg_begin, G, max_k, lds, s);
+    preq ? launch<256, true>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s)
+         : launch<256, false>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s);
   return hipGetLastError();
 }

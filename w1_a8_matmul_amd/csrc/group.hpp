@@ -10,16 +10,24 @@ struct GroupOp {
   const uint8_t* packed;  // packed ternary weights, [N/16][K/256] tiles of 1 KiB
   const float* gamma;     // gamma_c (one float)
   float* Y;               // [M][N] output
+  int64_t xq_off;         // byte offset of this layer's int8 [M][K] in the workspace
   int32_t K, N;
   int32_t dtype, relu2;
   int32_t item_begin;     // index of this layer's first 16-row tile in the flat list
-  int32_t pad[3];
+  int32_t pad;
 };
 static_assert(sizeof(GroupOp) == 64, "GroupOp must stay 64 bytes");
 
-// Largest K of a grouped layer and largest token count.
+// Largest K of a grouped layer and largest token count.  Up to
+// kGroupInlineQuantMaxM tokens each workgroup quantizes the activations of
+// the layer it starts on itself (one launch); above, a separate launch
+// quantizes them once into the workspace.
 constexpr int kGroupMaxK = 12288;
 constexpr int kGroupMaxM = 16;
+constexpr int kGroupInlineQuantMaxM = 4;
+
+// Whether the group needs the quantization launch and workspace.
+bool bl_group_prequantizes(int M);
 
 // LDS available to one workgroup.
 constexpr size_t kGroupMaxLds = 160 * 1024;
@@ -32,7 +40,10 @@ size_t bl_group_lds_bytes(int M, int max_k);
 // LDS it needs.
 hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu);
 
-// Grouped forward: one launch.  wg_begin[g]..wg_begin[g+1] is workgroup g's
-// tile range; G workgroups of `threads` threads; max_k the largest K.
+// Grouped forward.  wg_begin[g]..wg_begin[g+1] is workgroup g's tile range;
+// G workgroups of `threads` threads; max_k the largest K.  xq, sx, rs: the
+// quantized activations, scales and row sums (used when
+// bl_group_prequantizes(M)).
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
-                           int max_k, int threads, hipStream_t s);
+                           int max_k, int threads, int8_t* xq, float* sx, int* rs,
+                           hipStream_t s);
