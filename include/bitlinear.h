@@ -148,7 +148,11 @@ bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, i
  * ternary weights and gamma_c (device float, as written by
  * bitlinear_quantize_weights).  Quantizes X per token, contracts in int32,
  * rescales, then applies `epi`.  `dbg` may be NULL.  `ws` holds at least
- * bitlinear_workspace_bytes(M, K, N) bytes (NULL allowed when that is 0). */
+ * bitlinear_workspace_bytes(M, K, N) bytes (NULL allowed when that is 0).
+ * Kernels by token count (both give the same bits): M <= 4 one fused launch
+ * (quantization and v_dot4 contraction); larger M a quantization launch and
+ * a tiled int8 MFMA GEMM.  For decode steps with several layers, the grouped
+ * forward below streams all of them in one launch for M <= 16. */
 bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t M,
                                    int64_t K, int64_t N, const uint8_t* packed,
                                    const float* gamma, float* Y, bitlinear_epilogue epi,

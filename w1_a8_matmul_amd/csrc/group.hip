@@ -205,35 +205,29 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   }
 }
 
-template <int NT, int KCH, bool PREQ>
-__global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops, int n_ops,
-                                                   int M, int max_k,
-                                                   const int* __restrict__ wg_begin,
-                                                   const int8_t* __restrict__ xq,
-                                                   const float* __restrict__ sx,
-                                                   const int* __restrict__ rs) {
+// Tiles item .. end-1 of the layers op_at(0..n_ops-1), in segments of at
+// most kSegTiles tiles of one layer; the activations are quantized (or
+// copied) when a segment starts a new layer.
+template <int NT, int KCH, bool PREQ, typename OpAt>
+__device__ __forceinline__ void run_range(OpAt op_at, int n_ops, int M, int max_k, int item,
+                                          int end, const int8_t* __restrict__ xq,
+                                          const float* __restrict__ sx,
+                                          const int* __restrict__ rs, int8_t* dyn, float* s_sx,
+                                          int* s_rs, Smem<NT>& sm) {
   // Dynamic LDS: int8 activations [M][max_k + 16] of the current layer (rows
   // padded by 16 bytes so that the 16 token rows of an A-operand read fall in
   // distinct banks), then the segment's outputs [M][kSegTiles][16] floats.
-  extern __shared__ __align__(16) int8_t dyn[];
   const int xstride = max_k + 16;
   int8_t* xs = dyn;
   float* s_y = reinterpret_cast<float*>(dyn + (size_t)M * xstride);
-  __shared__ float s_sx[kGroupMaxM];
-  __shared__ int s_rs[kGroupMaxM];
-  __shared__ Smem<NT> sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int item = wg_begin[blockIdx.x];
-  const int end = wg_begin[blockIdx.x + 1];
   int op = 0;
-  while (op + 1 < n_ops && ops[op + 1].item_begin <= item) ++op;
+  while (op + 1 < n_ops && op_at(op + 1).item_begin <= item) ++op;
 
-  // Segments: runs of at most kSegTiles tiles of one layer.  The activations
-  // are quantized when a segment starts a new layer.
   int quantized_op = -1;
   while (item < end) {
-    const GroupOp o = ops[op];
+    const GroupOp o = op_at(op);
     const int op_end = o.item_begin + o.N / kTileRows;
     const int seg_end = min(min(end, op_end), item + kSegTiles);
     const bool quantize = quantized_op != op;
@@ -251,6 +245,23 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
     item = seg_end;
     if (item == op_end) ++op;
   }
+}
+
+// Many layers: the table in device memory, tile ranges planned on the host.
+template <int NT, int KCH, bool PREQ>
+__global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops, int n_ops,
+                                                   int M, int max_k,
+                                                   const int* __restrict__ wg_begin,
+                                                   const int8_t* __restrict__ xq,
+                                                   const float* __restrict__ sx,
+                                                   const int* __restrict__ rs) {
+  extern __shared__ __align__(16) int8_t dyn[];
+  __shared__ float s_sx[kGroupMaxM];
+  __shared__ int s_rs[kGroupMaxM];
+  __shared__ Smem<NT> sm;
+  run_range<NT, KCH, PREQ>([=](int i) { return ops[i]; }, n_ops, M, max_k,
+                           wg_begin[blockIdx.x], wg_begin[blockIdx.x + 1], xq, sx, rs, dyn, s_sx,
+                           s_rs, sm);
 }
 
 // Per-token quantization of every layer's activations (one workgroup per
