@@ -39,6 +39,11 @@ METRIC = ("ternary GEMV HBM GB/s (% of peak), µs/token for all linears; "
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
 MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
+# Sources of each measured kernel: a committed counter summary applies only
+# to the kernel version it was taken on (matched by their hash).
+GEMV_SOURCES = ["gemv.hip", "gemv_tile.hpp", "common.hpp"]
+GEMM_SOURCES = ["gemm.hip", "common.hpp"]
+GROUP_SOURCES = ["group.hip", "group.hpp", "gemv_tile.hpp", "quant_row.hpp", "common.hpp"]
 
 
 def log(*a):
@@ -197,13 +202,13 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
         key = f"gemm_q_{dom.K}x{dom.N}_m{M}"
-        src = source_hash(["gemm.hip", "common.hpp"])
+        src = source_hash(GEMM_SOURCES)
     else:
         achieved = dom.bytes() / (us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
         key = f"gemv_{dom.K}x{dom.N}_m{M}"
-        src = source_hash(["gemv.hip", "quant_row.hpp", "common.hpp"])
+        src = source_hash(GEMV_SOURCES)
     roof["traffic"] = traffic_from_profile(src, key)
     roof["kernel"] = key
     roof["kernel_us"] = round(us, 3)
@@ -221,7 +226,7 @@ def roofline_grouped(args, torch, step, bytes_step, wk, M, n_lin):
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profile(
-                source_hash(["group.hip", "group.hpp", "quant_row.hpp", "common.hpp"]), key),
+                source_hash(GROUP_SOURCES), key),
             "kernel": key, "kernel_us": round(us, 3),
             "launches_per_forward": 1 if M <= 4 else 2}
     log(f"grouped forward: {us:.3f} us per step ({n_lin} linears)")
