@@ -1,20 +1,27 @@
-// BitLinear forward from int8 activations on the CDNA4 int8 matrix cores
-// (v_mfma_i32_16x16x64_i8).  For larger M the ternary x int8 product is a
-// dense contraction (prefill), so the 2-bit codes are unpacked into MFMA B
-// operands and multiplied against int8 activation tiles.
+// BitLinear forward from int8 activations on the CDNA4 int8 matrix cores,
+// 32x32x32 form (v_mfma_i32_32x32x32_i8).  For larger M the ternary x int8
+// product is a dense contraction (prefill): the 2-bit codes are unpacked in
+// registers into MFMA B operands and multiplied against int8 activation
+// tiles.  On gfx950 the 32x32x32 int8 instruction sustains about 1.7x the
+// rate of the 16x16x64 one (measured: ~3.5 vs ~2.0 POP/s with random
+// operands at 8 waves per CU), so the tiles are built around it.
 //
-// A workgroup of WM x WN waves computes a (16*TM*WM) x (16*TN*WN) output
+// A workgroup of WM x WN waves computes a (32*TM*WM) x (32*TN*WN) output
 // tile, walking K in steps of 128 columns (half of a packed 256-column
-// block).  Each step's int8 activation rows (A) and packed weight chunks (B,
-// still 2 bits per weight) are copied into LDS by direct-to-LDS buffer
-// loads (buffer_load_dwordx4 ... lds: no register staging) into a ring of
-// S stages, up to S steps ahead of the multiply; each wave reads a step's
-// fragments into registers one step before its MFMAs use them.  Each wave reads its A
-// fragments (16 bytes per lane from XOR-swizzled rows, so eight lanes hit
-// eight distinct bank groups) and 8 bytes of packed codes per B fragment
-// pair, unpacks the codes in registers and issues TM*TN*2 MFMAs per step.
-// Codes
-// are q+1 in {0,1,2}; the activation row sums turn sum(code*x) into
+// block).  Each step's int8 activation rows (A) and packed weight half-tiles
+// (B, still 2 bits per weight) are copied into LDS by direct-to-LDS buffer
+// loads (no register staging) into a ring of S stages, up to S steps ahead of
+// the multiply; each wave reads the fragments of the next half step (64
+// columns) into registers while the MFMAs of the current one run.
+//
+// Operands of one MFMA (32 rows or columns, 32 k): lane l supplies row (or
+// column) l % 32 and 16 k values, the lanes 0-31 one set and 32-63 another;
+// any k order works as long as A and B use the same one.  For the 64-column
+// group p of a step, lane half h takes packed words 2h and 2h+1 of its row's
+// 16-byte chunk (one 8-byte LDS read) -- word w holds the codes of columns
+// 16w .. 16w+15 of the group -- and MFMA u (0, 1) of the group uses word
+// 2h+u with the matching 16 activation columns 64p + 32h + 16u .. +15.
+// Codes are q+1 in {0,1,2}; the activation row sums turn sum(code*x) into
 // sum(q*x) exactly in the epilogue.
 //
 // The load/unpack/multiply order follows the kernel outline of the "BitNet
@@ -27,6 +34,7 @@ namespace {
 using namespace bl;
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 // Raw buffer descriptor (gfx9 layout: 48-bit base, stride 0, byte range,
 // raw-buffer format word) for the copies below.
@@ -57,19 +65,17 @@ struct Tile {
   static constexpr int kStages = S;  // LDS ring depth (S-1 steps in flight)
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int BM = 16 * TM * WM;
-  static constexpr int BN = 16 * TN * WN;
+  static constexpr int BM = 32 * TM * WM;
+  static constexpr int BN = 32 * TN * WN;
   static constexpr int kBTiles = BN / kTileRows;                // weight tiles per workgroup
   static constexpr int kABytes = BM * kStepCols;                // A bytes per step
-  static constexpr int kAInstr = kABytes / 1024;                // 1 KiB per wave DMA
-  static constexpr int kBInstrUsed = kBTiles / 2;               // 2 tiles' halves each
-  // Every wave issues the same number of copies per step (the waits count
-  // them): B is padded with copies that read zeros into a spare area.
+  static constexpr int kAInstr = kABytes / 1024;                // 1 KiB per wave copy
+  static constexpr int kBInstr = kBTiles / 2;                   // 2 half-tiles per copy
   static constexpr int kAPerWave = kAInstr / kWaves;
-  static constexpr int kBPerWave = (kBInstrUsed + kWaves - 1) / kWaves;
-  static constexpr int kBBytes = kBPerWave * kWaves * 1024;     // B bytes per step (padded)
+  static constexpr int kBPerWave = kBInstr / kWaves;
+  static constexpr int kBBytes = kBInstr * 1024;                // B bytes per step
   static constexpr int kStageBytes = kABytes + kBBytes;
-  static_assert(kAInstr % kWaves == 0 && kBTiles % 2 == 0, "stage sizes");
+  static_assert(kAInstr % kWaves == 0 && kBInstr % kWaves == 0, "copies split evenly");
   static_assert(S >= 2 && S * kStageBytes <= 160 * 1024, "LDS ring must fit 160 KiB");
   static_assert((S - 1) * (kAPerWave + kBPerWave) < 64, "vmcnt range");
 };
@@ -96,7 +102,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
+__global__ __launch_bounds__(64 * WM * WN, 3) void gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
@@ -130,14 +136,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
   const v4i b_rsrc = rsrc_words(packed + (int64_t)nt0 * kblocks * kTileBytes,
                                 (uint32_t)tiles_here * (uint32_t)kblocks * kTileBytes);
 
-  // DMA of step kh into ring slot `slot`.  A: wave instruction q writes rows
-  // 8q..8q+7 (128 bytes each); lane j fills row 8q + j/8, 16-byte slot j%8,
-  // loading activation column (j%8) ^ (row & 7) -- the XOR swizzle.
-  // B: instruction q writes weight tiles 2q, 2q+1 (their half for this step,
-  // 512 bytes each).
-  // Steps past the end are issued too, with offsets moved out of the buffer
-  // range (so they read zeros without touching memory): a branch around the
-  // copies would make the compiler wait for all of them before LDS reads.
+  // Copies of step kh into ring slot `slot`.  A: wave instruction q writes
+  // rows 8q..8q+7 (128 bytes each); lane j fills row 8q + j/8, 16-byte slot
+  // j%8, loading activation column group (j%8) ^ ((row / 2) & 7) -- the XOR
+  // swizzle: the 16 rows that one A-fragment read touches at a time then
+  // fall in 16 distinct 16-byte bank groups (a row is 128 bytes, so rows r
+  // and r+8 would otherwise share banks).  B: instruction q writes weight tiles 2q, 2q+1 (their half for
+  // this step, 512 bytes each).  Steps past the end are issued too, with
+  // offsets moved out of the buffer range (so they read zeros without
+  // touching memory): a branch around the copies would make the compiler
+  // wait for all of them before LDS reads.
   auto dma = [&](int kh, int slot) {
     int8_t* base = stage_ptr(slot);
     const uint32_t past = kh < nsteps ? 0u : 0x80000000u;
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
     for (int p = 0; p < T::kAPerWave; ++p) {
       const int q = wave + p * T::kWaves;
       const int r = 8 * q + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
       const uint32_t voff =
           ((uint32_t)r * (uint32_t)K + (uint32_t)(kh * kStepCols + c * 16)) | past;
       copy16(a_rsrc, voff, base + q * 1024);
@@ -154,119 +162,118 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_q_kernel(
     for (int p = 0; p < T::kBPerWave; ++p) {
       const int q = wave + p * T::kWaves;
       const int t = 2 * q + (lane >> 5);
-      const uint32_t pad = q < T::kBInstrUsed ? 0u : 0x80000000u;
       const uint32_t voff = (uint32_t)((t * kblocks + (kh >> 1)) * kTileBytes +
                                        (kh & 1) * (kTileBytes / 2) + (lane & 31) * 16) |
-                            past | pad;
+                            past;
       copy16(b_rsrc, voff, base + T::kABytes + q * 1024);
     }
   };
   // Copies this wave issues per step.
   constexpr int kMyDma = T::kAPerWave + T::kBPerWave;
 
-  v4i acc[TM][TN];
+  v16i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  // Fragments of one step, read from LDS into registers one step ahead of
-  // their MFMAs.  Lane group grp takes sub-block (grp & 1) of the step's
-  // half block and, in MFMA t, word 2*(grp >> 1) + t of that 64-column
-  // chunk: columns 64*(grp & 1) + 16*(2*(grp >> 1) + t) .. +15 of the step.
-  // The B words a lane needs for t = 0, 1 are adjacent (one 8-byte read).
+  // Fragments of one half step (64-column group p of a step): for MFMA u,
+  // A rows of 16 activation columns 64p + 32h + 16u .. +15, and per weight
+  // column tile the two packed words of group p (one 8-byte read).
   struct Frag {
     v4i a[2][TM];
     uint2 b[TN];
   };
-  const int r16 = lane & 15, grp = lane >> 4;
-  auto read_frags = [&](int slot, Frag& f) {
+  const int r32 = lane & 31, h = lane >> 5;
+  auto read_frags = [&](int slot, int p, Frag& f) {
     const int8_t* sa = stage_ptr(slot);
     const int8_t* sb = sa + T::kABytes;
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      f.b[j] = *reinterpret_cast<const uint2*>(
-          sb + (wn * TN + j) * (kTileBytes / 2) + ((grp & 1) * 16 + r16) * 16 + (grp >> 1) * 8);
+    for (int j = 0; j < TN; ++j) {
+      const int n = (wn * TN + j) * 32 + r32;  // column within the workgroup tile
+      f.b[j] = *reinterpret_cast<const uint2*>(sb + (n >> 4) * (kTileBytes / 2) +
+                                               (16 * p + (n & 15)) * 16 + h * 8);
+    }
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int r = wm * 16 * TM + i * 16 + r16;
-        const int c = (4 * (grp & 1) + 2 * (grp >> 1) + t) ^ (r & 7);
-        f.a[t][i] = *reinterpret_cast<const v4i*>(sa + r * kStepCols + c * 16);
+        const int r = (wm * TM + i) * 32 + r32;
+        const int c = (4 * p + 2 * h + u) ^ ((r >> 1) & 7);
+        f.a[u][i] = *reinterpret_cast<const v4i*>(sa + r * kStepCols + c * 16);
       }
   };
   auto compute = [&](const Frag& f) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint32_t w = t == 0 ? f.b[j].x : f.b[j].y;
-        const v4i b = v4i{(int)codes(w, 0), (int)codes(w, 1), (int)codes(w, 2), (int)codes(w, 3)};
+        const uint32_t w = u == 0 ? f.b[j].x : f.b[j].y;
+        const v4i b =
+            v4i{(int)codes(w, 0), (int)codes(w, 1), (int)codes(w, 2), (int)codes(w, 3)};
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.a[t][i], b, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[u][i], b, acc[i][j], 0, 0, 0);
       }
   };
 
-  // Prologue: copies of steps 0..S-1 into every slot; fragments of step 0.
+  // Prologue: copies of steps 0..S-1 into every slot; first half of step 0.
 #pragma unroll
   for (int st = 0; st < kStages; ++st) dma(st, st);
   wait_copies_and_reads<(kStages - 1) * kMyDma>();
   lds_barrier();
   Frag f0, f1;
-  read_frags(0, f0);
+  read_frags(0, 0, f0);
 
-  // Step kh: its fragments are in registers (cur).  Wait until this wave's
-  // copies of step kh+1 have landed (at most those of the S-2 later steps
+  // Step kh (its first half in registers, cur): read its second half (nxt)
+  // and run the first half's MFMAs.  Then wait until this wave's copies of
+  // step kh+1 have landed (at most those of the S-2 later steps
   // outstanding) and its reads of step kh have returned; after the barrier
   // every wave's copies of kh+1 are visible and nobody reads step kh's slot
-  // any more, so it takes the copies of step kh+S.  Then read step kh+1's
-  // fragments (nxt) and run step kh's MFMAs while those reads are in
-  // flight.  (Not __syncthreads(): its workgroup fence would wait for every
-  // outstanding copy, emptying the pipeline.)
-  auto step = [&](int kh, int slot, Frag& cur, Frag& nxt) {
+  // any more, so it takes the copies of step kh+S.  Read the first half of
+  // step kh+1 (into cur) and run the second half's MFMAs while those reads
+  // are in flight.  (Not __syncthreads(): its workgroup fence would wait for
+  // every outstanding copy, emptying the pipeline.)
+  auto step = [&](int kh, int slot) {
+    read_frags(slot, 1, f1);
+    compute(f0);
     wait_copies_and_reads<(kStages - 2) * kMyDma>();
     lds_barrier();
     dma(kh + kStages, slot);
-    read_frags((slot + 1) % kStages, nxt);
-    compute(cur);
+    read_frags((slot + 1) % kStages, 0, f0);
+    compute(f1);
   };
-  // Unrolled so that slot and fragment-buffer indices are constants, and
-  // padded to whole rounds instead of a remainder loop (a second loop makes
-  // the compiler shuffle the accumulators every iteration).  Padding steps
-  // read zero activations (their copies are out of range) and add nothing.
-  constexpr int kUnroll = (kStages % 2 == 0) ? kStages : 2 * kStages;
-  const int nrounds = (nsteps + kUnroll - 1) / kUnroll;
+  // Unrolled so that slot indices are constants, and padded to whole rounds
+  // instead of a remainder loop (a second loop makes the compiler shuffle
+  // the accumulators every iteration).  Padding steps read zero activations
+  // (their copies are out of range) and add nothing.
+  const int nrounds = (nsteps + kStages - 1) / kStages;
   for (int rd = 0; rd < nrounds; ++rd) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (u % 2 == 0)
-        step(rd * kUnroll + u, u % kStages, f0, f1);
-      else
-        step(rd * kUnroll + u, u % kStages, f1, f0);
-    }
+    for (int u = 0; u < kStages; ++u) step(rd * kStages + u, u);
   }
   // No copy may still be writing LDS when the workgroup exits.
   wait_copies_and_reads<0>();
 
-  // D layout of a 16x16 int32 MFMA tile: lane holds column (lane % 16) and
-  // rows 4*(lane / 16) + r, r = 0..3.
+  // D layout of a 32x32 int32 MFMA tile: lane holds column (lane % 32) and,
+  // in register e, row 8*(e / 4) + 4*(lane / 32) + e % 4.  One store
+  // instruction (fixed e) writes two 128-byte row segments.
   const float gamma = *gamma_p;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 16 * TM + i * 16 + grp * 4 + r;
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
       if (m >= M) continue;
       const float sx = x_scale[m];
       const int rs = x_rowsum[m];
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int nt = nt0 + wn * TN + j;
-        if (nt >= ntiles) continue;
-        const int64_t n = (int64_t)nt * kTileRows + r16;
-        const int v = acc[i][j][r] - rs;
+        const int64_t n = (int64_t)(nt0 * kTileRows) + (wn * TN + j) * 32 + r32;
+        if (n >= N) continue;
+        const int v = acc[i][j][e] - rs;
         Y[(int64_t)m * N + n] = rescale(v, sx, gamma, relu2 != 0);
         if constexpr (DEBUG) acc_out[(int64_t)m * N + n] = v;
       }
@@ -283,27 +290,27 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
   const int total = tiles_m * tiles_n;
   if (acc_out)
-    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, S, true>), dim3(total), dim3(T::kThreads), 0,
-                       s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y, relu2 ? 1 : 0,
-                       acc_out, tiles_n, total);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, true>), dim3(total), dim3(T::kThreads),
+                       0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y,
+                       relu2 ? 1 : 0, acc_out, tiles_n, total);
   else
-    hipLaunchKernelGGL((gemm_q_kernel<WM, WN, TM, TN, S, false>), dim3(total), dim3(T::kThreads), 0,
-                       s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y, relu2 ? 1 : 0,
-                       acc_out, tiles_n, total);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, false>), dim3(total),
+                       dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed,
+                       gamma, Y, relu2 ? 1 : 0, acc_out, tiles_n, total);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Tile choice: measured on MI355X over the prefill shapes (M = 512, 2048;
-// K = 2560..11008; N = 2560..22016), 64x128 tiles (4 waves of 32x64, up to
-// four workgroups per compute unit) beat 128x128, 128x160 and 128x256 on
-// every shape: this kernel is bound by latency hiding (waves per SIMD), not
-// by LDS bandwidth.
+// Tile choice, measured on MI355X over the prefill shapes (M = 512, 2048;
+// K = 2560..6912; N = 2560..22016): 128x128 workgroup tiles (4 waves of
+// 64x64) with a two-stage ring and three waves per SIMD beat 128x256 tiles
+// (fewer workgroups than slots at N = 2560) and three-stage rings (LDS-
+// limited occupancy).
 hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                             const float* gamma, float* Y, bool relu2, int32_t* acc_out,
                             hipStream_t s) {
-  return launch_cfg<2, 2, 2, 4, 3>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
+  return launch_cfg<2, 2, 2, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
                                    acc_out, s);
 }
