@@ -54,7 +54,7 @@
  *     safe) results.
  *   - Shapes: N % 16 == 0 and K % 256 == 0 (the packed tile); M >= 0 and
  *     M == 0 is a no-op that returns BITLINEAR_OK; N, K >= 1 otherwise.
- *     |acc| <= 127*K must fit int32: K <= 16,908,288 (checked).
+ *     K <= 8,388,608 (checked; |acc| <= 127*K then fits int32 with room).
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H

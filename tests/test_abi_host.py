@@ -61,7 +61,8 @@ def test_quantize_weights_validation(L):
     assert qw(A, 15, 256, A, A, A, 1 << 20, None) == ERR_SHAPE
     assert qw(A, 16, 100, A, A, A, 1 << 20, None) == ERR_SHAPE
     assert qw(A, 0, 256, A, A, A, 1 << 20, None) == ERR_SHAPE
-    assert qw(A, 16, 256 * 70000, A, A, A, 1 << 30, None) == ERR_SHAPE  # 127*K overflows int32
+    assert qw(A, 16, 256 * 70000, A, A, A, 1 << 30, None) == ERR_SHAPE
+    assert qw(A, 16, (1 << 23) + 256, A, A, A, 1 << 30, None) == ERR_SHAPE  # K <= 2^23
     assert qw(U, 16, 256, A, A, A, 1 << 20, None) == ERR_ALIGN
     assert qw(A, 16, 256, U, A, A, 1 << 20, None) == ERR_ALIGN
     assert qw(A, 16, 256, A, A, None, 0, None) == ERR_WS

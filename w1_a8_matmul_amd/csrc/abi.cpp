@@ -37,7 +37,10 @@ bitlinear_status from_hip(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int64_t kMaxK = 16908288;  // 127 * K must fit int32
+// |acc| <= 127 * K must fit int32, and the prefill kernel's buffer ranges
+// (128 rows of K bytes, with bit 31 of an offset meaning "past the end")
+// must stay below 2^31: K <= 2^23.
+constexpr int64_t kMaxK = 8388608;
 
 bitlinear_status check_nk(int64_t N, int64_t K) {
   if (N < 1 || K < 1) return fail(BITLINEAR_ERR_SHAPE, "N=%lld K=%lld must be >= 1", (long long)N, (long long)K);
