@@ -137,7 +137,8 @@ def test_group_validation(L):
     arr = (bl.GroupOp * 2)(_gop(), _gop(K=6912, N=2560))
     need = L.bitlinear_group_workspace_bytes(arr, 2, 1)
     assert need >= 2 * 64 + 4 * 2049  # layer table and tile schedule
-    assert L.bitlinear_group_workspace_bytes(arr, 2, 17) == 0     # M > 16
+    assert L.bitlinear_group_workspace_bytes(arr, 2, 17) > 0      # M > 16: grouped GEMM
+    assert L.bitlinear_group_workspace_bytes(arr, 2, 65537) == 0
     assert L.bitlinear_group_workspace_bytes(arr, 2, 16) > 0      # 16 x 6912 fits in LDS
     big = (bl.GroupOp * 1)(_gop(K=12288, N=16))
     assert L.bitlinear_group_workspace_bytes(big, 1, 11) > 0

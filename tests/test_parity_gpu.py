@@ -342,6 +342,22 @@ def test_group_2b_layer(dev, bl, orc, M):
         assert np.array_equal(y.cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("M", [17, 64, 130])
+def test_group_gemm_matches_oracle(dev, bl, orc, M):
+    # above 16 tokens a group runs as one persistent tiled GEMM over all layers
+    shapes = [(256, 16, "normal_f32", None), (2560, 272, "normal_bf16", "relu2"),
+              (6912, 2560, "normal_bf16", None), (4096, 512, "student_t3_bf16", None),
+              (12544, 48, "normal_bf16", None)]
+    layers, refs = _group_layers(dev, bl, orc, M, shapes, 7300 + M)
+    g = bl.Group(layers)
+    outs = [y.clone() for y in g.forward()]
+    torch.cuda.synchronize()
+    for (Xt, packed, gamma, N, epi, _), y, y_ref in zip(layers, outs, refs):
+        assert np.array_equal(y.cpu().numpy(), y_ref)
+    for y, y2 in zip(outs, g.forward()):
+        assert torch.equal(y, y2)
+
+
 def test_group_2b_layer_graph_replay(dev, bl, orc):
     shapes = [(l.K, l.N, "normal_bf16", None) for l in wl.LAYER_2B]
     layers, refs = _group_layers(dev, bl, orc, 1, shapes, 7900)

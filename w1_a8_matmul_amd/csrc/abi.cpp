@@ -88,8 +88,9 @@ GroupLayout group_layout(const bitlinear_group_op* ops, int n_ops, int64_t M) {
 bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   if (!ops) return fail(BITLINEAR_ERR_NULL, "ops is required");
   if (n_ops < 1 || n_ops > 65536) return fail(BITLINEAR_ERR_ARG, "n_ops=%d out of range", n_ops);
-  if (M < 1 || M > kGroupMaxM)
-    return fail(BITLINEAR_ERR_SHAPE, "grouped forward needs 1 <= M <= %d, got %lld", kGroupMaxM, (long long)M);
+  if (M < 1 || M > 65536)
+    return fail(BITLINEAR_ERR_SHAPE, "grouped forward needs 1 <= M <= 65536, got %lld", (long long)M);
+  const bool skinny = M <= kGroupMaxM;
   int64_t items = 0;
   for (int i = 0; i < n_ops; ++i) {
     const bitlinear_group_op& o = ops[i];
@@ -99,13 +100,16 @@ bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M
       return fail(BITLINEAR_ERR_ARG, "op %d: unknown epilogue %d", i, (int)o.epi);
     bitlinear_status st = check_nk(o.N, o.K);
     if (st != BITLINEAR_OK) return st;
-    if (o.K > kGroupMaxK) return fail(BITLINEAR_ERR_SHAPE, "op %d: K=%lld exceeds %d", i, (long long)o.K, kGroupMaxK);
+    if (skinny && o.K > kGroupMaxK)
+      return fail(BITLINEAR_ERR_SHAPE, "op %d: K=%lld exceeds %d (M <= %d)", i, (long long)o.K,
+                  kGroupMaxK, kGroupMaxM);
     if (!o.X || !o.packed || !o.gamma || !o.Y) return fail(BITLINEAR_ERR_NULL, "op %d: X, packed, gamma and Y are required", i);
     if (!aligned16(o.X) || !aligned16(o.packed) || !aligned16(o.gamma) || !aligned16(o.Y))
       return fail(BITLINEAR_ERR_ALIGN, "op %d: tensor pointers must be 16-byte aligned", i);
-    items += o.N / 16;
+    items += skinny ? o.N / 16 : bl_group_gemm_tiles((int)M, (int)o.N);
   }
   if (items > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "too many output tiles");
+  if (!skinny) return BITLINEAR_OK;
   int64_t max_k = 0;
   for (int i = 0; i < n_ops; ++i) max_k = ops[i].K > max_k ? ops[i].K : max_k;
   if (bl_group_lds_bytes((int)M, (int)max_k) > kGroupMaxLds)
@@ -123,6 +127,7 @@ struct bitlinear_group {
   int G;
   int max_k;
   int threads;
+  bool gemm;
   GroupOp* ops;
   int* wg_begin;
   int8_t* xq;
@@ -295,6 +300,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   *out = nullptr;
   bitlinear_status st = check_group(ops, n_ops, M);
   if (st != BITLINEAR_OK) return st;
+  const bool skinny = M <= kGroupMaxM;
   const GroupLayout L = group_layout(ops, n_ops, M);
   if (!ws || ws_bytes < L.total)
     return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
@@ -323,29 +329,37 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     t.item_begin = (int32_t)item;
     t.xq_off = xq_off;
     xq_off += (int64_t)align256((size_t)M * (size_t)o.K);
-    item += o.N / 16;
-    total_blocks += (o.N / 16) * (o.K / 256);
+    // Work items: 16-row weight tiles (skinny) or output tiles of the GEMM;
+    // either way an item's cost is proportional to K.
+    const int64_t items = skinny ? o.N / 16 : bl_group_gemm_tiles((int)M, (int)o.N);
+    item += items;
+    total_blocks += items * (o.K / 256);
     if (o.K > max_k) max_k = (int)o.K;
   }
-  // As many workgroups as fit on the chip at once (each holds one layer's
-  // int8 activations in LDS), at most four per compute unit: the weights are
-  // split into that many contiguous streams.
+  // As many workgroups as fit on the chip at once, at most four per compute
+  // unit (skinny: each holds one layer's int8 activations in LDS; the
+  // weights are split into that many contiguous streams).
   int threads = 256, per_cu = 1;
-  e = bl_group_plan((int)M, max_k, &threads, &per_cu);
-  if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
+  if (skinny) {
+    e = bl_group_plan((int)M, max_k, &threads, &per_cu);
+    if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
+  } else {
+    per_cu = bl_group_gemm_blocks_per_cu();
+  }
   if (per_cu > 4) per_cu = 4;
   int G = per_cu * (cus > 0 ? cus : 1);
   if (G > kGroupMaxWG) G = kGroupMaxWG;
 
-  // Byte-balanced contiguous tile ranges: workgroup g starts at the first
-  // tile whose preceding weight reaches g/G of the total.
+  // Cost-balanced contiguous item ranges: workgroup g starts at the first
+  // item whose preceding cost reaches g/G of the total.
   std::vector<int> wg_begin((size_t)G + 1);
   {
     int g = 0;
     int64_t before = 0, it = 0;
     for (int i = 0; i < n_ops && g <= G; ++i) {
-      const int64_t tiles = ops[i].N / 16, kblocks = ops[i].K / 256;
-      for (int64_t t = 0; t < tiles; ++t, ++it) {
+      const int64_t items = skinny ? ops[i].N / 16 : bl_group_gemm_tiles((int)M, (int)ops[i].N);
+      const int64_t kblocks = ops[i].K / 256;
+      for (int64_t t = 0; t < items; ++t, ++it) {
         while (g <= G && before * G >= (int64_t)g * total_blocks) wg_begin[(size_t)g++] = (int)it;
         before += kblocks;
       }
@@ -365,6 +379,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->G = G;
   g->max_k = max_k;
   g->threads = threads;
+  g->gemm = !skinny;
   g->ops = reinterpret_cast<GroupOp*>(base + L.table);
   g->wg_begin = reinterpret_cast<int*>(base + L.wg_begin);
   g->xq = reinterpret_cast<int8_t*>(base + L.xq);
@@ -376,6 +391,13 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
 
 bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream) {
   if (!g) return fail(BITLINEAR_ERR_NULL, "group handle is required");
+  if (g->gemm) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = bl_launch_group_quant(g->ops, g->n_ops, g->M, g->xq, g->sx, g->rs, s);
+    if (e == hipSuccess)
+      e = bl_launch_group_gemm(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->xq, g->sx, g->rs, s);
+    return from_hip(e, "bitlinear_group_forward");
+  }
   return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k,
                                   g->threads, g->xq, g->sx, g->rs,
                                   static_cast<hipStream_t>(stream)),

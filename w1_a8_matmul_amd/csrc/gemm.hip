@@ -28,6 +28,7 @@
 // b1.58 2B4T Technical Report" card, section "Method Adaptation"; the tiling
 // is this library's own, for gfx950.
 #include "common.hpp"
+#include "group.hpp"
 
 namespace {
 
@@ -101,28 +102,22 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// One output tile (tm, tn) of one layer: the whole K loop and the
+// epilogue.  `ring` is the workgroup's LDS ring (S stages of kStageBytes).
 template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
-__global__ __launch_bounds__(64 * WM * WN, 3) void gemm_kernel(
-    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+__device__ __forceinline__ void gemm_tile(
+    int8_t* ring, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
-    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tiles_n,
-    int tiles_total) {
+    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tm, int tn) {
   using T = Tile<WM, WN, TM, TN, S>;
   constexpr int kStages = S;
-  __shared__ __align__(1024) int8_t ring[kStages][T::kStageBytes];
-  auto stage_ptr = [&](int slot) -> int8_t* { return &ring[slot][0]; };
+  auto stage_ptr = [&](int slot) -> int8_t* { return ring + slot * T::kStageBytes; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-
-  // Consecutive workgroup ids go to different XCDs; give each XCD a
-  // contiguous run of tiles (row-major), so tiles that share activation rows
-  // share that XCD's L2.
-  int tile = blockIdx.x;
-  if (tiles_total % 8 == 0) tile = (blockIdx.x % 8) * (tiles_total / 8) + blockIdx.x / 8;
-  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  (void)tid;
   const int m0 = tm * T::BM;
   const int nt0 = tn * T::kBTiles;  // first 16-row weight tile
   const int ntiles = N / kTileRows;
@@ -281,6 +276,53 @@ __global__ __launch_bounds__(64 * WM * WN, 3) void gemm_kernel(
   }
 }
 
+// One layer: a workgroup per output tile.
+template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
+__global__ __launch_bounds__(64 * WM * WN, 3) void gemm_kernel(
+    const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ x_rowsum, int M, int K, int N,
+    const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
+    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tiles_n,
+    int tiles_total) {
+  using T = Tile<WM, WN, TM, TN, S>;
+  __shared__ __align__(1024) int8_t ring[S * T::kStageBytes];
+  // Consecutive workgroup ids go to different XCDs; give each XCD a
+  // contiguous run of tiles (row-major), so tiles that share activation rows
+  // share that XCD's L2.
+  int tile = blockIdx.x;
+  if (tiles_total % 8 == 0) tile = (blockIdx.x % 8) * (tiles_total / 8) + blockIdx.x / 8;
+  gemm_tile<WM, WN, TM, TN, S, DEBUG>(ring, Xq, x_scale, x_rowsum, M, K, N, packed, gamma_p, Y,
+                                      relu2, acc_out, tile / tiles_n, tile % tiles_n);
+}
+
+// Many layers (a whole step): a persistent grid; workgroup g takes output
+// tiles wg_begin[g] .. wg_begin[g+1]-1 of the concatenation of every layer's
+// tiles (each layer row-major over its tm x tn tiles, starting at its
+// item_begin), from activations quantized beforehand into xq / sx / rs.
+template <int WM, int WN, int TM, int TN, int S>
+__global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
+    const GroupOp* __restrict__ ops, int n_ops, int M, const int* __restrict__ wg_begin,
+    const int8_t* __restrict__ xq, const float* __restrict__ sx, const int* __restrict__ rs) {
+  using T = Tile<WM, WN, TM, TN, S>;
+  __shared__ __align__(1024) int8_t ring[S * T::kStageBytes];
+  int item = wg_begin[blockIdx.x];
+  const int end = wg_begin[blockIdx.x + 1];
+  int op = 0;
+  while (op + 1 < n_ops && ops[op + 1].item_begin <= item) ++op;
+  const int tiles_m = (M + T::BM - 1) / T::BM;
+  bool first = true;
+  for (; item < end; ++item) {
+    while (op + 1 < n_ops && ops[op + 1].item_begin <= item) ++op;
+    const GroupOp o = ops[op];
+    const int local = item - o.item_begin;
+    const int tn = local / tiles_m, tm = local - tn * tiles_m;  // m fastest: weights reused
+    if (!first) lds_barrier();  // every wave is past the previous tile's LDS reads
+    first = false;
+    gemm_tile<WM, WN, TM, TN, S, false>(ring, xq + o.xq_off, sx + op * M, rs + op * M, M, o.K,
+                                        o.N, o.packed, o.gamma, o.Y, o.relu2, nullptr, tm, tn);
+  }
+}
+
 template <int WM, int WN, int TM, int TN, int S>
 hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M,
                       int64_t K, int64_t N, const uint8_t* packed, const float* gamma, float* Y,
@@ -307,6 +349,28 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 // 64x64) with a two-stage ring and three waves per SIMD beat 128x256 tiles
 // (fewer workgroups than slots at N = 2560) and three-stage rings (LDS-
 // limited occupancy).
+using GroupCfg = Tile<2, 2, 2, 2, 2>;
+
+int bl_group_gemm_tiles(int M, int N) {
+  return ((M + GroupCfg::BM - 1) / GroupCfg::BM) * ((N + GroupCfg::BN - 1) / GroupCfg::BN);
+}
+
+int bl_group_gemm_blocks_per_cu() {
+  int blocks = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &blocks, reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 2, 2>),
+      GroupCfg::kThreads, 0);
+  return (e == hipSuccess && blocks > 0) ? blocks : 1;
+}
+
+hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
+                                const int8_t* xq, const float* sx, const int* rs,
+                                hipStream_t s) {
+  hipLaunchKernelGGL((group_gemm_kernel<2, 2, 2, 2, 2>), dim3(G), dim3(GroupCfg::kThreads), 0,
+                     s, ops, n_ops, M, wg_begin, xq, sx, rs);
+  return hipGetLastError();
+}
+
 hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                             const float* gamma, float* Y, bool relu2, int32_t* acc_out,

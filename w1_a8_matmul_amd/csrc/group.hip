@@ -328,6 +328,13 @@ int blocks_per_cu(int threads, bool preq, size_t lds, int max_k) {
 
 bool bl_group_prequantizes(int M) { return M > kGroupInlineQuantMaxM; }
 
+hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int8_t* xq, float* sx,
+                                 int* rs, hipStream_t s) {
+  hipLaunchKernelGGL(group_quant_kernel, dim3((unsigned)(n_ops * M)), dim3(256), 0, s, ops, M,
+                     xq, sx, rs);
+  return hipGetLastError();
+}
+
 size_t bl_group_lds_bytes(int M, int max_k) {
   return (size_t)M * (size_t)(max_k + 16) + (size_t)M * kSegTiles * kTileRows * sizeof(float);
 }
@@ -362,9 +369,7 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
   const size_t lds = bl_group_lds_bytes(M, max_k);
   const bool preq = bl_group_prequantizes(M);
   if (preq) {
-    hipLaunchKernelGGL(group_quant_kernel, dim3((unsigned)(n_ops * M)), dim3(256), 0, s, ops, M,
-                       xq, sx, rs);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = bl_launch_group_quant(ops, n_ops, M, xq, sx, rs, s);
     if (e != hipSuccess) return e;
   }
   if (threads == 512)

@@ -47,3 +47,16 @@ hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu);
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
                            int max_k, int threads, int8_t* xq, float* sx, int* rs,
                            hipStream_t s);
+
+// Above kGroupMaxM tokens a group runs as one persistent tiled int8 GEMM over
+// the output tiles of all its layers (activations quantized beforehand).
+// Output tiles of one layer at M tokens; workgroups per compute unit.
+int bl_group_gemm_tiles(int M, int N);
+int bl_group_gemm_blocks_per_cu();
+hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
+                                const int8_t* xq, const float* sx, const int* rs,
+                                hipStream_t s);
+// The quantization launch of the grouped forward (one workgroup per layer
+// and token) into xq / sx / rs at each layer's xq_off.
+hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int8_t* xq, float* sx,
+                                 int* rs, hipStream_t s);
