@@ -151,8 +151,8 @@ bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, i
  * bitlinear_workspace_bytes(M, K, N) bytes (NULL allowed when that is 0).
  * Kernels by token count (both give the same bits): M <= 4 one fused launch
  * (quantization and v_dot4 contraction); larger M a quantization launch and
- * a tiled int8 MFMA GEMM.  For decode steps with several layers, the grouped
- * forward below streams all of them in one launch for M <= 16. */
+ * a tiled int8 MFMA GEMM.  For steps with several layers, the grouped
+ * forward below runs all of them together. */
 bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t M,
                                    int64_t K, int64_t N, const uint8_t* packed,
                                    const float* gamma, float* Y, bitlinear_epilogue epi,
@@ -168,19 +168,24 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      float* Y, bitlinear_epilogue epi, void* stream);
 
 /* ---- Grouped decode forward ------------------------------------------------
- * Many independent BitLinear layers that share the token count M (1..16), run
- * as one persistent launch that streams the packed weights of all layers
- * back to back.  Up to 4 tokens each workgroup quantizes the activations of
- * the layers it works on itself; above, one more launch quantizes them first
- * into the workspace.  Each layer's result is bit-identical to
- * bitlinear_forward on the same arguments.  Intended for decode, where one
- * launch per layer of a few megabytes is dominated by the launch's start-up
- * and drain. */
+ * Many independent BitLinear layers that share the token count M
+ * (1..65536), run by persistent launches over the output tiles of all
+ * layers.  Up to 16 tokens one launch streams the packed weights of all
+ * layers back to back with v_dot4 / skinny MFMA contraction; up to 4 tokens
+ * each workgroup quantizes the activations of the layers it works on itself,
+ * above one more launch quantizes them first into the workspace.  Above 16
+ * tokens the quantization launch is followed by one tiled int8 MFMA GEMM
+ * launch whose work items are the 128x128 output tiles of all layers.  Each
+ * layer's result is bit-identical to bitlinear_forward on the same
+ * arguments.  Intended for decode and short prefill, where one launch per
+ * layer of a few megabytes is dominated by the launch's start-up and
+ * drain. */
 typedef struct {
   const void* X;          /* [M][K] activations, device, 16-byte aligned */
   bitlinear_dtype dtype;  /* BITLINEAR_F32 or BITLINEAR_BF16 */
   bitlinear_epilogue epi; /* BITLINEAR_EPI_NONE or BITLINEAR_EPI_RELU2 */
-  int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 12288, and
+  int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 8388608; for
+                             M <= 16 also K <= 12288 and
                              M * (max K + 16) + M * 2048 <= 160 KiB */
   const uint8_t* packed;  /* packed weights of this layer */
   const float* gamma;     /* gamma_c of this layer (device float) */
@@ -191,7 +196,8 @@ typedef struct {
 typedef struct bitlinear_group bitlinear_group;
 
 /* Device workspace bytes for a group of n_ops layers at M tokens (the layer
- * table, the tile schedule and, for M > 4, the quantized activations).
+ * table, the tile schedule and, for M > 4, the quantized activations,
+ * their scales and row sums).
  * Returns 0 on a bad argument; needs no GPU. */
 size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops, int64_t M);
 
@@ -204,8 +210,9 @@ size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops,
 bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops, int64_t M,
                                         void* ws, size_t ws_bytes, bitlinear_group** out);
 
-/* Runs every layer of the group on `stream` (one launch, two for M > 4;
- * capturable in a HIP graph).  Calls that overlap on one group race. */
+/* Runs every layer of the group on `stream` (one launch for M <= 4, two
+ * above; capturable in a HIP graph).  Calls that overlap on one group
+ * race. */
 bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream);
 
 /* Frees the handle (not the workspace).  NULL is allowed. */

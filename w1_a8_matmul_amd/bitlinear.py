@@ -237,7 +237,8 @@ def forward_q(Xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor,
 
 # -- grouped decode forward ----------------------------------------------------
 class Group:
-    """Independent BitLinear layers sharing M (1..16), run in one launch.
+    """Independent BitLinear layers sharing M (1..65536), run by one or two
+    persistent launches (skinny kernel up to 16 tokens, tiled GEMM above).
 
     layers: list of (X, packed, gamma, N, epilogue, Y) with X [M][K] on the
     GPU and Y [M][N] float32 (allocated when None).  The tensors must stay

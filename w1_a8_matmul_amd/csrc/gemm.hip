@@ -166,6 +166,18 @@ __device__ __forceinline__ void gemm_tile(
   // Copies this wave issues per step.
   constexpr int kMyDma = T::kAPerWave + T::kBPerWave;
 
+  // The tile's activation scales and row sums: thread t < BM loads row m0 + t
+  // now (rows past M, and threads past BM, read zeros through the buffer
+  // range), so that the loads' latency hides behind the K loop; the epilogue
+  // hands them to the lanes that need them through LDS.  gamma likewise.
+  static_assert(T::kThreads >= T::BM, "one thread per tile row");
+  const uint32_t row_off = (uint32_t)min(tid, T::BM) * 4u;
+  const float my_sx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(x_scale + m0, (uint32_t)rows_here * 4u), (int)row_off, 0, 0));
+  const int my_rs = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(x_rowsum + m0, (uint32_t)rows_here * 4u), (int)row_off, 0, 0);
+  const float gamma = *gamma_p;
+
   v16i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -249,28 +261,44 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
     for (int u = 0; u < kStages; ++u) step(rd * kStages + u, u);
   }
-  // No copy may still be writing LDS when the workgroup exits.
+  // Every wave's copies have landed (none may still be writing LDS when the
+  // workgroup exits or the ring is reused) and nobody reads the ring any
+  // more: it now passes the row scales and sums around.
   wait_copies_and_reads<0>();
+  lds_barrier();
+  float* s_sx = reinterpret_cast<float*>(ring);
+  int* s_rs = reinterpret_cast<int*>(ring + T::BM * 4);
+  if (tid < T::BM) {
+    s_sx[tid] = my_sx;
+    s_rs[tid] = my_rs;
+  }
+  __syncthreads();
 
   // D layout of a 32x32 int32 MFMA tile: lane holds column (lane % 32) and,
   // in register e, row 8*(e / 4) + 4*(lane / 32) + e % 4.  One store
-  // instruction (fixed e) writes two 128-byte row segments.
-  const float gamma = *gamma_p;
+  // instruction (fixed e) writes two 128-byte row segments.  No load follows
+  // a store here, so the stores never wait for each other.
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m0 + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-      if (m >= M) continue;
-      const float sx = x_scale[m];
-      const int rs = x_rowsum[m];
+    for (int g = 0; g < 4; ++g) {
+      const int r = (wm * TM + i) * 32 + 8 * g + 4 * h;  // rows r .. r+3 of the tile
+      const float4 sx4 = *reinterpret_cast<const float4*>(s_sx + r);
+      const int4 rs4 = *reinterpret_cast<const int4*>(s_rs + r);
+      const float sxv[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
+      const int rsv[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = (int64_t)(nt0 * kTileRows) + (wn * TN + j) * 32 + r32;
-        if (n >= N) continue;
-        const int v = acc[i][j][e] - rs;
-        Y[(int64_t)m * N + n] = rescale(v, sx, gamma, relu2 != 0);
-        if constexpr (DEBUG) acc_out[(int64_t)m * N + n] = v;
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + r + q;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int64_t n = (int64_t)(nt0 * kTileRows) + (wn * TN + j) * 32 + r32;
+          if (n >= N) continue;
+          const int v = acc[i][j][4 * g + q] - rsv[q];
+          Y[(int64_t)m * N + n] = rescale(v, sxv[q], gamma, relu2 != 0);
+          if constexpr (DEBUG) acc_out[(int64_t)m * N + n] = v;
+        }
       }
     }
   }
