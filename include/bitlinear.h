@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_ABI_VERSION 2
 
 typedef enum {
   BITLINEAR_OK = 0,
@@ -111,10 +111,16 @@ size_t bitlinear_packed_bytes(int64_t N, int64_t K);
  * (per-row double sums).  0 on a bad shape. */
 size_t bitlinear_weights_workspace_bytes(int64_t N, int64_t K);
 
-/* Workspace bytes bitlinear_forward needs for M tokens x K -> N (quantized
- * activations, scales and row sums when the large-M path runs; may be 0).
- * Returns (size_t)-1 on a bad shape. */
+/* Workspace bytes bitlinear_forward needs for M tokens x K -> N (may be 0):
+ * when the large-M path runs, the quantized activations, scales and row
+ * sums, then bitlinear_forward_q's workspace.  Returns (size_t)-1 on a bad
+ * shape.  Needs no GPU. */
 size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* Workspace bytes bitlinear_forward_q can use for M x K -> N (about 16 MiB:
+ * counters, then partial int32 sums of output tiles cut along K).
+ * Returns (size_t)-1 on a bad shape.  Needs no GPU. */
+size_t bitlinear_forward_q_workspace_bytes(int64_t M, int64_t K, int64_t N);
 
 /* Absmean ternary quantization and packing of float W [N][K] ("BitNet b1.58
  * 2B4T Technical Report" card, Method Adaptation: absmean to {-1,0,+1}, four
@@ -151,8 +157,10 @@ bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, i
  * bitlinear_workspace_bytes(M, K, N) bytes (NULL allowed when that is 0).
  * Kernels by token count (both give the same bits): M <= 4 one fused launch
  * (quantization and v_dot4 contraction); larger M a quantization launch and
- * a tiled int8 MFMA GEMM.  For steps with several layers, the grouped
- * forward below runs all of them together. */
+ * the tiled int8 MFMA GEMM of bitlinear_forward_q, with its workspace (which
+ * the quantization launch clears, so `ws` needs no initial contents).  For
+ * steps with several layers, the grouped forward below runs all of them
+ * together. */
 bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t M,
                                    int64_t K, int64_t N, const uint8_t* packed,
                                    const float* gamma, float* Y, bitlinear_epilogue epi,
@@ -161,11 +169,19 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
 
 /* The same forward from activations already quantized by
  * bitlinear_quantize_acts: Xq [M][K], x_scale [M], x_rowsum [M] (all three
- * required). */
+ * required).  The output tiles (128 x 128) are spread over the compute
+ * units one workgroup each; when they do not divide evenly, each tile of the
+ * last, partial round is instead cut along K into pieces, one workgroup
+ * each, whose exact int32 partial sums meet in `ws` (same bits either way).  `ws` (device, 16-byte aligned, at least
+ * bitlinear_forward_q_workspace_bytes) enables that; NULL runs one workgroup
+ * per tile.  Its first 4 KiB (counters) must be zero the first time a
+ * workspace is used, and every call leaves them zero again; the rest needs
+ * no initial contents.  Calls that share a workspace must not overlap. */
 bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      const int32_t* x_rowsum, int64_t M, int64_t K,
                                      int64_t N, const uint8_t* packed, const float* gamma,
-                                     float* Y, bitlinear_epilogue epi, void* stream);
+                                     float* Y, bitlinear_epilogue epi, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /* ---- Grouped decode forward ------------------------------------------------
  * Many independent BitLinear layers that share the token count M

@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert L.bitlinear_abi_version() == 1
+    assert L.bitlinear_abi_version() == 2
     for s in range(8):
         assert L.bitlinear_status_string(s).decode()
     assert L.bitlinear_status_string(99).decode() == "unknown status"
@@ -48,6 +48,11 @@ def test_packed_and_workspace_sizes(L):
     assert big >= 2048 * 2560 + 2 * 2048 * 4
     assert L.bitlinear_workspace_bytes(-1, 2560, 6912) == ctypes.c_size_t(-1).value
     assert L.bitlinear_workspace_bytes(4, 100, 6912) == ctypes.c_size_t(-1).value
+    qws = L.bitlinear_forward_q_workspace_bytes(2048, 2560, 6912)
+    assert qws >= 4096 + 256 * 128 * 128 * 4  # counters, a partial tile per piece
+    assert big >= 2048 * 2560 + 2 * 2048 * 4 + qws  # forward holds forward_q's workspace
+    assert L.bitlinear_forward_q_workspace_bytes(0, 2560, 6912) == 0
+    assert L.bitlinear_forward_q_workspace_bytes(8, 100, 6912) == ctypes.c_size_t(-1).value
 
 
 def _err(L):
@@ -115,11 +120,14 @@ def test_forward_validation(L):
 
 def test_forward_q_validation(L):
     f = L.bitlinear_forward_q
-    assert f(A, A, A, 4, 256, 16, A, A, A, 9, None) == ERR_ARG
-    assert f(A, A, None, 4, 256, 16, A, A, A, 0, None) == ERR_NULL
-    assert f(A, A, A, 4, 256, 17, A, A, A, 0, None) == ERR_SHAPE
-    assert f(A, A, A, 4, 256, 16, A, U, A, 0, None) == ERR_ALIGN
-    assert f(None, None, None, 0, 256, 16, None, None, None, 0, None) == OK
+    assert f(A, A, A, 4, 256, 16, A, A, A, 9, None, 0, None) == ERR_ARG
+    assert f(A, A, None, 4, 256, 16, A, A, A, 0, None, 0, None) == ERR_NULL
+    assert f(A, A, A, 4, 256, 17, A, A, A, 0, None, 0, None) == ERR_SHAPE
+    assert f(A, A, A, 4, 256, 16, A, U, A, 0, None, 0, None) == ERR_ALIGN
+    # a workspace, when given, must be large enough and aligned
+    assert f(A, A, A, 4, 256, 16, A, A, A, 0, A, 1024, None) == ERR_WS
+    assert f(A, A, A, 4, 256, 16, A, A, A, 0, U, 1 << 30, None) == ERR_ALIGN
+    assert f(None, None, None, 0, 256, 16, None, None, None, 0, None, 0, None) == OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -399,3 +399,77 @@ def test_prefill_repeatable(dev, bl, orc):
     xq, sx, _ = orc.quant_acts(X[rows], bf16=True)
     y_ref = orc.rescale(orc.int_matmul(xq, qw), sx, gc)
     assert np.array_equal(first.cpu().numpy()[rows], y_ref)
+
+
+# ---------------------------------------------------------------------------
+# prefill GEMM: the last, partial round of tiles shared along K
+# ---------------------------------------------------------------------------
+SPLIT_SHAPES = [
+    (2048, 2560, 6912),   # 864 tiles of 128x128: a partial last round
+    (2048, 6912, 2560),   # 320 tiles
+    (512, 4096, 22016),   # 688 tiles
+    (300, 2816, 1040),    # fewer tiles than compute units; ragged M and N; 22 steps
+    (130, 256, 16),       # two ragged tiles of two steps
+    (4096, 256, 4096),    # 1024 tiles: whole rounds only
+]
+
+
+@pytest.mark.parametrize("M,K,N", SPLIT_SHAPES)
+def test_forward_q_split_remainder(dev, bl, orc, M, K, N):
+    # int32 partial sums are exact in any order, so sharing tiles along K
+    # gives the bits of one workgroup per tile; the tile counters return to
+    # zero after every call (the same workspace is reused); sampled rows
+    # match the oracle.
+    W = wl.gen_weight(8200 + N % 97, N, K)
+    X, _ = wl.gen_acts(8300 + M, M, K, "normal_bf16")
+    packed, gamma, qw, gc = _quantize_both(bl, orc, W, dev)
+    Xq, sx, rs = bl.quantize_acts(_acts_gpu(X, True, dev))
+    plain = bl.forward_q(Xq, sx, rs, packed, gamma, N, split_remainder=False)
+    ws = bl.forward_q_workspace(M, K, N, dev)
+    for _ in range(3):
+        assert torch.equal(bl.forward_q(Xq, sx, rs, packed, gamma, N, workspace=ws), plain)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(M).integers(0, M, 6)]))
+    xq, sxr, _ = orc.quant_acts(X[rows], bf16=True)
+    y_ref = orc.rescale(orc.int_matmul(xq, qw), sxr, gc)
+    assert np.array_equal(plain.cpu().numpy()[rows], y_ref)
+
+
+def test_forward_workspace_contents_do_not_matter(dev, bl, orc):
+    # forward clears the GEMM's tile counters itself: a workspace full of
+    # 0xff bytes gives the oracle's bits, with ReLU^2 and the debug outputs.
+    M, K, N = 300, 2816, 1040
+    W = wl.gen_weight(8401, N, K)
+    X, _ = wl.gen_acts(8402, M, K, "outlier_bf16")
+    packed, gamma, qw, gc = _quantize_both(bl, orc, W, dev)
+    ws = torch.full((bl.workspace_bytes(M, K, N),), 0xFF, dtype=torch.uint8, device=dev)
+    Y, dbg = bl.forward(_acts_gpu(X, True, dev), packed, gamma, N, epilogue="relu2",
+                        debug=True, workspace=ws)
+    y_ref, xq_ref, sx_ref, acc_ref = orc.forward(X, qw, gc, bf16=True)
+    assert np.array_equal(dbg["acc"].cpu().numpy(), acc_ref)
+    assert np.array_equal(Y.cpu().numpy(), orc.relu2(y_ref))
+
+
+def test_forward_q_split_graph_replay(dev, bl, orc):
+    # Replays of a captured call reuse the workspace; each must match eager.
+    M, K, N = 2048, 2560, 6912
+    W = wl.gen_weight(8501, N, K)
+    X, _ = wl.gen_acts(8502, M, K, "normal_bf16")
+    packed, gamma, qw, gc = _quantize_both(bl, orc, W, dev)
+    Xq, sx, rs = bl.quantize_acts(_acts_gpu(X, True, dev))
+    eager = bl.forward_q(Xq, sx, rs, packed, gamma, N, split_remainder=False)
+    ws = bl.forward_q_workspace(M, K, N, dev)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bl.forward_q(Xq, sx, rs, packed, gamma, N, out=out, workspace=ws)  # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        bl.forward_q(Xq, sx, rs, packed, gamma, N, out=out, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"

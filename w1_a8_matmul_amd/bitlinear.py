@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_weights_workspace_bytes.restype = _sz
     L.bitlinear_workspace_bytes.argtypes = [_i64, _i64, _i64]
     L.bitlinear_workspace_bytes.restype = _sz
+    L.bitlinear_forward_q_workspace_bytes.argtypes = [_i64, _i64, _i64]
+    L.bitlinear_forward_q_workspace_bytes.restype = _sz
     L.bitlinear_quantize_weights.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
     L.bitlinear_pack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_unpack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
@@ -71,7 +73,7 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p,
                                     ctypes.c_int, ctypes.POINTER(Debug), _p, _sz, _p]
     L.bitlinear_forward_q.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p,
-                                      ctypes.c_int, _p]
+                                      ctypes.c_int, _p, _sz, _p]
     for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
                  "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
                  "bitlinear_forward_q"):
@@ -222,14 +224,30 @@ def forward(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
     return (out, dbg) if debug else out
 
 
+def forward_q_workspace(M: int, K: int, N: int, device) -> torch.Tensor:
+    """A workspace for forward_q, counters zeroed (reusable across calls)."""
+    n = lib().bitlinear_forward_q_workspace_bytes(M, K, N)
+    if n == ctypes.c_size_t(-1).value:
+        raise BitLinearError(f"bad shape M={M} K={K} N={N}")
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
 def forward_q(Xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor,
               packed: torch.Tensor, gamma: torch.Tensor, N: int,
-              epilogue: Optional[str] = None, out: Optional[torch.Tensor] = None):
+              epilogue: Optional[str] = None, out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None, split_remainder: bool = True):
+    """Y from pre-quantized activations.  ``workspace`` (from
+    forward_q_workspace, counters zero) is allocated when None;
+    split_remainder=False runs one workgroup per tile without it."""
     M, K = Xq.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    if workspace is None and split_remainder:
+        workspace = forward_q_workspace(M, K, N, Xq.device)
+    ws = workspace if split_remainder else None
     st = lib().bitlinear_forward_q(_ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), M, K, N,
                                    _ptr(packed), _ptr(gamma), _ptr(out), EPI[epilogue],
+                                   _ptr(ws), ws.numel() if ws is not None else 0,
                                    _stream())
     check(st, "bitlinear_forward_q")
     return out

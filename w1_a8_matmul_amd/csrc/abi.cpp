@@ -53,8 +53,13 @@ bitlinear_status check_nk(int64_t N, int64_t K) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace of the large-M path: int8 activations, scales, row sums.
+// Forward workspace above the fused small-M path: quantized activations,
+// scales and row sums, then the GEMM's own workspace.
 size_t q_workspace(int64_t M, int64_t K) {
   return align256((size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
+}
+size_t forward_workspace(int64_t M, int64_t K, int64_t N) {
+  return q_workspace(M, K) + align256(bl_gemm_workspace_bytes(M, K, N));
 }
 
 // Grouped forward: device workspace layout (layer table, tile schedule).
@@ -152,7 +157,13 @@ size_t bitlinear_weights_workspace_bytes(int64_t N, int64_t K) {
 size_t bitlinear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || N < 1 || K < 1 || N % 16 != 0 || K % 256 != 0) return (size_t)-1;
   if (M == 0 || bl_gemv_supports(M, K)) return 0;
-  return q_workspace(M, K);
+  return forward_workspace(M, K, N);
+}
+
+size_t bitlinear_forward_q_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 1 || K < 1 || N % 16 != 0 || K % 256 != 0) return (size_t)-1;
+  if (M == 0) return 0;
+  return bl_gemm_workspace_bytes(M, K, N);
 }
 
 bitlinear_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
@@ -212,7 +223,7 @@ bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, i
   if (!aligned16(X) || !aligned16(Xq) || !aligned16(x_scale) ||
       (x_rowsum && !aligned16(x_rowsum)))
     return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
-  return from_hip(bl_launch_quant_acts(X, (int)dtype, M, K, Xq, x_scale, x_rowsum,
+  return from_hip(bl_launch_quant_acts(X, (int)dtype, M, K, Xq, x_scale, x_rowsum, nullptr, 0,
                                        static_cast<hipStream_t>(stream)),
                   "bitlinear_quantize_acts");
 }
@@ -247,7 +258,7 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
                                    xs_out, acc_out, s),
                     "bitlinear_forward");
 
-  const size_t need = q_workspace(M, K);
+  const size_t need = forward_workspace(M, K, N);
   if (!ws || ws_bytes < need)
     return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 ws ? ws_bytes : (size_t)0);
@@ -257,20 +268,25 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
   float* sx = reinterpret_cast<float*>(base + align256((size_t)M * (size_t)K));
   int32_t* rs = reinterpret_cast<int32_t*>(base + align256((size_t)M * (size_t)K) +
                                            align256((size_t)M * 4));
-  hipError_t e = bl_launch_quant_acts(X, (int)dtype, M, K, xq, sx, rs, s);
+  int* gemm_ws = reinterpret_cast<int*>(base + q_workspace(M, K));
+  // The quantization launch also clears the GEMM's counters, so the
+  // workspace's contents on entry do not matter.
+  hipError_t e = bl_launch_quant_acts(X, (int)dtype, M, K, xq, sx, rs, gemm_ws,
+                                      (int)(bl_gemm_counter_bytes() / sizeof(int)), s);
   if (e == hipSuccess && xq_out)
     e = hipMemcpyAsync(xq_out, xq, (size_t)M * (size_t)K, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess && xs_out)
     e = hipMemcpyAsync(xs_out, sx, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
-    e = bl_launch_gemm_q(xq, sx, rs, M, K, N, packed, gamma, Y, relu2, acc_out, s);
+    e = bl_launch_gemm_q(xq, sx, rs, M, K, N, packed, gamma, Y, relu2, acc_out, gemm_ws, s);
   return from_hip(e, "bitlinear_forward");
 }
 
 bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      const int32_t* x_rowsum, int64_t M, int64_t K, int64_t N,
                                      const uint8_t* packed, const float* gamma, float* Y,
-                                     bitlinear_epilogue epi, void* stream) {
+                                     bitlinear_epilogue epi, void* ws, size_t ws_bytes,
+                                     void* stream) {
   if (epi != BITLINEAR_EPI_NONE && epi != BITLINEAR_EPI_RELU2)
     return fail(BITLINEAR_ERR_ARG, "unknown epilogue %d", (int)epi);
   if (M < 0) return fail(BITLINEAR_ERR_SHAPE, "M=%lld is negative", (long long)M);
@@ -283,8 +299,15 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
   if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(x_rowsum) || !aligned16(packed) ||
       !aligned16(gamma) || !aligned16(Y))
     return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (ws) {
+    const size_t need = bl_gemm_workspace_bytes(M, K, N);
+    if (ws_bytes < need)
+      return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  ws_bytes);
+    if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
   return from_hip(bl_launch_gemm_q(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
-                                   epi == BITLINEAR_EPI_RELU2, nullptr,
+                                   epi == BITLINEAR_EPI_RELU2, nullptr, ws,
                                    static_cast<hipStream_t>(stream)),
                   "bitlinear_forward_q");
 }

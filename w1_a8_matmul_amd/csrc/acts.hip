@@ -12,10 +12,13 @@ template <int DT>
 __global__ __launch_bounds__(256) void quant_acts_kernel(const void* __restrict__ X, int64_t K,
                                                          int8_t* __restrict__ Xq,
                                                          float* __restrict__ x_scale,
-                                                         int32_t* __restrict__ x_rowsum) {
+                                                         int32_t* __restrict__ x_rowsum,
+                                                         int* __restrict__ zero, int n_zero) {
   __shared__ float red_f[4];
   __shared__ int red_i[4];
   const int64_t m = blockIdx.x;
+  if (m == 0)
+    for (int i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0;
   const RowQuant rq = row_absmax_scale<DT, 256>(X, m, K, red_f);
   const int sum = row_quantize_to<DT, 256>(X, m, K, rq.qs, Xq + m * K, red_i);
   if (threadIdx.x == 0) {
@@ -27,12 +30,14 @@ __global__ __launch_bounds__(256) void quant_acts_kernel(const void* __restrict_
 }  // namespace
 
 hipError_t bl_launch_quant_acts(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
-                                float* x_scale, int32_t* x_rowsum, hipStream_t s) {
+                                float* x_scale, int32_t* x_rowsum, int* zero, int n_zero,
+                                hipStream_t s) {
+  if (!zero) n_zero = 0;
   if (dtype == 1)
     hipLaunchKernelGGL(quant_acts_kernel<1>, dim3((unsigned)M), dim3(256), 0, s, X, K, Xq,
-                       x_scale, x_rowsum);
+                       x_scale, x_rowsum, zero, n_zero);
   else
     hipLaunchKernelGGL(quant_acts_kernel<0>, dim3((unsigned)M), dim3(256), 0, s, X, K, Xq,
-                       x_scale, x_rowsum);
+                       x_scale, x_rowsum, zero, n_zero);
   return hipGetLastError();
 }

@@ -117,16 +117,24 @@ hipError_t bl_launch_pack(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packe
                           hipStream_t s);
 hipError_t bl_launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
                             hipStream_t s);
+// Per-token activation quantization; also zeroes n_zero ints at `zero`
+// (may be null) for the launch that follows.
 hipError_t bl_launch_quant_acts(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
-                                float* x_scale, int32_t* x_rowsum, hipStream_t s);
+                                float* x_scale, int32_t* x_rowsum, int* zero, int n_zero,
+                                hipStream_t s);
 // Small-M fused forward (activation quantization inside the kernel).
 bool bl_gemv_supports(int64_t M, int64_t K);
 hipError_t bl_launch_gemv(const void* X, int dtype, int64_t M, int64_t K, int64_t N,
                           const uint8_t* packed, const float* gamma, float* Y, bool relu2,
                           int8_t* xq_out, float* xscale_out, int32_t* acc_out,
                           hipStream_t s);
-// Forward from quantized activations on the int8 MFMA units.
+// Forward from quantized activations on the int8 MFMA units.  gemm_ws
+// (bl_gemm_workspace_bytes, its first bl_gemm_counter_bytes zero on entry
+// and left zero) lets the last, partial round of tiles be shared along K;
+// null runs one workgroup per tile.
+size_t bl_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+size_t bl_gemm_counter_bytes();
 hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                             const float* gamma, float* Y, bool relu2, int32_t* acc_out,
-                            hipStream_t s);
+                            void* gemm_ws, hipStream_t s);

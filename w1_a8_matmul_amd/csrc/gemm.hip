@@ -27,6 +27,8 @@
 // The load/unpack/multiply order follows the kernel outline of the "BitNet
 // b1.58 2B4T Technical Report" card, section "Method Adaptation"; the tiling
 // is this library's own, for gfx950.
+#include <algorithm>
+
 #include "common.hpp"
 #include "group.hpp"
 
@@ -56,6 +58,14 @@ __device__ __forceinline__ v4i rsrc_words(const void* p, uint32_t bytes) {
 __device__ __forceinline__ void copy16(v4i rs, uint32_t voff, void* lds) {
   const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :: "v"(voff), "s"(la), "s"(rs) : "memory", "m0");
+}
+
+// The same copy with the sc1 cache policy (device-coherent: it does not
+// hit data that another XCD's L2 may hold stale).
+__device__ __forceinline__ void copy16_coherent(v4i rs, uint32_t voff, void* lds) {
+  const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc1 lds"
                :: "v"(voff), "s"(la), "s"(rs) : "memory", "m0");
 }
 
@@ -102,27 +112,27 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One output tile (tm, tn) of one layer: the whole K loop and the
-// epilogue.  `ring` is the workgroup's LDS ring (S stages of kStageBytes).
-template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
-__device__ __forceinline__ void gemm_tile(
-    int8_t* ring, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ x_rowsum, int M, int K, int N,
-    const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
-    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tm, int tn) {
+// The K loop of output tile (tm, tn) of one layer over pipeline steps
+// [k0, k1) (128 columns each) into acc.  `ring` is the workgroup's LDS ring
+// (S stages of kStageBytes).  Every wave leaves with its copies landed and
+// its LDS reads returned; other waves may still be reading the ring.
+template <int WM, int WN, int TM, int TN, int S>
+__device__ __forceinline__ void tile_mainloop(int8_t* ring, const int8_t* __restrict__ Xq,
+                                              int M, int K, int N,
+                                              const uint8_t* __restrict__ packed, int tm,
+                                              int tn, int k0, int k1,
+                                              v16i (&acc)[TM][TN]) {
   using T = Tile<WM, WN, TM, TN, S>;
   constexpr int kStages = S;
   auto stage_ptr = [&](int slot) -> int8_t* { return ring + slot * T::kStageBytes; };
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  (void)tid;
   const int m0 = tm * T::BM;
   const int nt0 = tn * T::kBTiles;  // first 16-row weight tile
   const int ntiles = N / kTileRows;
   const int kblocks = K / kTileCols;
-  const int nsteps = K / kStepCols;
 
   // Buffer ranges: rows past M and weight tiles past N read as zero.
   const int rows_here = min(T::BM, M - m0);
@@ -143,7 +153,7 @@ __device__ __forceinline__ void gemm_tile(
   // wait for all of them before LDS reads.
   auto dma = [&](int kh, int slot) {
     int8_t* base = stage_ptr(slot);
-    const uint32_t past = kh < nsteps ? 0u : 0x80000000u;
+    const uint32_t past = kh < k1 ? 0u : 0x80000000u;
 #pragma unroll
     for (int p = 0; p < T::kAPerWave; ++p) {
       const int q = wave + p * T::kWaves;
@@ -166,19 +176,7 @@ __device__ __forceinline__ void gemm_tile(
   // Copies this wave issues per step.
   constexpr int kMyDma = T::kAPerWave + T::kBPerWave;
 
-  // The tile's activation scales and row sums: thread t < BM loads row m0 + t
-  // now (rows past M, and threads past BM, read zeros through the buffer
-  // range), so that the loads' latency hides behind the K loop; the epilogue
-  // hands them to the lanes that need them through LDS.  gamma likewise.
-  static_assert(T::kThreads >= T::BM, "one thread per tile row");
-  const uint32_t row_off = (uint32_t)min(tid, T::BM) * 4u;
-  const float my_sx = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(x_scale + m0, (uint32_t)rows_here * 4u), (int)row_off, 0, 0));
-  const int my_rs = (int)__builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(x_rowsum + m0, (uint32_t)rows_here * 4u), (int)row_off, 0, 0);
-  const float gamma = *gamma_p;
 
-  v16i acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -226,9 +224,10 @@ __device__ __forceinline__ void gemm_tile(
       }
   };
 
-  // Prologue: copies of steps 0..S-1 into every slot; first half of step 0.
+  // Prologue: copies of steps k0..k0+S-1 into every slot; first half of
+  // step k0.
 #pragma unroll
-  for (int st = 0; st < kStages; ++st) dma(st, st);
+  for (int st = 0; st < kStages; ++st) dma(k0 + st, st);
   wait_copies_and_reads<(kStages - 1) * kMyDma>();
   lds_barrier();
   Frag f0, f1;
@@ -256,21 +255,64 @@ __device__ __forceinline__ void gemm_tile(
   // instead of a remainder loop (a second loop makes the compiler shuffle
   // the accumulators every iteration).  Padding steps read zero activations
   // (their copies are out of range) and add nothing.
-  const int nrounds = (nsteps + kStages - 1) / kStages;
+  const int nrounds = (k1 - k0 + kStages - 1) / kStages;
   for (int rd = 0; rd < nrounds; ++rd) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) step(rd * kStages + u, u);
+    for (int u = 0; u < kStages; ++u) step(k0 + rd * kStages + u, u);
   }
-  // Every wave's copies have landed (none may still be writing LDS when the
-  // workgroup exits or the ring is reused) and nobody reads the ring any
-  // more: it now passes the row scales and sums around.
+  // No copy of this wave may still be writing LDS when the ring is reused
+  // or the workgroup exits.
   wait_copies_and_reads<0>();
+}
+
+// Activation scale and row sum of one tile row: thread t < BM holds row
+// m0 + t (rows past M, and threads past BM, read zeros through the buffer
+// range).  Loaded before the K loop so that the loads' latency hides behind
+// it; the epilogue hands them to the lanes that need them through LDS.
+struct RowScale {
+  float sx;
+  int rs;
+};
+
+template <int WM, int WN, int TM, int TN, int S>
+__device__ __forceinline__ RowScale load_row_scale(const float* __restrict__ x_scale,
+                                                   const int32_t* __restrict__ x_rowsum, int M,
+                                                   int tm) {
+  using T = Tile<WM, WN, TM, TN, S>;
+  static_assert(T::kThreads >= T::BM, "one thread per tile row");
+  const int m0 = tm * T::BM;
+  const uint32_t rows_here = (uint32_t)min(T::BM, M - m0);
+  const uint32_t off = (uint32_t)min((int)threadIdx.x, T::BM) * 4u;
+  RowScale r;
+  r.sx = __uint_as_float(
+      __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(x_scale + m0, rows_here * 4u), (int)off, 0, 0));
+  r.rs = (int)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(x_rowsum + m0, rows_here * 4u),
+                                                   (int)off, 0, 0);
+  return r;
+}
+
+// Epilogue of tile (tm, tn): Y = ((acc - rowsum) * s_x) * gamma, then the
+// optional ReLU^2.  Called by every wave after its K loop.
+template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
+__device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM][TN],
+                                              RowScale own, float gamma, int M, int N,
+                                              float* __restrict__ Y, int relu2,
+                                              int32_t* __restrict__ acc_out, int tm, int tn) {
+  using T = Tile<WM, WN, TM, TN, S>;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int m0 = tm * T::BM;
+  const int nt0 = tn * T::kBTiles;
+  // Every wave is past its K loop (its copies landed, its ring reads
+  // returned): the ring now passes the row scales and sums around.
   lds_barrier();
   float* s_sx = reinterpret_cast<float*>(ring);
   int* s_rs = reinterpret_cast<int*>(ring + T::BM * 4);
   if (tid < T::BM) {
-    s_sx[tid] = my_sx;
-    s_rs[tid] = my_rs;
+    s_sx[tid] = own.sx;
+    s_rs[tid] = own.rs;
   }
   __syncthreads();
 
@@ -304,23 +346,173 @@ __device__ __forceinline__ void gemm_tile(
   }
 }
 
-// One layer: a workgroup per output tile.
+
+// One output tile, whole K: the K loop and the epilogue.
 template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
-__global__ __launch_bounds__(64 * WM * WN, 3) void gemm_kernel(
+__device__ __forceinline__ void gemm_tile(
+    int8_t* ring, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ x_rowsum, int M, int K, int N,
+    const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
+    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tm, int tn) {
+  const RowScale own = load_row_scale<WM, WN, TM, TN, S>(x_scale, x_rowsum, M, tm);
+  const float gamma = *gamma_p;
+  v16i acc[TM][TN];
+  tile_mainloop<WM, WN, TM, TN, S>(ring, Xq, M, K, N, packed, tm, tn, 0, K / kStepCols, acc);
+  tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, relu2, acc_out, tm,
+                                          tn);
+}
+
+// ---- Split tiles: the remainder round, cut along K ----
+// When the output tiles do not divide evenly among the compute units, the
+// tiles of the last, partial round are not given one workgroup each (most
+// compute units would idle while a few run one more tile).  Instead each of
+// those R tiles is cut along K into f pieces (f = compute units / R, at
+// least two pipeline steps each), one workgroup per piece.  int32 sums are
+// exact in any order, so the pieces of a tile combine bit for bit: every
+// piece stores its partial sums in its workspace slot and counts itself in
+// at the tile's counter; the last one to arrive adds the others' sums to its
+// own and runs the epilogue.  Nobody waits for anybody, so the workgroups
+// need not be resident together.
+struct SkPlan {
+  int tiles_dp;  // tiles with one workgroup each (the first tiles_dp tiles)
+  int tiles_sk;  // R: the remaining tiles, after them
+  int steps;     // S: pipeline steps per tile
+  int pieces;    // f: pieces per remaining tile (R * f workgroups; 0: none)
+};
+
+constexpr int kSkMaxGroups = 256;      // at most this many pieces in all
+constexpr int kSkCounterInts = 1024;   // one counter per remaining tile
+constexpr int kSkSlotInts = 128 * 128; // partial sums of one 128x128 tile
+
+// Pipeline steps [k0, k1) of piece `piece` of a tile.
+__device__ __forceinline__ int sk_piece_begin(const SkPlan& p, int piece) {
+  return piece * p.steps / p.pieces;
+}
+
+// Hands this workgroup's piece of remaining tile t over.  Returns true (for
+// the whole workgroup) when it was the last piece to arrive; acc then holds
+// the tile's whole sums.  Register e = 4q..4q+3 of block (i, j) of thread
+// tid sits at int4 index ((i*TN + j)*4 + q)*threads + tid of the slot.  Slot
+// stores and loads carry the sc1 cache policy (device-coherent: they do not
+// stop at the per-XCD L2s, which are not coherent with each other).  The
+// counter is raised only after every wave's stores have completed.  The
+// last piece brings the other slots in through LDS (each wave its own 8 KiB
+// of the ring), so that all of a slot's loads are in flight at once without
+// holding registers.
+constexpr int kCoherent = 16;  // cache policy of the slot stores: sc1
+
+template <int WM, int WN, int TM, int TN, int S>
+__device__ __forceinline__ bool sk_contribute(int8_t* ring, v16i (&acc)[TM][TN],
+                                              const SkPlan& p, int* __restrict__ sk_ws,
+                                              int t, int g) {
+  using T = Tile<WM, WN, TM, TN, S>;
+  static_assert(T::BM * T::BN == kSkSlotInts, "slot holds one tile");
+  constexpr int kChunks = TM * TN * 4;  // 16-byte stores per thread
+  constexpr int kHalf = kChunks / 2;
+  static_assert(T::kWaves * kHalf * 1024 + 64 <= S * T::kStageBytes, "ring holds the halves");
+  int* counters = sk_ws;
+  int* slots = sk_ws + kSkCounterInts;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const auto mine = make_rsrc(slots + (int64_t)g * kSkSlotInts, kSkSlotInts * 4u);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4u v = {(uint32_t)acc[i][j][4 * q], (uint32_t)acc[i][j][4 * q + 1],
+                       (uint32_t)acc[i][j][4 * q + 2], (uint32_t)acc[i][j][4 * q + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v, mine, ((((i * TN + j) * 4 + q) * T::kThreads) + tid) * 16, 0, kCoherent);
+      }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave's stores have completed; the ring is free
+  const int g_first = t * p.pieces;
+  const int g_last = g_first + p.pieces - 1;
+  // Past the waves' 8 KiB regions, so that no wave's copies overwrite it
+  // while another wave still reads it.
+  int* s_last = reinterpret_cast<int*>(ring + T::kWaves * kHalf * 1024);
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(counters + t, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == g_last - g_first ? 1 : 0;
+    // Back to zero for the next launch (nobody else touches it in this one).
+    if (last) __hip_atomic_store(counters + t, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = last;
+  }
+  __syncthreads();
+  if (*s_last == 0) return false;
+  int8_t* region = ring + wave * (kHalf * 1024);
+  for (int o = g_first; o <= g_last; ++o) {
+    if (o == g) continue;
+    v4i src = rsrc_words(slots + (int64_t)o * kSkSlotInts, kSkSlotInts * 4u);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) src[w] = __builtin_amdgcn_readfirstlane(src[w]);  // uniform
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int c = 0; c < kHalf; ++c) {
+        const int ch = half * kHalf + c;
+        copy16_coherent(src, (uint32_t)((ch * T::kThreads + wave * 64 + lane) * 16),
+                        region + c * 1024);
+      }
+      wait_copies_and_reads<0>();
+#pragma unroll
+      for (int c = 0; c < kHalf; ++c) {
+        const int ch = half * kHalf + c;
+        const int blk = ch / 4, q = ch % 4, i = blk / TN, j = blk % TN;
+        const v4i v = *reinterpret_cast<const v4i*>(region + c * 1024 + lane * 16);
+        acc[i][j][4 * q] += v.x;
+        acc[i][j][4 * q + 1] += v.y;
+        acc[i][j][4 * q + 2] += v.z;
+        acc[i][j][4 * q + 3] += v.w;
+      }
+      // This wave's reads of its region return before its next copies land
+      // there (the adds above consume them; the copy asm is a memory fence
+      // for the compiler).
+    }
+  }
+  return true;
+}
+
+// One layer.  Workgroups below plan.tiles_dp take one output tile each
+// (whole K); the tiles_sk * pieces workgroups after them take one piece of
+// a remaining tile each (sk_ws: counters, then one slot per piece).
+template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
+__global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
     float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tiles_n,
-    int tiles_total) {
+    SkPlan plan, int* __restrict__ sk_ws) {
   using T = Tile<WM, WN, TM, TN, S>;
   __shared__ __align__(1024) int8_t ring[S * T::kStageBytes];
-  // Consecutive workgroup ids go to different XCDs; give each XCD a
-  // contiguous run of tiles (row-major), so tiles that share activation rows
-  // share that XCD's L2.
-  int tile = blockIdx.x;
-  if (tiles_total % 8 == 0) tile = (blockIdx.x % 8) * (tiles_total / 8) + blockIdx.x / 8;
-  gemm_tile<WM, WN, TM, TN, S, DEBUG>(ring, Xq, x_scale, x_rowsum, M, K, N, packed, gamma_p, Y,
-                                      relu2, acc_out, tile / tiles_n, tile % tiles_n);
+  const int b = blockIdx.x;
+  const bool split = b >= plan.tiles_dp;
+  int tile, k0 = 0, k1 = plan.steps, g = 0, t = 0;
+  if (!split) {
+    // Whole tiles: consecutive workgroup ids go to different XCDs; give each
+    // XCD a contiguous run of tiles (row-major), so tiles that share
+    // activation rows share that XCD's L2.
+    const int n = plan.tiles_dp;
+    tile = n % 8 == 0 ? (b % 8) * (n / 8) + b / 8 : b;
+  } else {
+    g = b - plan.tiles_dp;
+    t = g / plan.pieces;
+    const int piece = g - t * plan.pieces;
+    tile = plan.tiles_dp + t;
+    k0 = sk_piece_begin(plan, piece);
+    k1 = sk_piece_begin(plan, piece + 1);
+  }
+  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  const RowScale own = load_row_scale<WM, WN, TM, TN, S>(x_scale, x_rowsum, M, tm);
+  const float gamma = *gamma_p;
+  v16i acc[TM][TN];
+  tile_mainloop<WM, WN, TM, TN, S>(ring, Xq, M, K, N, packed, tm, tn, k0, k1, acc);
+  if (!split || sk_contribute<WM, WN, TM, TN, S>(ring, acc, plan, sk_ws, t, g))
+    tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, relu2, acc_out, tm,
+                                            tn);
 }
 
 // Many layers (a whole step): a persistent grid; workgroup g takes output
@@ -351,22 +543,51 @@ __global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kSkMaxGroups;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      return kSkMaxGroups;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
 template <int WM, int WN, int TM, int TN, int S>
 hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M,
                       int64_t K, int64_t N, const uint8_t* packed, const float* gamma, float* Y,
-                      bool relu2, int32_t* acc_out, hipStream_t s) {
+                      bool relu2, int32_t* acc_out, int* sk_ws, hipStream_t s) {
   using T = Tile<WM, WN, TM, TN, S>;
   const int tiles_m = (int)((M + T::BM - 1) / T::BM);
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
   const int total = tiles_m * tiles_n;
+  SkPlan plan{total, 0, (int)(K / kStepCols), 0};
+  if (sk_ws) {
+    const int P = std::min(device_cus(), kSkMaxGroups);
+    const int R = total % P;
+    // Pieces per remaining tile: fill the compute units, at least two
+    // steps a piece.
+    const int f = R > 0 ? std::min(P / R, plan.steps / 2) : 0;
+    if (f >= 2) {
+      plan.tiles_dp = total - R;
+      plan.tiles_sk = R;
+      plan.pieces = f;
+    }
+  }
+  const int grid = plan.tiles_dp + plan.tiles_sk * plan.pieces;
   if (acc_out)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, true>), dim3(total), dim3(T::kThreads),
-                       0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y,
-                       relu2 ? 1 : 0, acc_out, tiles_n, total);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, true>), dim3(grid), dim3(T::kThreads), 0,
+                       s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y, relu2 ? 1 : 0,
+                       acc_out, tiles_n, plan, sk_ws);
   else
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, false>), dim3(total),
-                       dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed,
-                       gamma, Y, relu2 ? 1 : 0, acc_out, tiles_n, total);
+    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, false>), dim3(grid), dim3(T::kThreads),
+                       0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma, Y,
+                       relu2 ? 1 : 0, acc_out, tiles_n, plan, sk_ws);
   return hipGetLastError();
 }
 
@@ -399,10 +620,17 @@ hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, const int*
   return hipGetLastError();
 }
 
+size_t bl_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  (void)M, (void)K, (void)N;
+  return (size_t)(kSkCounterInts + (size_t)kSkMaxGroups * kSkSlotInts) * sizeof(int);
+}
+
+size_t bl_gemm_counter_bytes() { return kSkCounterInts * sizeof(int); }
+
 hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                             const float* gamma, float* Y, bool relu2, int32_t* acc_out,
-                            hipStream_t s) {
+                            void* gemm_ws, hipStream_t s) {
   return launch_cfg<2, 2, 2, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
-                                   acc_out, s);
+                                   acc_out, static_cast<int*>(gemm_ws), s);
 }
