@@ -54,7 +54,8 @@
  *     safe) results.
  *   - Shapes: N % 16 == 0 and K % 256 == 0 (the packed tile); M >= 0 and
  *     M == 0 is a no-op that returns BITLINEAR_OK; N, K >= 1 otherwise.
- *     K <= 8,388,608 (checked; |acc| <= 127*K then fits int32 with room).
+ *     K <= 8,388,608 (checked; |acc| <= 127*K then fits int32 with room)
+ *     and N <= 4,194,304 (checked).
  */
 #ifndef BITLINEAR_H
 #define BITLINEAR_H
@@ -200,9 +201,9 @@ typedef struct {
   const void* X;          /* [M][K] activations, device, 16-byte aligned */
   bitlinear_dtype dtype;  /* BITLINEAR_F32 or BITLINEAR_BF16 */
   bitlinear_epilogue epi; /* BITLINEAR_EPI_NONE or BITLINEAR_EPI_RELU2 */
-  int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 8388608; for
-                             M <= 16 also K <= 12288 and
-                             M * (max K + 16) + M * 2048 <= 160 KiB */
+  int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 8388608,
+                             N <= 4194304; for M <= 16 also K <= 12288
+                             and M * (max K + 16) + M * 2048 <= 160 KiB */
   const uint8_t* packed;  /* packed weights of this layer */
   const float* gamma;     /* gamma_c of this layer (device float) */
   float* Y;               /* [M][N] output; must not overlap any layer's input */

@@ -41,12 +41,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // (128 rows of K bytes, with bit 31 of an offset meaning "past the end")
 // must stay below 2^31: K <= 2^23.
 constexpr int64_t kMaxK = 8388608;
+// Largest N: 128 output rows of float32 stay addressable by one 32-bit buffer
+// range (the GEMM epilogue's branch-free stores).
+constexpr int64_t kMaxN = 4194304;
 
 bitlinear_status check_nk(int64_t N, int64_t K) {
   if (N < 1 || K < 1) return fail(BITLINEAR_ERR_SHAPE, "N=%lld K=%lld must be >= 1", (long long)N, (long long)K);
   if (N % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "N=%lld is not a multiple of 16", (long long)N);
   if (K % 256 != 0) return fail(BITLINEAR_ERR_SHAPE, "K=%lld is not a multiple of 256", (long long)K);
   if (K > kMaxK) return fail(BITLINEAR_ERR_SHAPE, "K=%lld exceeds %lld", (long long)K, (long long)kMaxK);
+  if (N > kMaxN) return fail(BITLINEAR_ERR_SHAPE, "N=%lld exceeds %lld", (long long)N, (long long)kMaxN);
   return BITLINEAR_OK;
 }
 

@@ -318,8 +318,15 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
 
   // D layout of a 32x32 int32 MFMA tile: lane holds column (lane % 32) and,
   // in register e, row 8*(e / 4) + 4*(lane / 32) + e % 4.  One store
-  // instruction (fixed e) writes two 128-byte row segments.  No load follows
-  // a store here, so the stores never wait for each other.
+  // instruction (fixed e) writes two 128-byte row segments.  Buffer stores
+  // over the tile's rows drop what falls outside Y without a branch (rows
+  // past M lie past the range; columns past N are moved past it): a branch
+  // per store made each one cost a few hundred cycles.  No load follows a
+  // store here, so the stores never wait for each other.
+  const uint32_t row_bytes = (uint32_t)N * 4u;
+  const uint32_t rows_here = (uint32_t)min(T::BM, M - m0);
+  const auto y_r = make_rsrc(Y + (int64_t)m0 * N, rows_here * row_bytes);
+  const auto a_r = make_rsrc(acc_out + (int64_t)m0 * N, DEBUG ? rows_here * row_bytes : 0u);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -331,21 +338,21 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
       const int rsv[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = m0 + r + q;
-        if (m >= M) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int64_t n = (int64_t)(nt0 * kTileRows) + (wn * TN + j) * 32 + r32;
-          if (n >= N) continue;
+          const int n = nt0 * kTileRows + (wn * TN + j) * 32 + r32;
+          const uint32_t off = n < N ? (uint32_t)(r + q) * row_bytes + (uint32_t)n * 4u
+                                     : 0x80000000u;
           const int v = acc[i][j][4 * g + q] - rsv[q];
-          Y[(int64_t)m * N + n] = rescale(v, sxv[q], gamma, relu2 != 0);
-          if constexpr (DEBUG) acc_out[(int64_t)m * N + n] = v;
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __float_as_uint(rescale(v, sxv[q], gamma, relu2 != 0)), y_r, (int)off, 0, 0);
+          if constexpr (DEBUG)
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, a_r, (int)off, 0, 0);
         }
       }
     }
   }
 }
-
 
 // One output tile, whole K: the K loop and the epilogue.
 template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
