@@ -42,7 +42,7 @@ MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
 # Sources of each measured kernel: a committed counter summary applies only
 # to the kernel version it was taken on (matched by their hash).
 GEMV_SOURCES = ["gemv.hip", "gemv_tile.hpp", "common.hpp"]
-GEMM_SOURCES = ["gemm.hip", "common.hpp"]
+GEMM_SOURCES = ["gemm.hip", "group.hpp", "common.hpp"]
 GROUP_SOURCES = ["group.hip", "group.hpp", "gemv_tile.hpp", "quant_row.hpp", "common.hpp"]
 
 
@@ -190,11 +190,22 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
     epi = "relu2" if (wk.chain_relu2 and dom is lins[0]) else None
     n = args.kernel_launches
     copies = len(dom.packed)
+    gemm = metric_kind == "tops" and dom.ws is not None
+    if gemm:
+        # The GEMM launch alone, from activations quantized beforehand (the
+        # forward's other launch, the per-token quantization, is not the
+        # contraction being measured).
+        Xq, sx, rs = bl.quantize_acts(dom.X)
+        qws = bl.forward_q_workspace(dom.M, dom.K, dom.N, dom.X.device)
 
     def dom_step(i):
         c = i % copies
-        bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
-                   workspace=dom.ws)
+        if gemm:
+            bl.forward_q(Xq, sx, rs, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi,
+                         out=dom.Y, workspace=qws)
+        else:
+            bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
+                       workspace=dom.ws)
 
     us = time_graph(torch, dom_step, n)
     if metric_kind == "tops":
@@ -212,7 +223,8 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
     roof["traffic"] = traffic_from_profile(src, key)
     roof["kernel"] = key
     roof["kernel_us"] = round(us, 3)
-    roof["launches_per_forward"] = 2 if dom.ws is not None else 1
+    roof["launches_timed"] = "gemm only (forward_q)" if gemm else (
+        "quantization + gemm" if dom.ws is not None else "one fused launch")
     log(f"dominant forward {key}: {us:.3f} us per call")
     return roof
 
@@ -368,10 +380,21 @@ def context_probes(torch):
                 best = (round(gbs, 1), round(us, 3), wg_per_cu)
         out[f"read_{label}"] = {"GBps": best[0], "us": best[1], "wg_per_cu": best[2]}
         del bufs
-    # int8 matrix cores, random operand bytes
+    # int8 matrix cores: random operand bytes, then operands shaped like the
+    # GEMM's (A: quantized N(0,1) activations, B: codes 0/1/2 with 35% zeros)
     src = torch.randint(-2**31, 2**31 - 1, (4096,), dtype=torch.int32, device="cuda")
-    for shape, label, macs in ((0, "mfma_i32_16x16x64_i8", 8 * 16 * 16 * 64),
-                               (1, "mfma_i32_32x32x32_i8", 4 * 32 * 32 * 32)):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    a_bytes = torch.clamp(torch.round(torch.randn(8192, device="cuda", generator=gen) * 28.0),
+                          -127, 127).to(torch.int8)
+    u = torch.rand(8192, device="cuda", generator=gen)
+    b_codes = torch.where(u < 0.35, 1, torch.where(u < 0.675, 0, 2)).to(torch.int8)
+    src_t = torch.cat([a_bytes, b_codes]).view(torch.int32).contiguous()
+    for shape, label, macs, operands in (
+            (0, "mfma_i32_16x16x64_i8", 8 * 16 * 16 * 64, src),
+            (1, "mfma_i32_32x32x32_i8", 4 * 32 * 32 * 32, src),
+            (1, "mfma_i32_32x32x32_i8_ternary_operands", 4 * 32 * 32 * 32, src_t)):
+        src = operands
         best = None
         for wg_per_cu in (1, 2, 4):
             grid, iters = wg_per_cu * cus, 2000
