@@ -137,6 +137,7 @@ struct bitlinear_group {
   int max_k;
   int threads;
   bool gemm;
+  int n_items;  // items over all layers (output tiles in the GEMM mode)
   GroupOp* ops;
   int* wg_begin;
   int8_t* xq;
@@ -377,8 +378,9 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   int G = per_cu * (cus > 0 ? cus : 1);
   if (G > kGroupMaxWG) G = kGroupMaxWG;
 
-  // Cost-balanced contiguous item ranges: workgroup g starts at the first
-  // item whose preceding cost reaches g/G of the total.
+  // Cost-balanced contiguous item ranges for the skinny kernel: workgroup g
+  // starts at the first item whose preceding cost reaches g/G of the total.
+  // (The GEMM mode takes items strided instead.)
   std::vector<int> wg_begin((size_t)G + 1);
   {
     int g = 0;
@@ -407,6 +409,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->max_k = max_k;
   g->threads = threads;
   g->gemm = !skinny;
+  g->n_items = (int)item;
   g->ops = reinterpret_cast<GroupOp*>(base + L.table);
   g->wg_begin = reinterpret_cast<int*>(base + L.wg_begin);
   g->xq = reinterpret_cast<int8_t*>(base + L.xq);
@@ -422,7 +425,7 @@ bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = bl_launch_group_quant(g->ops, g->n_ops, g->M, g->xq, g->sx, g->rs, s);
     if (e == hipSuccess)
-      e = bl_launch_group_gemm(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->xq, g->sx, g->rs, s);
+      e = bl_launch_group_gemm(g->ops, g->n_ops, g->M, g->n_items, g->G, g->xq, g->sx, g->rs, s);
     return from_hip(e, "bitlinear_group_forward");
   }
   return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k,

@@ -522,23 +522,27 @@ __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
                                             tn);
 }
 
-// Many layers (a whole step): a persistent grid; workgroup g takes output
-// tiles wg_begin[g] .. wg_begin[g+1]-1 of the concatenation of every layer's
-// tiles (each layer row-major over its tm x tn tiles, starting at its
-// item_begin), from activations quantized beforehand into xq / sx / rs.
+// Many layers (a whole step): a persistent grid over the concatenation of
+// every layer's output tiles (each layer row-major over its tm x tn tiles
+// with tm fastest, starting at its item_begin), from activations quantized
+// beforehand into xq / sx / rs.  Workgroup v takes items v, v + G, v + 2G,
+// ...: at any time the grid works on a window of G consecutive items, so
+// the tiles in flight share activation row blocks and weight tiles.  Each
+// XCD takes a contiguous block of the window (consecutive workgroup ids go
+// to different XCDs), so what they share stays in one L2.  Every layer's
+// items spread evenly over the workgroups, which balances the cost.
 template <int WM, int WN, int TM, int TN, int S>
 __global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
-    const GroupOp* __restrict__ ops, int n_ops, int M, const int* __restrict__ wg_begin,
+    const GroupOp* __restrict__ ops, int n_ops, int M, int n_items,
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int* __restrict__ rs) {
   using T = Tile<WM, WN, TM, TN, S>;
   __shared__ __align__(1024) int8_t ring[S * T::kStageBytes];
-  int item = wg_begin[blockIdx.x];
-  const int end = wg_begin[blockIdx.x + 1];
-  int op = 0;
-  while (op + 1 < n_ops && ops[op + 1].item_begin <= item) ++op;
+  const int b = blockIdx.x, G = gridDim.x;
+  const int v = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
   const int tiles_m = (M + T::BM - 1) / T::BM;
+  int op = 0;
   bool first = true;
-  for (; item < end; ++item) {
+  for (int item = v; item < n_items; item += G) {
     while (op + 1 < n_ops && ops[op + 1].item_begin <= item) ++op;
     const GroupOp o = ops[op];
     const int local = item - o.item_begin;
@@ -619,11 +623,11 @@ int bl_group_gemm_blocks_per_cu() {
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
-hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
+hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
                                 const int8_t* xq, const float* sx, const int* rs,
                                 hipStream_t s) {
   hipLaunchKernelGGL((group_gemm_kernel<2, 2, 2, 2, 2>), dim3(G), dim3(GroupCfg::kThreads), 0,
-                     s, ops, n_ops, M, wg_begin, xq, sx, rs);
+                     s, ops, n_ops, M, n_items, xq, sx, rs);
   return hipGetLastError();
 }
 
