@@ -372,7 +372,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     e = bl_group_plan((int)M, max_k, &threads, &per_cu);
     if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   } else {
-    per_cu = bl_group_gemm_blocks_per_cu();
+    per_cu = bl_group_gemm_blocks_per_cu((int)M);
   }
   if (per_cu > 4) per_cu = 4;
   int G = per_cu * (cus > 0 ? cus : 1);

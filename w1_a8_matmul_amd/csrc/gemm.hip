@@ -413,7 +413,7 @@ __device__ __forceinline__ bool sk_contribute(int8_t* ring, v16i (&acc)[TM][TN],
                                               const SkPlan& p, int* __restrict__ sk_ws,
                                               int t, int g) {
   using T = Tile<WM, WN, TM, TN, S>;
-  static_assert(T::BM * T::BN == kSkSlotInts, "slot holds one tile");
+  static_assert(T::BM * T::BN <= kSkSlotInts, "slot holds one tile");
   constexpr int kChunks = TM * TN * 4;  // 16-byte stores per thread
   constexpr int kHalf = kChunks / 2;
   static_assert(T::kWaves * kHalf * 1024 + 64 <= S * T::kStageBytes, "ring holds the halves");
@@ -606,28 +606,37 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 
 // Tile choice, measured on MI355X over the prefill shapes (M = 512, 2048;
 // K = 2560..6912; N = 2560..22016): 128x128 workgroup tiles (4 waves of
-// 64x64) with a two-stage ring and three waves per SIMD beat 128x256 tiles
-// (fewer workgroups than slots at N = 2560) and three-stage rings (LDS-
-// limited occupancy).
-using GroupCfg = Tile<2, 2, 2, 2, 2>;
+// 64x64) with a two-stage ring and four waves per SIMD beat 128x256 tiles
+// (fewer workgroups than slots at N = 2560), 64x128 and 64x256 tiles, and
+// deeper rings with shorter steps.  Up to 64 tokens, 64x128 tiles (4 waves
+// of 32x64) avoid multiplying 64 empty rows.
+using BigCfg = Tile<2, 2, 2, 2, 2>;
+using SmallCfg = Tile<2, 2, 1, 2, 2>;
+constexpr int kSmallM = 64;
 
 int bl_group_gemm_tiles(int M, int N) {
-  return ((M + GroupCfg::BM - 1) / GroupCfg::BM) * ((N + GroupCfg::BN - 1) / GroupCfg::BN);
+  const int bm = M <= kSmallM ? SmallCfg::BM : BigCfg::BM;
+  return ((M + bm - 1) / bm) * ((N + BigCfg::BN - 1) / BigCfg::BN);
 }
 
-int bl_group_gemm_blocks_per_cu() {
+int bl_group_gemm_blocks_per_cu(int M) {
   int blocks = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks, reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 2, 2>),
-      GroupCfg::kThreads, 0);
+  const void* k = M <= kSmallM
+                      ? reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 1, 2, 2>)
+                      : reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 2, 2>);
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 256, 0);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
                                 const int8_t* xq, const float* sx, const int* rs,
                                 hipStream_t s) {
-  hipLaunchKernelGGL((group_gemm_kernel<2, 2, 2, 2, 2>), dim3(G), dim3(GroupCfg::kThreads), 0,
-                     s, ops, n_ops, M, n_items, xq, sx, rs);
+  if (M <= kSmallM)
+    hipLaunchKernelGGL((group_gemm_kernel<2, 2, 1, 2, 2>), dim3(G), dim3(SmallCfg::kThreads), 0,
+                       s, ops, n_ops, M, n_items, xq, sx, rs);
+  else
+    hipLaunchKernelGGL((group_gemm_kernel<2, 2, 2, 2, 2>), dim3(G), dim3(BigCfg::kThreads), 0,
+                       s, ops, n_ops, M, n_items, xq, sx, rs);
   return hipGetLastError();
 }
 
@@ -642,6 +651,9 @@ hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
                             const float* gamma, float* Y, bool relu2, int32_t* acc_out,
                             void* gemm_ws, hipStream_t s) {
+  if (M <= kSmallM)
+    return launch_cfg<2, 2, 1, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
+                                     acc_out, static_cast<int*>(gemm_ws), s);
   return launch_cfg<2, 2, 2, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
                                    acc_out, static_cast<int*>(gemm_ws), s);
 }

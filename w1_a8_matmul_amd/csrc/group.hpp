@@ -52,7 +52,7 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
 // the output tiles of all its layers (activations quantized beforehand).
 // Output tiles of one layer at M tokens; workgroups per compute unit.
 int bl_group_gemm_tiles(int M, int N);
-int bl_group_gemm_blocks_per_cu();
+int bl_group_gemm_blocks_per_cu(int M);
 // n_items: output tiles over all layers; G workgroups take them strided.
 hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
                                 const int8_t* xq, const float* sx, const int* rs,
