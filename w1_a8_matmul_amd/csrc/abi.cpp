@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include <new>
+#include <algorithm>
 #include <vector>
 
 #include "../../include/bitlinear.h"
@@ -66,12 +67,50 @@ size_t forward_workspace(int64_t M, int64_t K, int64_t N) {
   return q_workspace(M, K) + align256(bl_gemm_workspace_bytes(M, K, N));
 }
 
-// Grouped forward: device workspace layout (layer table, tile schedule).
+// Grouped forward: device workspace layout (layer table, work units and
+// their queue for the skinny kernel, quantized activations).
 constexpr int kGroupMaxWG = 2048;
 
 struct GroupLayout {
-  size_t table, wg_begin, xq, sx, rs, total;
+  size_t table, wg_begin, units, queue, xq, sx, rs, total;
+  int64_t split;    // first tile of the shared (queued) part
+  int64_t n_units;  // units of the shared part
 };
+
+// The skinny kernel's split of the tiles (in layer order, a tile costing
+// K/256 blocks) into the static part -- the first kGroupStaticPercent* of
+// the cost -- and the shared part, cut into runs of kGroupUnitTiles tiles of
+// one layer.  Calls f(op, first, end) for each unit.
+template <typename F>
+void group_split(const bitlinear_group_op* ops, int n_ops, int64_t M, int64_t* split,
+                 int64_t* n_units, F f) {
+  const int64_t pct = bl_group_prequantizes((int)M) ? kGroupStaticPercentPreq
+                                                    : kGroupStaticPercentInline;
+  int64_t total = 0;
+  for (int i = 0; i < n_ops; ++i) total += (ops[i].N / 16) * (ops[i].K / 256);
+  int64_t cost = 0, item = 0, s = -1, n = 0;
+  for (int i = 0; i < n_ops; ++i) {
+    const int64_t tiles = ops[i].N / 16, kb = ops[i].K / 256;
+    int64_t t = 0;
+    if (s < 0) {
+      // tiles of this layer still inside the static part
+      while (t < tiles && (cost + kb) * 100 <= total * pct) {
+        cost += kb;
+        ++t;
+      }
+      if (t == tiles) {
+        item += tiles;
+        continue;
+      }
+      s = item + t;
+    }
+    for (; t < tiles; t += kGroupUnitTiles, ++n)
+      f(i, item + t, item + std::min(t + kGroupUnitTiles, tiles));
+    item += tiles;
+  }
+  *split = s < 0 ? item : s;
+  *n_units = n;
+}
 
 // The quantized activations, scales and row sums exist only for token
 // counts whose activations are quantized by a launch of their own.
@@ -82,6 +121,14 @@ GroupLayout group_layout(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   off += align256((size_t)n_ops * sizeof(GroupOp));
   L.wg_begin = off;
   off += align256((size_t)(kGroupMaxWG + 1) * sizeof(int));
+  L.split = 0;
+  L.n_units = 0;
+  if (M <= kGroupMaxM)
+    group_split(ops, n_ops, M, &L.split, &L.n_units, [](int, int64_t, int64_t) {});
+  L.units = off;
+  off += align256((size_t)L.n_units * sizeof(GroupUnit));
+  L.queue = off;
+  off += 256;
   L.xq = L.sx = L.rs = off;
   if (bl_group_prequantizes((int)M)) {
     for (int i = 0; i < n_ops; ++i) off += align256((size_t)M * (size_t)ops[i].K);
@@ -138,8 +185,11 @@ struct bitlinear_group {
   int threads;
   bool gemm;
   int n_items;  // items over all layers (output tiles in the GEMM mode)
+  int n_units;  // shared work units of the skinny kernel
   GroupOp* ops;
   int* wg_begin;
+  GroupUnit* units;
+  int* queue;
   int8_t* xq;
   float* sx;
   int* rs;
@@ -340,7 +390,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   std::vector<GroupOp> table((size_t)n_ops);
-  int64_t item = 0, total_blocks = 0, xq_off = 0;
+  int64_t item = 0, xq_off = 0;
   int max_k = 0;
   for (int i = 0; i < n_ops; ++i) {
     const bitlinear_group_op& o = ops[i];
@@ -361,12 +411,11 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     // either way an item's cost is proportional to K.
     const int64_t items = skinny ? o.N / 16 : bl_group_gemm_tiles((int)M, (int)o.N);
     item += items;
-    total_blocks += items * (o.K / 256);
     if (o.K > max_k) max_k = (int)o.K;
   }
   // As many workgroups as fit on the chip at once, at most four per compute
-  // unit (skinny: each holds one layer's int8 activations in LDS; the
-  // weights are split into that many contiguous streams).
+  // unit (skinny: each holds one layer's int8 activations in LDS and takes
+  // work units from the queue; GEMM: output tiles strided).
   int threads = 256, per_cu = 1;
   if (skinny) {
     e = bl_group_plan((int)M, max_k, &threads, &per_cu);
@@ -378,28 +427,48 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   int G = per_cu * (cus > 0 ? cus : 1);
   if (G > kGroupMaxWG) G = kGroupMaxWG;
 
-  // Cost-balanced contiguous item ranges for the skinny kernel: workgroup g
-  // starts at the first item whose preceding cost reaches g/G of the total.
-  // (The GEMM mode takes items strided instead.)
-  std::vector<int> wg_begin((size_t)G + 1);
-  {
-    int g = 0;
-    int64_t before = 0, it = 0;
-    for (int i = 0; i < n_ops && g <= G; ++i) {
-      const int64_t items = skinny ? ops[i].N / 16 : bl_group_gemm_tiles((int)M, (int)ops[i].N);
-      const int64_t kblocks = ops[i].K / 256;
-      for (int64_t t = 0; t < items; ++t, ++it) {
-        while (g <= G && before * G >= (int64_t)g * total_blocks) wg_begin[(size_t)g++] = (int)it;
-        before += kblocks;
+  // Skinny kernel: cost-balanced contiguous static ranges over the tiles
+  // before the split (workgroup g starts at the first tile whose preceding
+  // cost reaches g/G of the static cost), then the shared units.  (The GEMM
+  // mode takes output tiles strided instead.)
+  std::vector<int> wg_begin((size_t)G + 1, 0);
+  std::vector<GroupUnit> units;
+  if (skinny) {
+    int64_t split = 0, n_units = 0;
+    group_split(ops, n_ops, M, &split, &n_units, [&](int op, int64_t first, int64_t end) {
+      units.push_back(GroupUnit{(int32_t)first, (int32_t)end, op, 0});
+    });
+    int64_t static_cost = 0;
+    {
+      int64_t it = 0;
+      for (int i = 0; i < n_ops && it < split; ++i) {
+        const int64_t tiles = std::min<int64_t>(ops[i].N / 16, split - it);
+        static_cost += tiles * (ops[i].K / 256);
+        it += tiles;
       }
     }
-    while (g <= G) wg_begin[(size_t)g++] = (int)item;
+    int g = 0;
+    int64_t before = 0, it = 0;
+    for (int i = 0; i < n_ops && it < split; ++i) {
+      const int64_t kb = ops[i].K / 256;
+      const int64_t tiles = ops[i].N / 16;
+      for (int64_t t = 0; t < tiles && it < split; ++t, ++it) {
+        while (g <= G && before * G >= (int64_t)g * static_cost) wg_begin[(size_t)g++] = (int)it;
+        before += kb;
+      }
+    }
+    while (g <= G) wg_begin[(size_t)g++] = (int)split;
   }
   char* base = static_cast<char*>(ws);
   e = hipMemcpy(base + L.table, table.data(), table.size() * sizeof(GroupOp), hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(base + L.wg_begin, wg_begin.data(), wg_begin.size() * sizeof(int),
                   hipMemcpyHostToDevice);
+  if (e == hipSuccess && !units.empty())
+    e = hipMemcpy(base + L.units, units.data(), units.size() * sizeof(GroupUnit),
+                  hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(base + L.queue, 0, 256);  // the kernel leaves it zero
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   bitlinear_group* g = new (std::nothrow) bitlinear_group;
   if (!g) return fail(BITLINEAR_ERR_ARG, "out of host memory");
@@ -410,8 +479,11 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->threads = threads;
   g->gemm = !skinny;
   g->n_items = (int)item;
+  g->n_units = (int)L.n_units;
   g->ops = reinterpret_cast<GroupOp*>(base + L.table);
   g->wg_begin = reinterpret_cast<int*>(base + L.wg_begin);
+  g->units = reinterpret_cast<GroupUnit*>(base + L.units);
+  g->queue = reinterpret_cast<int*>(base + L.queue);
   g->xq = reinterpret_cast<int8_t*>(base + L.xq);
   g->sx = reinterpret_cast<float*>(base + L.sx);
   g->rs = reinterpret_cast<int*>(base + L.rs);
@@ -428,8 +500,8 @@ bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream)
       e = bl_launch_group_gemm(g->ops, g->n_ops, g->M, g->n_items, g->G, g->xq, g->sx, g->rs, s);
     return from_hip(e, "bitlinear_group_forward");
   }
-  return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->G, g->max_k,
-                                  g->threads, g->xq, g->sx, g->rs,
+  return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->units, g->n_units,
+                                  g->queue, g->G, g->max_k, g->threads, g->xq, g->sx, g->rs,
                                   static_cast<hipStream_t>(stream)),
                   "bitlinear_group_forward");
 }

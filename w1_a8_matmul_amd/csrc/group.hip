@@ -205,53 +205,25 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   }
 }
 
-// Tiles item .. end-1 of the layers op_at(0..n_ops-1), in segments of at
-// most kSegTiles tiles of one layer; the activations are quantized (or
-// copied) when a segment starts a new layer.
-template <int NT, int KCH, bool PREQ, typename OpAt>
-__device__ __forceinline__ void run_range(OpAt op_at, int n_ops, int M, int max_k, int item,
-                                          int end, const int8_t* __restrict__ xq,
-                                          const float* __restrict__ sx,
-                                          const int* __restrict__ rs, int8_t* dyn, float* s_sx,
-                                          int* s_rs, Smem<NT>& sm) {
-  // Dynamic LDS: int8 activations [M][max_k + 16] of the current layer (rows
-  // padded by 16 bytes so that the 16 token rows of an A-operand read fall in
-  // distinct banks), then the segment's outputs [M][kSegTiles][16] floats.
-  const int xstride = max_k + 16;
-  int8_t* xs = dyn;
-  float* s_y = reinterpret_cast<float*>(dyn + (size_t)M * xstride);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int op = 0;
-  while (op + 1 < n_ops && op_at(op + 1).item_begin <= item) ++op;
-
-  int quantized_op = -1;
-  while (item < end) {
-    const GroupOp o = op_at(op);
-    const int op_end = o.item_begin + o.N / kTileRows;
-    const int seg_end = min(min(end, op_end), item + kSegTiles);
-    const bool quantize = quantized_op != op;
-    if (PREQ)
-      run_segment<NT, KCH, 0, true>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y,
-                                    sm, xq, sx, rs, op, wave, lane);
-    else if (o.dtype == 1)
-      run_segment<NT, KCH, 1, false>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y,
-                                     sm, xq, sx, rs, op, wave, lane);
-    else
-      run_segment<NT, KCH, 0, false>(o, M, item, seg_end, quantize, xs, xstride, s_sx, s_rs, s_y,
-                                     sm, xq, sx, rs, op, wave, lane);
-    __syncthreads();  // before the next segment overwrites xs, the scales or s_y
-    quantized_op = op;
-    item = seg_end;
-    if (item == op_end) ++op;
-  }
-}
-
-// Many layers: the table in device memory, tile ranges planned on the host.
+// Many layers.  Work is in two parts.  First a static, cost-balanced
+// contiguous range of 16-row tiles per workgroup (wg_begin[g] ..
+// wg_begin[g+1]-1), run in segments of at most kSegTiles tiles of one layer.
+// Then units of up to kGroupUnitTiles tiles of one layer (the rest of the
+// tiles, in layer order) taken from a queue as workgroups become free.  The
+// workgroups of a compute unit do not stream at the same rate (the oldest
+// wave wins arbitration), so static shares alone leave a long tail with few
+// workgroups streaming; the queue keeps them all busy to the end, and the
+// static part keeps the per-unit set-up (quantizing a new layer's
+// activations) off most of the work.  queue[0] is the next unit, queue[1]
+// counts the workgroups that found the queue empty; the last of them puts
+// both back to zero for the next launch.  A layer's int8 activations are
+// quantized (or copied) whenever a workgroup moves to a new layer.
 template <int NT, int KCH, bool PREQ>
 __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops, int n_ops,
                                                    int M, int max_k,
                                                    const int* __restrict__ wg_begin,
+                                                   const GroupUnit* __restrict__ units,
+                                                   int n_units, int* __restrict__ queue,
                                                    const int8_t* __restrict__ xq,
                                                    const float* __restrict__ sx,
                                                    const int* __restrict__ rs) {
@@ -259,9 +231,62 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
   __shared__ float s_sx[kGroupMaxM];
   __shared__ int s_rs[kGroupMaxM];
   __shared__ Smem<NT> sm;
-  run_range<NT, KCH, PREQ>([=](int i) { return ops[i]; }, n_ops, M, max_k,
-                           wg_begin[blockIdx.x], wg_begin[blockIdx.x + 1], xq, sx, rs, dyn, s_sx,
-                           s_rs, sm);
+  __shared__ int s_unit;
+  // Dynamic LDS: int8 activations [M][max_k + 16] of the current layer (rows
+  // padded by 16 bytes so that the 16 token rows of an A-operand read fall in
+  // distinct banks), then a segment's outputs [M][kSegTiles][16] floats.
+  const int xstride = max_k + 16;
+  int8_t* xs = dyn;
+  float* s_y = reinterpret_cast<float*>(dyn + (size_t)M * xstride);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int quantized_op = -1;
+  // Tiles first .. end-1 of layer op (end - first <= kSegTiles).
+  auto segment = [&](int op, int first, int end) {
+    const GroupOp o = ops[op];
+    const bool quantize = quantized_op != op;
+    if (PREQ)
+      run_segment<NT, KCH, 0, true>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+                                    sm, xq, sx, rs, op, wave, lane);
+    else if (o.dtype == 1)
+      run_segment<NT, KCH, 1, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+                                     sm, xq, sx, rs, op, wave, lane);
+    else
+      run_segment<NT, KCH, 0, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+                                     sm, xq, sx, rs, op, wave, lane);
+    __syncthreads();  // before the next segment overwrites xs, the scales, s_y or s_unit
+    quantized_op = op;
+  };
+
+  // Static part.
+  int item = wg_begin[blockIdx.x];
+  const int end = wg_begin[blockIdx.x + 1];
+  int op = 0;
+  while (op + 1 < n_ops && ops[op + 1].item_begin <= item) ++op;
+  while (item < end) {
+    const int op_end = ops[op].item_begin + ops[op].N / kTileRows;
+    const int seg_end = min(min(end, op_end), item + kSegTiles);
+    segment(op, item, seg_end);
+    item = seg_end;
+    if (item == op_end) ++op;
+  }
+  // Shared part.
+  for (;;) {
+    if (threadIdx.x == 0)
+      s_unit = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int u = s_unit;
+    if (u >= n_units) break;
+    const GroupUnit un = units[u];
+    segment(un.op, un.first, un.end);
+  }
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          (int)gridDim.x - 1) {
+    // Every workgroup is past its last take from the queue.
+    __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Per-token quantization of every layer's activations (one workgroup per
@@ -304,17 +329,18 @@ const void* kernel_for(int threads, bool preq, int max_k) {
 }
 
 template <int NT, bool PREQ>
-void launch(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G, int max_k,
-            size_t lds, const int8_t* xq, const float* sx, const int* rs, hipStream_t s) {
+void launch(const GroupOp* ops, int n_ops, int M, const int* wg_begin, const GroupUnit* units,
+            int n_units, int* queue, int G, int max_k, size_t lds, const int8_t* xq,
+            const float* sx, const int* rs, hipStream_t s) {
   if (max_k <= NT * 8 * 2)
     hipLaunchKernelGGL((group_kernel<NT, 2, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
-                       max_k, wg_begin, xq, sx, rs);
+                       max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else if (max_k <= NT * 8 * 4)
     hipLaunchKernelGGL((group_kernel<NT, 4, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
-                       max_k, wg_begin, xq, sx, rs);
+                       max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else
     hipLaunchKernelGGL((group_kernel<NT, 6, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
-                       max_k, wg_begin, xq, sx, rs);
+                       max_k, wg_begin, units, n_units, queue, xq, sx, rs);
 }
 
 int blocks_per_cu(int threads, bool preq, size_t lds, int max_k) {
@@ -363,9 +389,9 @@ hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu) {
   return hipSuccess;
 }
 
-hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
-                           int max_k, int threads, int8_t* xq, float* sx, int* rs,
-                           hipStream_t s) {
+hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin,
+                           const GroupUnit* units, int n_units, int* queue, int G, int max_k,
+                           int threads, int8_t* xq, float* sx, int* rs, hipStream_t s) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
   const bool preq = bl_group_prequantizes(M);
   if (preq) {
@@ -373,10 +399,14 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
     if (e != hipSuccess) return e;
   }
   if (threads == 512)
-    preq ? launch<512, true>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s)
-         : launch<512, false>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s);
+    preq ? launch<512, true>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                             sx, rs, s)
+         : launch<512, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                              sx, rs, s);
   else
-    preq ? launch<256, true>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s)
-         : launch<256, false>(ops, n_ops, M, wg_begin, G, max_k, lds, xq, sx, rs, s);
+    preq ? launch<256, true>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                             sx, rs, s)
+         : launch<256, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                              sx, rs, s);
   return hipGetLastError();
 }

@@ -18,6 +18,19 @@ struct GroupOp {
 };
 static_assert(sizeof(GroupOp) == 64, "GroupOp must stay 64 bytes");
 
+// A unit of grouped work: tiles first..end-1 (indices into the concatenation
+// of every layer's 16-row tiles) of layer op.
+struct GroupUnit {
+  int32_t first, end, op, pad;
+};
+constexpr int kGroupUnitTiles = 8;
+// Share of the work (by bytes) in the static ranges, in percent, when the
+// workgroups quantize activations themselves (a new layer costs a
+// quantization) and when they copy pre-quantized rows (a new layer costs a
+// copy of M rows); measured on MI355X over 2B and 7B decode steps.
+constexpr int kGroupStaticPercentInline = 75;
+constexpr int kGroupStaticPercentPreq = 95;
+
 // Largest K of a grouped layer and largest token count.  Up to
 // kGroupInlineQuantMaxM tokens each workgroup quantizes the activations of
 // the layer it starts on itself (one launch); above, a separate launch
@@ -40,13 +53,14 @@ size_t bl_group_lds_bytes(int M, int max_k);
 // LDS it needs.
 hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu);
 
-// Grouped forward.  wg_begin[g]..wg_begin[g+1] is workgroup g's tile range;
-// G workgroups of `threads` threads; max_k the largest K.  xq, sx, rs: the
-// quantized activations, scales and row sums (used when
+// Grouped forward: G workgroups of `threads` threads; workgroup g first runs
+// tiles wg_begin[g] .. wg_begin[g+1]-1, then takes the n_units units from the
+// queue (two ints, zero on entry and left zero); max_k the largest K.  xq,
+// sx, rs: the quantized activations, scales and row sums (used when
 // bl_group_prequantizes(M)).
-hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin, int G,
-                           int max_k, int threads, int8_t* xq, float* sx, int* rs,
-                           hipStream_t s);
+hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin,
+                           const GroupUnit* units, int n_units, int* queue, int G, int max_k,
+                           int threads, int8_t* xq, float* sx, int* rs, hipStream_t s);
 
 // Above kGroupMaxM tokens a group runs as one persistent tiled int8 GEMM over
 // the output tiles of all its layers (activations quantized beforehand).
