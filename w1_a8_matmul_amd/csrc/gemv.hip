@@ -26,11 +26,16 @@ constexpr int kNT = 256;
 constexpr int kMaxLoadsPerLane = 12;
 
 // Codes are q+1 in {0,1,2}: sum_k code*x - sum_k x = sum_k q*x exactly.
-// 256 threads (4 waves) per 16-row tile; L = weight loads per lane
-// (K <= L*1024) and KCH = (L+1)/2 eight-element activation chunks per
-// thread per row (K <= KCH*2048).  The debug outputs are written only when
-// their pointers are set.
-template <int M, int DT, int L>
+// 256 threads (4 waves) per TPW 16-row tiles (tiles TPW*g .. TPW*g+TPW-1;
+// a tile past the last reads zeros and stores nothing); L = weight loads
+// per lane and tile (K <= L*1024) and KCH = (L+1)/2 eight-element
+// activation chunks per thread per row (K <= KCH*2048).  The debug outputs
+// are written only when their pointers are set.  The library launches one
+// tile per workgroup: measured on MI355X, two or four tiles per workgroup
+// (fewer workgroups, less repeated quantization) and eight-wave workgroups
+// were slower on both decode projections, and this form of the kernel was
+// faster than one written for a single tile (3.2 vs 3.5 us for 2560->6912).
+template <int M, int DT, int L, int TPW>
 __global__ __launch_bounds__(kNT) void gemv_kernel(
     const void* __restrict__ X, int K, int64_t N, const uint8_t* __restrict__ packed,
     const float* __restrict__ gamma_p, float* __restrict__ Y, int relu2,
@@ -44,19 +49,22 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(
   __shared__ int red_i[W];
   __shared__ float s_scale[M];
   __shared__ int s_rowsum[M];
-  __shared__ int partial[M][W][kWave];
-
+  __shared__ int partial[TPW][M][W][kWave];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t tile_row = blockIdx.x;
+  const int64_t ntiles = N / kTileRows;
   const int kblocks = K / kTileCols;
-
   // 1) activation rows 0..P-1, then 2) every weight load of this lane.
   Chunk<DT> pre[P > 0 ? P : 1][KCH];
 #pragma unroll
   for (int m = 0; m < P; ++m) load_row<DT, kNT, KCH>(X, m, K, pre[m]);
-  uint4 wv[L];
-  load_tile_weights<W, L>(packed, tile_row, kblocks, wave, lane, wv);
+  uint4 wv[TPW][L];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int64_t tile = (int64_t)blockIdx.x * TPW + t;
+    load_tile_weights<W, L>(packed, tile < ntiles ? tile : 0, tile < ntiles ? kblocks : 0,
+                            wave, lane, wv[t]);
+  }
 
   // 3) per-token quantization into LDS while the weights arrive.
 #pragma unroll
@@ -72,16 +80,32 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(
   }
   __syncthreads();
 
-  // 4) unpack + v_dot4 over this lane's column blocks, 5) fold and rescale.
-  int part[M];
-  contract_tile<M, W, L>(wv, xs, K, kblocks, wave, lane, part);
-  int s;
-  if (fold_tile<M, W>(part, partial, wave, lane, &s)) {
-    const int m = tid / kTileRows, i = tid % kTileRows;
-    const int acc_true = s - s_rowsum[m];
-    const int64_t n = tile_row * kTileRows + i;
-    Y[m * N + n] = rescale(acc_true, s_scale[m], *gamma_p, relu2 != 0);
-    if (acc_out) acc_out[m * N + n] = acc_true;
+  // 4) unpack + v_dot4 over this lane's column blocks, 5) fold the lanes'
+  // partial sums of all waves through LDS (lanes l, l+16, l+32, l+48 hold
+  // tile row l%16) and rescale.
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    int part[M];
+    contract_tile<M, W, L>(wv[t], xs, K, kblocks, wave, lane, part);
+#pragma unroll
+    for (int m = 0; m < M; ++m) partial[t][m][wave][lane] = part[m];
+  }
+  __syncthreads();
+  if (tid < TPW * M * kTileRows) {
+    const int t = tid / (M * kTileRows), r = tid % (M * kTileRows);
+    const int m = r / kTileRows, i = r % kTileRows;
+    const int64_t tile = (int64_t)blockIdx.x * TPW + t;
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s += partial[t][m][w][q * 16 + i];
+    if (tile < ntiles) {
+      const int acc_true = s - s_rowsum[m];
+      const int64_t n = tile * kTileRows + i;
+      Y[m * N + n] = rescale(acc_true, s_scale[m], *gamma_p, relu2 != 0);
+      if (acc_out) acc_out[m * N + n] = acc_true;
+    }
   }
   if (blockIdx.x == 0) {
     if (xq_out)
@@ -95,7 +119,9 @@ hipError_t launch_one(const void* X, int64_t K, int64_t N, const uint8_t* packed
                       const float* gamma, float* Y, bool relu2, int8_t* xq, float* xs,
                       int32_t* acc, hipStream_t s) {
   const size_t lds = (size_t)M * (size_t)K;
-  hipLaunchKernelGGL((gemv_kernel<M, DT, L>), dim3((unsigned)(N / kTileRows)), dim3(kNT), lds,
+  constexpr int kTilesPerWorkgroup = 1;
+  hipLaunchKernelGGL((gemv_kernel<M, DT, L, kTilesPerWorkgroup>),
+                     dim3((unsigned)(N / kTileRows / kTilesPerWorkgroup)), dim3(kNT), lds,
                      s, X, (int)K, N, packed, gamma, Y, relu2 ? 1 : 0, xq, xs, acc);
   return hipGetLastError();
 }

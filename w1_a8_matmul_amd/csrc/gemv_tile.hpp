@@ -169,25 +169,4 @@ __device__ __forceinline__ void contract_tile(const uint4 (&wv)[L], const int8_t
   for (int m = 0; m < M; ++m) part[m] = a0[m] + (a1[m] >> 2) + (a2[m] >> 4);
 }
 
-// Folds the lanes' partial sums of all W waves through LDS (partial is
-// [M][W][64] ints).  Afterwards thread t < M*16 holds in *acc the exact
-// sum_k code*x of token t/16, row t%16 of the tile, and returns true.
-template <int M, int W>
-__device__ __forceinline__ bool fold_tile(const int (&part)[M], int (*partial)[W][kWave],
-                                          int wave, int lane, int* acc) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) partial[m][wave][lane] = part[m];
-  __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid >= M * kTileRows) return false;
-  const int m = tid / kTileRows, i = tid % kTileRows;
-  int s = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) s += partial[m][w][q * 16 + i];
-  *acc = s;
-  return true;
-}
-
 }  // namespace bl
