@@ -120,7 +120,7 @@ template <int WM, int WN, int TM, int TN, int S, bool LEVEL>
 __device__ __forceinline__ void tile_mainloop(int8_t* ring, const int8_t* __restrict__ Xq,
                                               int M, int K, int N,
                                               const uint8_t* __restrict__ packed, int tm,
-                                              int tn, int k0, int k1,
+                                              int tn, int k0, int k1, bool level,
                                               v16i (&acc)[TM][TN]) {
   using T = Tile<WM, WN, TM, TN, S>;
   constexpr int kStages = S;
@@ -262,9 +262,9 @@ __device__ __forceinline__ void tile_mainloop(int8_t* ring, const int8_t* __rest
   // wave steps its priority down 3 -> 0 over the quarters of its K range,
   // which keeps the resident workgroups level.
   const int nrounds = (k1 - k0 + kStages - 1) / kStages;
-  if constexpr (LEVEL) __builtin_amdgcn_s_setprio(3);
+  if constexpr (LEVEL) if (level) __builtin_amdgcn_s_setprio(3);
   for (int rd = 0; rd < nrounds; ++rd) {
-    if constexpr (LEVEL) {
+    if constexpr (LEVEL) if (level) {
       if (rd == nrounds / 4) __builtin_amdgcn_s_setprio(2);
       if (rd == nrounds / 2) __builtin_amdgcn_s_setprio(1);
       if (rd == 3 * nrounds / 4) __builtin_amdgcn_s_setprio(0);
@@ -378,7 +378,7 @@ __device__ __forceinline__ void gemm_tile(
   const float gamma = *gamma_p;
   v16i acc[TM][TN];
   tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, 0, K / kStepCols,
-                                          acc);
+                                          true, acc);
   tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, relu2, acc_out, tm,
                                           tn);
 }
@@ -530,7 +530,11 @@ __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
   const RowScale own = load_row_scale<WM, WN, TM, TN, S>(x_scale, x_rowsum, M, tm);
   const float gamma = *gamma_p;
   v16i acc[TM][TN];
-  tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, k0, k1, acc);
+  // Leveled launches run the pieces first (top priority), so the hand-over
+  // and epilogue of split tiles overlap the whole tiles' K loops.
+  if constexpr (LEVEL) if (split) __builtin_amdgcn_s_setprio(3);
+  tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, k0, k1, !split, acc);
+  if constexpr (LEVEL) __builtin_amdgcn_s_setprio(0);
   if (!split || sk_contribute<WM, WN, TM, TN, S>(ring, acc, plan, sk_ws, t, g))
     tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, relu2, acc_out, tm,
                                             tn);
@@ -621,13 +625,16 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
     }
   }
   const int grid = plan.tiles_dp + plan.tiles_sk * plan.pieces;
-  // Level the workgroups (priority steps) when the whole grid is resident
-  // at once and no tile is split: with rounds queued behind them, staggered
-  // finishes overlap one workgroup's epilogue with the next one's start, and
-  // with split pieces (short) oldest-first issue, whole tiles first, measured
-  // 3-5% faster (2048 x 2560 -> 6912).
-  const bool level =
-      plan.pieces == 0 && grid <= device_cus() * resident_per_cu<WM, WN, TM, TN, S>();
+  // Level the whole-tile workgroups (priority steps) when the whole grid is
+  // resident at once: with rounds queued behind them, staggered finishes
+  // overlap one workgroup's epilogue with the next one's start.  With split
+  // pieces, only when at least two whole tiles per CU remain once the
+  // pieces are done; with one (2048 x 6912 -> 2560: one tile and one piece
+  // per CU) that tile would finish alone, and oldest-first issue measured
+  // 8% faster.
+  const int cus = device_cus();
+  const bool level = grid <= cus * resident_per_cu<WM, WN, TM, TN, S>() &&
+                     (plan.pieces == 0 || plan.tiles_dp >= 2 * cus);
   if (acc_out)
     hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, true, false>), dim3(grid),
                        dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma,
