@@ -229,18 +229,27 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
     return roof
 
 
-def roofline_grouped(args, torch, step, bytes_step, wk, M, n_lin):
-    """The grouped forward of a whole step (one launch, quantization included)."""
+def roofline_grouped(args, torch, step, bytes_step, ops_step, wk, M, n_lin, metric_kind):
+    """The grouped forward of a whole step (quantization included).  Up to 16
+    tokens it streams the weights (HBM roof); above, it is one tiled int8 GEMM
+    over all linears, and from 128 tokens on (where the step's ops per weight
+    byte pass the chip's 625) the matrix cores bound it."""
     n = max(4, args.kernel_launches // 20)
     us = time_graph(torch, step, n)
-    achieved = bytes_step / (us * 1e-6) / 1e9
-    key = f"group_gemv_{wk.key}_m{M}"
-    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profile(
-                source_hash(GROUP_SOURCES), key),
-            "kernel": key, "kernel_us": round(us, 3),
-            "launches_per_forward": 1 if M <= 4 else 2}
+    if metric_kind == "tops":
+        achieved = ops_step / (us * 1e-6) / 1e12
+        key = f"group_gemm_{wk.key}_m{M}"
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+                "traffic": traffic_from_profile(source_hash(GEMM_SOURCES), key)}
+    else:
+        achieved = bytes_step / (us * 1e-6) / 1e9
+        key = f"group_gemv_{wk.key}_m{M}"
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(source_hash(GROUP_SOURCES), key)}
+    roof.update({"kernel": key, "kernel_us": round(us, 3),
+                 "launches_per_forward": 1 if M <= 4 else 2})
     log(f"grouped forward: {us:.3f} us per step ({n_lin} linears)")
     return roof
 
@@ -466,7 +475,8 @@ def main():
     log(f"timed {args.steps} steps: wall {wall*1e3:.3f} ms, events {gpu_ms:.3f} ms")
 
     if groups is not None:
-        roof = roofline_grouped(args, torch, step, bytes_step, wk, M, len(lins))
+        roof = roofline_grouped(args, torch, step, bytes_step, ops_step, wk, M, len(lins),
+                                metric_kind)
     else:
         roof = roofline_single(args, torch, bl, wk, M, lins, metric_kind)
 
