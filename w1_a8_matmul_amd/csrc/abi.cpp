@@ -79,8 +79,8 @@ struct GroupLayout {
 
 // The skinny kernel's split of the tiles (in layer order, a tile costing
 // K/256 blocks) into the static part -- the first kGroupStaticPercent* of
-// the cost -- and the shared part, cut into runs of kGroupUnitTiles tiles of
-// one layer.  Calls f(op, first, end) for each unit.
+// the cost -- and the shared part, cut into runs of about kGroupUnitBlocks
+// weight blocks of one layer.  Calls f(op, first, end) for each unit.
 template <typename F>
 void group_split(const bitlinear_group_op* ops, int n_ops, int64_t M, int64_t* split,
                  int64_t* n_units, F f) {
@@ -104,8 +104,9 @@ void group_split(const bitlinear_group_op* ops, int n_ops, int64_t M, int64_t* s
       }
       s = item + t;
     }
-    for (; t < tiles; t += kGroupUnitTiles, ++n)
-      f(i, item + t, item + std::min(t + kGroupUnitTiles, tiles));
+    const int64_t per_unit =
+        std::min<int64_t>(kGroupSegTiles, std::max<int64_t>(1, (kGroupUnitBlocks + kb / 2) / kb));
+    for (; t < tiles; t += per_unit, ++n) f(i, item + t, item + std::min(t + per_unit, tiles));
     item += tiles;
   }
   *split = s < 0 ? item : s;

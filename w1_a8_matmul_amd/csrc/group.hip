@@ -26,7 +26,7 @@ namespace {
 using namespace bl;
 
 constexpr int kChunk = 6;        // column blocks per streamed chunk
-constexpr int kSegTiles = 32;    // tiles whose outputs are held in LDS at once
+constexpr int kSegTiles = kGroupSegTiles;
 
 // One 1 KiB block of a 16-row tile on the matrix cores.  Lane l loaded
 // row l%16 of the tile, columns 64q .. 64q+63 of the block (q = l/16), as
@@ -101,7 +101,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
                              valid ? (uint32_t)kblocks * kTileBytes : 0u);
 #pragma unroll
     for (int i = 0; i < C; ++i)
-      buf[i] = buf_load16(r, lane * 16, (uint32_t)(q.c * C + i) * kTileBytes);
+      buf[i] = buf_load16_stream(r, lane * 16, (uint32_t)(q.c * C + i) * kTileBytes);
   };
 
   // Activation row 0 first, then the first weight chunk, then the
@@ -208,7 +208,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
 // Many layers.  Work is in two parts.  First a static, cost-balanced
 // contiguous range of 16-row tiles per workgroup (wg_begin[g] ..
 // wg_begin[g+1]-1), run in segments of at most kSegTiles tiles of one layer.
-// Then units of up to kGroupUnitTiles tiles of one layer (the rest of the
+// Then units of about kGroupUnitBlocks weight blocks of one layer (the rest of the
 // tiles, in layer order) taken from a queue as workgroups become free.  The
 // workgroups of a compute unit do not stream at the same rate (the oldest
 // wave wins arbitration), so static shares alone leave a long tail with few

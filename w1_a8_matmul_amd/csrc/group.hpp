@@ -23,7 +23,13 @@ static_assert(sizeof(GroupOp) == 64, "GroupOp must stay 64 bytes");
 struct GroupUnit {
   int32_t first, end, op, pad;
 };
-constexpr int kGroupUnitTiles = 8;
+// A unit holds about kGroupUnitBlocks 1 KiB weight blocks (16 rows x 256
+// columns each): 16 tiles at K = 2560, 6 at K = 6912, so that units cost
+// about the same whatever their layer (smaller units measured slower: each
+// costs a new layer's quantization and a pipeline restart).
+constexpr int kGroupUnitBlocks = 160;
+// Tiles whose outputs a workgroup holds in LDS at once (one segment).
+constexpr int kGroupSegTiles = 32;
 // Share of the work (by bytes) in the static ranges, in percent, when the
 // workgroups quantize activations themselves (a new layer costs a
 // quantization) and when they copy pre-quantized rows (a new layer costs a
