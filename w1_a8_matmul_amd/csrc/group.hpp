@@ -24,10 +24,11 @@ struct GroupUnit {
   int32_t first, end, op, pad;
 };
 // A unit holds about kGroupUnitBlocks 1 KiB weight blocks (16 rows x 256
-// columns each): 16 tiles at K = 2560, 6 at K = 6912, so that units cost
-// about the same whatever their layer (smaller units measured slower: each
-// costs a new layer's quantization and a pipeline restart).
-constexpr int kGroupUnitBlocks = 160;
+// columns each), at most one segment: 32 tiles at K = 2560, 12 at K = 6912,
+// 20 at K = 4096.  Measured on MI355X over 80..640: smaller units cost more
+// set-ups (a new layer's quantization, a pipeline restart), larger ones a
+// longer tail (2B step at M = 1: 93 us at 320, 98 at 160, 100 at 80).
+constexpr int kGroupUnitBlocks = 320;
 // Tiles whose outputs a workgroup holds in LDS at once (one segment).
 constexpr int kGroupSegTiles = 32;
 // Share of the work (by bytes) in the static ranges, in percent, when the
