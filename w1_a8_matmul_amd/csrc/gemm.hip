@@ -335,7 +335,9 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
   // over the tile's rows drop what falls outside Y without a branch (rows
   // past M lie past the range; columns past N are moved past it): a branch
   // per store made each one cost a few hundred cycles.  No load follows a
-  // store here, so the stores never wait for each other.
+  // store here, so the stores never wait for each other.  Y is written once
+  // and not read back here: its stores use the non-temporal policy (NT, 2),
+  // measured 1-7% faster over the prefill shapes.
   const uint32_t row_bytes = (uint32_t)N * 4u;
   const uint32_t rows_here = (uint32_t)min(T::BM, M - m0);
   const auto y_r = make_rsrc(Y + (int64_t)m0 * N, rows_here * row_bytes);
@@ -358,7 +360,7 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
                                      : 0x80000000u;
           const int v = acc[i][j][4 * g + q] - rsv[q];
           __builtin_amdgcn_raw_buffer_store_b32(
-              __float_as_uint(rescale(v, sxv[q], gamma, relu2 != 0)), y_r, (int)off, 0, 0);
+              __float_as_uint(rescale(v, sxv[q], gamma, relu2 != 0)), y_r, (int)off, 0, 2);
           if constexpr (DEBUG)
             __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, a_r, (int)off, 0, 0);
         }
