@@ -113,11 +113,28 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   if (PREQ) {
     issue(bufA, 0, qi);
     if (quantize) {
+      // The layer's int8 rows, in batches of kCopyBatch 16-byte pieces per
+      // thread: every load of a batch is issued before its LDS stores (loads
+      // past the rows read zero through the buffer range, no branch), so a
+      // batch costs one L2 round trip.  One piece per iteration made the
+      // copy wait for a round trip per piece: 27 at M = 16, K = 6912.
+      constexpr int kCopyBatch = 8;
       const int row16 = K / 16;  // 16-byte pieces per row
-      const uint4* src = reinterpret_cast<const uint4*>(xq + o.xq_off);
-      for (int i = threadIdx.x; i < M * row16; i += kThreads) {
-        const int m = i / row16, c = i - m * row16;
-        *reinterpret_cast<uint4*>(xs + m * xstride + c * 16) = src[i];
+      const int n16 = M * row16;
+      const auto xr = make_rsrc(xq + o.xq_off, (uint32_t)n16 * 16u);
+      for (int b0 = 0; b0 < n16; b0 += kCopyBatch * kThreads) {
+        uint4 v[kCopyBatch];
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u)
+          v[u] = buf_load16(xr, (uint32_t)(b0 + u * kThreads + (int)threadIdx.x) * 16u, 0);
+#pragma unroll
+        for (int u = 0; u < kCopyBatch; ++u) {
+          const int i = b0 + u * kThreads + (int)threadIdx.x;
+          if (i < n16) {
+            const int m = i / row16, c = i - m * row16;
+            *reinterpret_cast<uint4*>(xs + m * xstride + c * 16) = v[u];
+          }
+        }
       }
       if ((int)threadIdx.x < M) {
         s_sx[threadIdx.x] = sx[op * M + threadIdx.x];
