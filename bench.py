@@ -375,7 +375,7 @@ def context_probes(torch):
                                   ("gemv_4.4MB", 4423680, 61)):
         bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
         best = None
-        for wg_per_cu in (2, 4, 8):
+        for wg_per_cu in (2, 3, 4, 8):
             grid = wg_per_cu * cus
 
             def fn(i):

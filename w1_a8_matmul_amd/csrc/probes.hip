@@ -13,19 +13,19 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // Streaming read: workgroup g reads the 16-byte chunks g*256 + t, advancing
-// by the whole grid, eight loads in flight per lane.  Each workgroup writes
+// by the whole grid, ten loads in flight per lane.  Each workgroup writes
 // one word so that the loads stay live.  `bytes` is a multiple of 16.
 __global__ __launch_bounds__(256) void read_kernel(const v4u* __restrict__ src, uint64_t n16,
                                                    uint32_t* __restrict__ sink) {
   const uint64_t stride = (uint64_t)gridDim.x * 256;
   uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
-    v4u v[8];
+  for (; i + 9 * stride < n16; i += 10 * stride) {
+    v4u v[10];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < 10; ++u) v[u] = src[i + u * stride];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < 10; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; i < n16; i += stride) {
     const v4u v = src[i];
