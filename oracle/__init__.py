@@ -73,6 +73,10 @@ class Oracle:
         lib.oracle_unpack.restype = ctypes.c_int
         lib.oracle_quant_acts_f32.argtypes = [_p, _i64, _i64, _p, _p, _p]
         lib.oracle_quant_acts_bf16.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        lib.oracle_quant_acts_rmsnorm_f32.argtypes = [_p, _p, ctypes.c_float, _i64, _i64, _p,
+                                                      _p, _p]
+        lib.oracle_quant_acts_rmsnorm_bf16.argtypes = [_p, _p, ctypes.c_float, _i64, _i64,
+                                                       _p, _p, _p]
         lib.oracle_int_matmul.argtypes = [_p, _p, _i64, _i64, _i64, _p]
         lib.oracle_int_dot_samples.argtypes = [_p, _p, _i64, _p, _p, _i64, _p]
         lib.oracle_rescale.argtypes = [_p, _p, ctypes.c_float, _i64, _i64, _p]
@@ -146,6 +150,28 @@ class Oracle:
         r = np.empty(M, np.int32)
         fn = self.lib.oracle_quant_acts_bf16 if bf16 else self.lib.oracle_quant_acts_f32
         fn(_ptr(X), M, K, _ptr(q), _ptr(s), _ptr(r))
+        return q, s, r
+
+    # -- R8: subln (RMSNorm with gain) before the absmax quantization --------
+    def quant_acts_rmsnorm(self, X: np.ndarray, g: np.ndarray, eps: float = 1e-5,
+                           bf16: bool = False):
+        """R8 then R4: returns (q_x int8 [M][K], s_x float [M], rowsum int32 [M]).
+
+        The codes are R4's codes of u = X * g; the scale carries the RMS factor
+        r = 1/sqrt(mean x^2 + eps).  ``bf16=True`` means X holds bf16 bits."""
+        if bf16:
+            X = np.ascontiguousarray(X, dtype=np.uint16)
+        else:
+            X = np.ascontiguousarray(X, dtype=np.float32)
+        M, K = X.shape
+        g = np.ascontiguousarray(g, dtype=np.float32)
+        assert g.shape == (K,)
+        q = np.empty((M, K), np.int8)
+        s = np.empty(M, np.float32)
+        r = np.empty(M, np.int32)
+        fn = (self.lib.oracle_quant_acts_rmsnorm_bf16 if bf16
+              else self.lib.oracle_quant_acts_rmsnorm_f32)
+        fn(_ptr(X), _ptr(g), ctypes.c_float(eps), M, K, _ptr(q), _ptr(s), _ptr(r))
         return q, s, r
 
     # -- R5: exact integer contraction --------------------------------------

@@ -35,6 +35,15 @@
  *   R6 y       = (float)((float)((float)acc * s_x) * gamma_c), left to right,
  *                no fused multiply-add.
  *   R7 ReLU^2  = h = r * r with r = max(y, 0) (a -0 input gives +0).
+ *   R8 subln   = the normalization a BitLinear layer contains, read as RMSNorm
+ *                of each token's K inputs with a per-feature gain g:
+ *                x_hat = x * r * g, r = 1 / sqrt(mean_k x^2 + eps_n), then R4
+ *                on x_hat.  Absmax quantization does not see a positive
+ *                factor shared by the row, so the codes are R4's codes of
+ *                u = x * g (one float product per element) and r enters the
+ *                scale only: s_x = (float)(s_x(u) * r).  The sum of squares is
+ *                taken in double in index order; r = (float)(1 / sqrt(S / K +
+ *                eps_n)) in double.  The 1e-5 guard of R4 applies to u.
  *
  * All float arithmetic here is IEEE binary32/binary64 with round-to-nearest-
  * even; the file must be compiled without fast-math and with
@@ -205,6 +214,46 @@ void oracle_quant_acts_bf16(const uint16_t* X, int64_t M, int64_t K, int8_t* q,
     float* row = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
     for (int64_t k = 0; k < K; ++k) row[k] = bf16_to_float(X[m * K + k]);
     quant_row(row, K, q + m * K, s_x + m, rowsum ? rowsum + m : NULL);
+    free(row);
+  }
+}
+
+/* ---------------------------------------------------------------------- */
+/* R8: subln before the activation quantization ([FA] the list of what a
+ * BitLinear layer contains: normalization; [TR] Method Adaptation).  One row
+ * of floats x, gains g.                                                    */
+static void quant_row_rmsnorm(const float* x, const float* g, int64_t K, float eps_n,
+                              int8_t* q, float* s_x, int32_t* rowsum) {
+  float* u = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+  double S = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    double d = (double)x[k];
+    S += d * d;
+    u[k] = x[k] * g[k];
+  }
+  float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));
+  quant_row(u, K, q, s_x, rowsum);
+  *s_x = *s_x * r;
+  free(u);
+}
+
+void oracle_quant_acts_rmsnorm_f32(const float* X, const float* g, float eps_n, int64_t M,
+                                   int64_t K, int8_t* q, float* s_x, int32_t* rowsum) {
+  int64_t m;
+#pragma omp parallel for schedule(static)
+  for (m = 0; m < M; ++m)
+    quant_row_rmsnorm(X + m * K, g, K, eps_n, q + m * K, s_x + m, rowsum ? rowsum + m : NULL);
+}
+
+void oracle_quant_acts_rmsnorm_bf16(const uint16_t* X, const float* g, float eps_n,
+                                    int64_t M, int64_t K, int8_t* q, float* s_x,
+                                    int32_t* rowsum) {
+  int64_t m;
+#pragma omp parallel for schedule(static)
+  for (m = 0; m < M; ++m) {
+    float* row = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+    for (int64_t k = 0; k < K; ++k) row[k] = bf16_to_float(X[m * K + k]);
+    quant_row_rmsnorm(row, g, K, eps_n, q + m * K, s_x + m, rowsum ? rowsum + m : NULL);
     free(row);
   }
 }

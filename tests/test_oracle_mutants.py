@@ -36,6 +36,14 @@ MUTANTS = {
     "rescale_other_order": ("float t = (float)acc[mn] * s_x[mn / N];\n    y[mn] = t * gamma_c;",
                             "float t = (float)acc[mn] * gamma_c;\n    y[mn] = t * s_x[mn / N];"),
     "relu_dropped": ("float r = y[i] > 0.0f ? y[i] : 0.0f;", "float r = y[i];"),
+    "norm_gain_dropped": ("    u[k] = x[k] * g[k];", "    u[k] = x[k];"),
+    "norm_sum_not_mean": ("float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));",
+                          "float r = (float)(1.0 / sqrt(S + (double)eps_n));"),
+    "norm_no_sqrt": ("float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));",
+                     "float r = (float)(1.0 / (S / (double)K + (double)eps_n));"),
+    "norm_eps_outside": ("float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));",
+                         "float r = (float)(1.0 / (sqrt(S / (double)K) + (double)eps_n));"),
+    "norm_scale_missing": ("  *s_x = *s_x * r;", "  (void)r;"),
 }
 
 

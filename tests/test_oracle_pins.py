@@ -1,6 +1,6 @@
 """Pins of the CPU oracle against facts that do not come from the oracle itself.
 
-Each group of tests names the reading (R1..R7, stated in oracle/bitlinear_oracle.c)
+Each group of tests names the reading (R1..R8, stated in oracle/bitlinear_oracle.c)
 and what pins it: exact rational arithmetic, closed forms, hand-worked cases
 from tests/golden/, invariants, a library routine, or brute force.  Sources:
 "BitNet b1.58 2B4T Technical Report" card (ai-papers.xuzou.cn), Method
@@ -452,3 +452,103 @@ def test_forward_zero_rows_and_matrix(orc):
     assert gz == EPS and np.all(qz == 0)
     yz, *_ = orc.forward(X, qz, gz)
     assert np.all(yz == 0)
+
+
+# --------------------------------------------------------------------------
+# R8: subln read as RMSNorm with a per-feature gain, before R4.  Pins: with a
+# unit gain the codes are R4's and the scale ratio normalizes the row to RMS
+# 1; a constant row gives closed-form codes and factor; power-of-two scaling
+# of the input changes nothing; brute force in double of the plain
+# definition (normalize, then quantize) agrees away from rounding ties.
+# --------------------------------------------------------------------------
+def _gain(seed, K):
+    return _rng(seed).uniform(0.5, 1.5, K).astype(np.float32)
+
+
+@pytest.mark.parametrize("M,K,seed", [(4, 256, 91), (3, 2560, 92), (2, 6912, 93)])
+def test_rmsnorm_unit_gain_is_plain_quant_and_normalizes(orc, M, K, seed):
+    X = _acts(seed, M, K, 3.0)
+    q, s, r = orc.quant_acts_rmsnorm(X, np.ones(K, np.float32), 0.0)
+    q0, s0, r0 = orc.quant_acts(X)
+    assert np.array_equal(q, q0) and np.array_equal(r, r0)
+    f = s.astype(np.float64) / s0.astype(np.float64)  # the RMS factor
+    rms = np.sqrt(np.mean((X.astype(np.float64) * f[:, None]) ** 2, axis=1))
+    assert np.all(np.abs(rms - 1.0) <= 3e-7)
+
+
+def _rint_even(v: Fraction) -> int:
+    fl = v.numerator // v.denominator
+    rem = v - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        return fl + 1
+    return fl
+
+
+def test_rmsnorm_constant_row_closed_form(orc):
+    K, c, eps = 512, np.float32(2.0 ** -7), float(np.float32(1e-4))
+    steps = [Fraction(j, 4) for j in range(-4, 5)]  # gains -1, -0.75, ..., 1
+    g = np.array([float(steps[k % 9]) for k in range(K)], np.float32)
+    X = np.full((2, K), c, np.float32)
+    X[1] = -c
+    q, s, r = orc.quant_acts_rmsnorm(X, g, eps)
+    want = np.array([_rint_even(127 * steps[k % 9]) for k in range(K)], np.int8)
+    assert np.array_equal(q[0], want) and np.array_equal(q[1], -want)
+    assert np.array_equal(r, q.astype(np.int32).sum(axis=1))
+    # mean x^2 = c^2 exactly, so r = 1/sqrt(c^2 + eps); max |u| = c
+    rf = np.float32(1.0 / np.sqrt(float(c) ** 2 + eps))
+    assert s[0] == s[1] == np.float32(np.float32(c / np.float32(127)) * rf)
+
+
+@pytest.mark.parametrize("j", [-6, 5])
+def test_rmsnorm_power_of_two_scaling_and_signs(orc, j):
+    X = _acts(94, 5, 768)
+    g = _gain(95, 768)
+    q0, s0, r0 = orc.quant_acts_rmsnorm(X, g, 0.0)
+    q1, s1, r1 = orc.quant_acts_rmsnorm(X * np.float32(2.0 ** j), g, 0.0)
+    assert np.array_equal(q1, q0) and np.array_equal(s1, s0) and np.array_equal(r1, r0)
+    qn, sn, _ = orc.quant_acts_rmsnorm(-X, g, 0.0)
+    qg, sg, _ = orc.quant_acts_rmsnorm(X, -g, 0.0)
+    assert np.array_equal(qn, -q0) and np.array_equal(sn, s0)
+    assert np.array_equal(qg, -q0) and np.array_equal(sg, s0)
+
+
+@pytest.mark.parametrize("M,K,seed", [(6, 2560, 96), (3, 6912, 97)])
+def test_rmsnorm_matches_double_definition(orc, M, K, seed):
+    X = _acts(seed, M, K, 2.0)
+    g = _gain(seed + 100, K)
+    eps = 1e-5
+    q, s, rs = orc.quant_acts_rmsnorm(X, g, eps)
+    Xd, gd = X.astype(np.float64), g.astype(np.float64)
+    rr = 1.0 / np.sqrt((Xd ** 2).mean(axis=1) + eps)
+    xh = Xd * rr[:, None] * gd[None, :]  # normalize first, as the definition says
+    a = np.abs(xh).max(axis=1)
+    t = xh * 127.0 / a[:, None]
+    near_tie = np.abs(np.abs(t - np.floor(t)) - 0.5) < 1e-4
+    assert np.all((q == np.clip(np.rint(t), -127, 127)) | near_tie)
+    assert near_tie.mean() < 1e-3
+    assert np.all(np.abs(s.astype(np.float64) / (a / 127.0) - 1.0) <= 3e-7)
+    assert np.array_equal(rs, q.astype(np.int32).sum(axis=1))
+
+
+def test_rmsnorm_zero_row_and_zero_gain(orc):
+    X = _acts(98, 3, 256)
+    X[1] = 0
+    g = _gain(99, 256)
+    g[10] = 0
+    q, s, _ = orc.quant_acts_rmsnorm(X, g, 1e-5)
+    assert np.all(q[:, 10] == 0)
+    assert np.all(q[1] == 0)
+    eps = np.float64(np.float32(1e-5))  # the epsilon is a float argument
+    assert s[1] == np.float32(np.float32(EPS / np.float32(127)) * np.float32(1.0 / np.sqrt(eps)))
+
+
+def test_rmsnorm_bf16_matches_widened_f32(orc):
+    from w1_a8_matmul_amd.workloads import to_bf16_bits
+
+    X = _acts(100, 4, 2560, 2.0)
+    g = _gain(101, 2560)
+    bits = to_bf16_bits(X)
+    widened = (bits.astype(np.uint32) << 16).view(np.float32)
+    qa, sa, ra = orc.quant_acts_rmsnorm(bits, g, 1e-5, bf16=True)
+    qb, sb, rb = orc.quant_acts_rmsnorm(widened, g, 1e-5)
+    assert np.array_equal(qa, qb) and np.array_equal(sa, sb) and np.array_equal(ra, rb)
