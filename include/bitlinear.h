@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 2
+#define BITLINEAR_ABI_VERSION 3
 
 typedef enum {
   BITLINEAR_OK = 0,
@@ -151,6 +151,21 @@ bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, i
                                          int64_t K, int8_t* Xq, float* x_scale,
                                          int32_t* x_rowsum, void* stream);
 
+/* The same quantization after subln, the normalization a BitLinear layer
+ * contains (fishai digest, list of BitLinear parts: normalization;
+ * technical-report card, Method Adaptation), read as an RMSNorm of each
+ * token with a per-feature gain: x_hat = x * r * g with
+ * r = 1 / sqrt(mean_k x^2 + norm_eps).  Absmax quantization cannot see the
+ * row's positive factor r, so Xq and x_rowsum are the codes of x * g (float
+ * products) and x_scale = (max|x * g| / 127) * r: the codes do not depend on
+ * the order of the sum of squares (taken in double).  norm_gain: float [K],
+ * device, 16-byte aligned, required; norm_eps finite and >= 0 (1e-5 is the
+ * usual value).  Other arguments and errors as bitlinear_quantize_acts. */
+bitlinear_status bitlinear_quantize_acts_rmsnorm(const void* X, bitlinear_dtype dtype,
+                                                 int64_t M, int64_t K, const float* norm_gain,
+                                                 float norm_eps, int8_t* Xq, float* x_scale,
+                                                 int32_t* x_rowsum, void* stream);
+
 /* The BitLinear forward: Y [M][N] (float) from X [M][K] (dtype), the packed
  * ternary weights and gamma_c (device float, as written by
  * bitlinear_quantize_weights).  Quantizes X per token, contracts in int32,
@@ -167,6 +182,18 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
                                    const float* gamma, float* Y, bitlinear_epilogue epi,
                                    const bitlinear_debug* dbg, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* bitlinear_forward with subln first, fused into the quantization (as in
+ * bitlinear_quantize_acts_rmsnorm): norm_gain float [K] (device, 16-byte
+ * aligned, required), norm_eps finite and >= 0.  Same kernels, workspace and
+ * errors as bitlinear_forward; xscale_out in `dbg` receives the scale with
+ * the RMS factor. */
+bitlinear_status bitlinear_forward_rmsnorm(const void* X, bitlinear_dtype dtype, int64_t M,
+                                           int64_t K, int64_t N, const float* norm_gain,
+                                           float norm_eps, const uint8_t* packed,
+                                           const float* gamma, float* Y,
+                                           bitlinear_epilogue epi, const bitlinear_debug* dbg,
+                                           void* ws, size_t ws_bytes, void* stream);
 
 /* The same forward from activations already quantized by
  * bitlinear_quantize_acts: Xq [M][K], x_scale [M], x_rowsum [M] (all three
@@ -207,6 +234,10 @@ typedef struct {
   const uint8_t* packed;  /* packed weights of this layer */
   const float* gamma;     /* gamma_c of this layer (device float) */
   float* Y;               /* [M][N] output; must not overlap any layer's input */
+  const float* norm_gain; /* NULL, or subln's gain [K] (device, 16-byte aligned):
+                             the layer then quantizes as
+                             bitlinear_quantize_acts_rmsnorm does */
+  float norm_eps;         /* subln epsilon (finite, >= 0) when norm_gain is set */
 } bitlinear_group_op;
 
 /* Opaque host-side handle of a planned group (host memory only). */

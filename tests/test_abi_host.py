@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert L.bitlinear_abi_version() == 2
+    assert L.bitlinear_abi_version() == 3
     for s in range(8):
         assert L.bitlinear_status_string(s).decode()
     assert L.bitlinear_status_string(99).decode() == "unknown status"
@@ -118,6 +118,27 @@ def test_forward_validation(L):
     assert f(None, 1, 0, 2560, 6912, None, None, None, 0, None, None, 0, None) == OK
 
 
+def test_rmsnorm_entry_points_validation(L):
+    qa = L.bitlinear_quantize_acts_rmsnorm
+    assert qa(A, 1, 4, 256, None, 1e-5, A, A, A, None) == ERR_NULL  # the gain is required
+    assert "norm_gain" in _err(L)
+    assert qa(A, 1, 4, 256, U, 1e-5, A, A, A, None) == ERR_ALIGN
+    assert qa(A, 1, 4, 256, A, -1.0, A, A, A, None) == ERR_ARG
+    assert qa(A, 1, 4, 256, A, float("nan"), A, A, A, None) == ERR_ARG
+    assert qa(A, 1, 4, 256, A, float("inf"), A, A, A, None) == ERR_ARG
+    assert qa(A, 7, 4, 256, A, 1e-5, A, A, A, None) == ERR_DTYPE
+    assert qa(A, 0, 4, 100, A, 1e-5, A, A, A, None) == ERR_SHAPE
+    assert qa(None, 1, 0, 256, None, 1e-5, None, None, None, None) == OK
+    f = L.bitlinear_forward_rmsnorm
+    assert f(A, 0, 1, 256, 16, None, 1e-5, A, A, A, 0, None, None, 0, None) == ERR_NULL
+    assert f(A, 0, 1, 256, 16, U, 1e-5, A, A, A, 0, None, None, 0, None) == ERR_ALIGN
+    assert f(A, 0, 1, 256, 16, A, -0.5, A, A, A, 0, None, None, 0, None) == ERR_ARG
+    assert f(A, 0, 1, 256, 24, A, 1e-5, A, A, A, 0, None, None, 0, None) == ERR_SHAPE
+    assert f(A, 1, 2048, 2560, 6912, A, 1e-5, A, A, A, 0, None, None, 0, None) == ERR_WS
+    assert f(None, 1, 0, 2560, 6912, None, 1e-5, None, None, None, 0, None, None, 0,
+             None) == OK
+
+
 def test_forward_q_validation(L):
     f = L.bitlinear_forward_q
     assert f(A, A, A, 4, 256, 16, A, A, A, 9, None, 0, None) == ERR_ARG
@@ -137,14 +158,14 @@ def test_binding_refuses_cpu_tensors():
         bl.quantize_acts(torch.zeros(4, 256))
 
 
-def _gop(X=A, dtype=1, epi=0, K=2560, N=256, packed=A, gamma=A, Y=A):
-    return bl.GroupOp(X, dtype, epi, K, N, packed, gamma, Y)
+def _gop(X=A, dtype=1, epi=0, K=2560, N=256, packed=A, gamma=A, Y=A, gain=None, eps=0.0):
+    return bl.GroupOp(X, dtype, epi, K, N, packed, gamma, Y, gain, eps)
 
 
 def test_group_validation(L):
     arr = (bl.GroupOp * 2)(_gop(), _gop(K=6912, N=2560))
     need = L.bitlinear_group_workspace_bytes(arr, 2, 1)
-    assert need >= 2 * 64 + (2 + 20) * 16 + 8  # layer table, work units of 8 tiles, queue
+    assert need >= 2 * 80 + (2 + 20) * 16 + 8  # layer table, work units, queue
     assert L.bitlinear_group_workspace_bytes(arr, 2, 17) > 0      # M > 16: grouped GEMM
     assert L.bitlinear_group_workspace_bytes(arr, 2, 65537) == 0
     assert L.bitlinear_group_workspace_bytes(arr, 2, 16) > 0      # 16 x 6912 fits in LDS
@@ -159,7 +180,8 @@ def test_group_validation(L):
     assert L.bitlinear_group_create(arr, 2, 1, A, need - 1, ctypes.byref(h)) == ERR_WS
     assert L.bitlinear_group_create(arr, 2, 1, U, need, ctypes.byref(h)) == ERR_ALIGN
     bad = [(_gop(dtype=5), ERR_DTYPE), (_gop(epi=3), ERR_ARG), (_gop(N=24), ERR_SHAPE),
-           (_gop(K=12288 + 256), ERR_SHAPE), (_gop(Y=None), ERR_NULL), (_gop(X=U), ERR_ALIGN)]
+           (_gop(K=12288 + 256), ERR_SHAPE), (_gop(Y=None), ERR_NULL), (_gop(X=U), ERR_ALIGN),
+           (_gop(gain=U, eps=1e-5), ERR_ALIGN), (_gop(gain=A, eps=-1.0), ERR_ARG)]
     for op, code in bad:
         one = (bl.GroupOp * 1)(op)
         assert L.bitlinear_group_create(one, 1, 1, A, 1 << 30, ctypes.byref(h)) == code

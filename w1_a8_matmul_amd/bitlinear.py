@@ -37,7 +37,8 @@ class Debug(ctypes.Structure):
 
 class GroupOp(ctypes.Structure):
     _fields_ = [("X", _p), ("dtype", ctypes.c_int), ("epi", ctypes.c_int), ("K", _i64),
-                ("N", _i64), ("packed", _p), ("gamma", _p), ("Y", _p)]
+                ("N", _i64), ("packed", _p), ("gamma", _p), ("Y", _p), ("norm_gain", _p),
+                ("norm_eps", ctypes.c_float)]
 
 
 _lib = None
@@ -70,8 +71,13 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_pack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_unpack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_quantize_acts.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
+    L.bitlinear_quantize_acts_rmsnorm.argtypes = [_p, ctypes.c_int, _i64, _i64, _p,
+                                                  ctypes.c_float, _p, _p, _p, _p]
     L.bitlinear_forward.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p,
                                     ctypes.c_int, ctypes.POINTER(Debug), _p, _sz, _p]
+    L.bitlinear_forward_rmsnorm.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p,
+                                            ctypes.c_float, _p, _p, _p, ctypes.c_int, _p, _p,
+                                            _sz, _p]
     L.bitlinear_forward_q.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p,
                                       ctypes.c_int, _p, _sz, _p]
     for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
@@ -183,24 +189,36 @@ def unpack_ternary(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
 
 
 # -- activations ------------------------------------------------------------
-def quantize_acts(X: torch.Tensor):
-    """Per-token absmax int8: returns (Xq int8 [M][K], x_scale [M], x_rowsum [M])."""
+def quantize_acts(X: torch.Tensor, norm_gain: Optional[torch.Tensor] = None,
+                  norm_eps: float = 1e-5):
+    """Per-token absmax int8: returns (Xq int8 [M][K], x_scale [M], x_rowsum [M]).
+
+    With ``norm_gain`` (float32 [K] on the GPU), subln (RMSNorm with that
+    gain and ``norm_eps``) runs first, fused into the same launch."""
     M, K = X.shape
     Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
     sx = torch.empty(M, dtype=torch.float32, device=X.device)
     rs = torch.empty(M, dtype=torch.int32, device=X.device)
-    check(lib().bitlinear_quantize_acts(_ptr(X), _dtype_code(X), M, K, _ptr(Xq), _ptr(sx),
-                                        _ptr(rs), _stream()),
-          "bitlinear_quantize_acts")
+    if norm_gain is None:
+        check(lib().bitlinear_quantize_acts(_ptr(X), _dtype_code(X), M, K, _ptr(Xq), _ptr(sx),
+                                            _ptr(rs), _stream()),
+              "bitlinear_quantize_acts")
+    else:
+        check(lib().bitlinear_quantize_acts_rmsnorm(_ptr(X), _dtype_code(X), M, K,
+                                                    _ptr(norm_gain), norm_eps, _ptr(Xq),
+                                                    _ptr(sx), _ptr(rs), _stream()),
+              "bitlinear_quantize_acts_rmsnorm")
     return Xq, sx, rs
 
 
 # -- forward ----------------------------------------------------------------
 def forward(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
             epilogue: Optional[str] = None, debug: bool = False,
-            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            norm_gain: Optional[torch.Tensor] = None, norm_eps: float = 1e-5):
     """Y [M][N] float32 = BitLinear(X).  With debug=True returns
-    (Y, {"xq": int8 [M][K], "x_scale": [M], "acc": int32 [M][N]})."""
+    (Y, {"xq": int8 [M][K], "x_scale": [M], "acc": int32 [M][N]}).  With
+    ``norm_gain`` (float32 [K]) subln runs first, fused into the quantization."""
     M, K = X.shape
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=X.device)
@@ -216,11 +234,18 @@ def forward(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
                "x_scale": torch.empty(M, dtype=torch.float32, device=X.device),
                "acc": torch.empty((M, N), dtype=torch.int32, device=X.device)}
         dbg_struct = Debug(_ptr(dbg["xq"]), _ptr(dbg["x_scale"]), _ptr(dbg["acc"]))
-    st = lib().bitlinear_forward(
-        _ptr(X), _dtype_code(X), M, K, N, _ptr(packed), _ptr(gamma), _ptr(out),
-        EPI[epilogue], ctypes.byref(dbg_struct) if dbg_struct is not None else None,
-        _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream())
-    check(st, "bitlinear_forward")
+    dbg_arg = ctypes.byref(dbg_struct) if dbg_struct is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    if norm_gain is None:
+        st = lib().bitlinear_forward(
+            _ptr(X), _dtype_code(X), M, K, N, _ptr(packed), _ptr(gamma), _ptr(out),
+            EPI[epilogue], dbg_arg, _ptr(workspace), ws_n, _stream())
+        check(st, "bitlinear_forward")
+    else:
+        st = lib().bitlinear_forward_rmsnorm(
+            _ptr(X), _dtype_code(X), M, K, N, _ptr(norm_gain), norm_eps, _ptr(packed),
+            _ptr(gamma), _ptr(out), EPI[epilogue], dbg_arg, _ptr(workspace), ws_n, _stream())
+        check(st, "bitlinear_forward_rmsnorm")
     return (out, dbg) if debug else out
 
 
@@ -259,8 +284,10 @@ class Group:
     persistent launches (skinny kernel up to 16 tokens, tiled GEMM above).
 
     layers: list of (X, packed, gamma, N, epilogue, Y) with X [M][K] on the
-    GPU and Y [M][N] float32 (allocated when None).  The tensors must stay
-    alive while the group is used; ``forward()`` enqueues on torch's stream."""
+    GPU and Y [M][N] float32 (allocated when None), optionally followed by a
+    subln gain (float32 [K] or None) and its epsilon (default 1e-5).  The
+    tensors must stay alive while the group is used; ``forward()`` enqueues
+    on torch's stream."""
 
     def __init__(self, layers):
         L = lib()
@@ -268,7 +295,10 @@ class Group:
         self.keep = []
         self.outputs = []
         M = None
-        for i, (X, packed, gamma, N, epilogue, Y) in enumerate(layers):
+        for i, layer in enumerate(layers):
+            X, packed, gamma, N, epilogue, Y = layer[:6]
+            gain = layer[6] if len(layer) > 6 else None
+            eps = float(layer[7]) if len(layer) > 7 else 1e-5
             m, K = X.shape
             M = m if M is None else M
             if m != M:
@@ -276,8 +306,8 @@ class Group:
             if Y is None:
                 Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
             arr[i] = GroupOp(_ptr(X), _dtype_code(X), EPI[epilogue], K, N, _ptr(packed),
-                             _ptr(gamma), _ptr(Y))
-            self.keep += [X, packed, gamma]
+                             _ptr(gamma), _ptr(Y), _ptr(gain), eps if gain is not None else 0.0)
+            self.keep += [X, packed, gamma] + ([gain] if gain is not None else [])
             self.outputs.append(Y)
         self.M = M
         need = L.bitlinear_group_workspace_bytes(arr, len(layers), M)

@@ -142,6 +142,16 @@ GroupLayout group_layout(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   return L;
 }
 
+// subln arguments: the gain is optional (NULL: none); when given it must be
+// 16-byte aligned device memory and the epsilon finite and non-negative.
+bitlinear_status check_norm(const float* norm_gain, float norm_eps) {
+  if (!norm_gain) return BITLINEAR_OK;
+  if (!aligned16(norm_gain)) return fail(BITLINEAR_ERR_ALIGN, "norm_gain must be 16-byte aligned");
+  if (!(norm_eps >= 0.0f) || norm_eps > 3.0e38f)
+    return fail(BITLINEAR_ERR_ARG, "norm_eps must be finite and >= 0");
+  return BITLINEAR_OK;
+}
+
 bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   if (!ops) return fail(BITLINEAR_ERR_NULL, "ops is required");
   if (n_ops < 1 || n_ops > 65536) return fail(BITLINEAR_ERR_ARG, "n_ops=%d out of range", n_ops);
@@ -163,6 +173,8 @@ bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M
     if (!o.X || !o.packed || !o.gamma || !o.Y) return fail(BITLINEAR_ERR_NULL, "op %d: X, packed, gamma and Y are required", i);
     if (!aligned16(o.X) || !aligned16(o.packed) || !aligned16(o.gamma) || !aligned16(o.Y))
       return fail(BITLINEAR_ERR_ALIGN, "op %d: tensor pointers must be 16-byte aligned", i);
+    st = check_norm(o.norm_gain, o.norm_eps);
+    if (st != BITLINEAR_OK) return st;
     items += skinny ? o.N / 16 : bl_group_gemm_tiles((int)M, (int)o.N);
   }
   if (items > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "too many output tiles");
@@ -184,6 +196,7 @@ struct bitlinear_group {
   int G;
   int max_k;
   int threads;
+  bool norm;  // some layer has a subln gain
   bool gemm;
   int n_items;  // items over all layers (output tiles in the GEMM mode)
   int n_units;  // shared work units of the skinny kernel
@@ -265,9 +278,10 @@ bitlinear_status bitlinear_unpack_ternary(const uint8_t* packed, int64_t N, int6
                   "bitlinear_unpack_ternary");
 }
 
-bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, int64_t M,
-                                         int64_t K, int8_t* Xq, float* x_scale,
-                                         int32_t* x_rowsum, void* stream) {
+static bitlinear_status quantize_acts_impl(const void* X, bitlinear_dtype dtype, int64_t M,
+                                           int64_t K, const float* norm_gain, float norm_eps,
+                                           int8_t* Xq, float* x_scale, int32_t* x_rowsum,
+                                           void* stream, const char* name) {
   if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
     return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
   if (M < 0 || K < 1 || K % 16 != 0 || K > kMaxK)
@@ -279,15 +293,36 @@ bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, i
   if (!aligned16(X) || !aligned16(Xq) || !aligned16(x_scale) ||
       (x_rowsum && !aligned16(x_rowsum)))
     return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  const bitlinear_status st = check_norm(norm_gain, norm_eps);
+  if (st != BITLINEAR_OK) return st;
   return from_hip(bl_launch_quant_acts(X, (int)dtype, M, K, Xq, x_scale, x_rowsum, nullptr, 0,
-                                       static_cast<hipStream_t>(stream)),
-                  "bitlinear_quantize_acts");
+                                       static_cast<hipStream_t>(stream), norm_gain, norm_eps),
+                  name);
 }
 
-bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t M, int64_t K,
-                                   int64_t N, const uint8_t* packed, const float* gamma,
-                                   float* Y, bitlinear_epilogue epi, const bitlinear_debug* dbg,
-                                   void* ws, size_t ws_bytes, void* stream) {
+bitlinear_status bitlinear_quantize_acts(const void* X, bitlinear_dtype dtype, int64_t M,
+                                         int64_t K, int8_t* Xq, float* x_scale,
+                                         int32_t* x_rowsum, void* stream) {
+  return quantize_acts_impl(X, dtype, M, K, nullptr, 0.0f, Xq, x_scale, x_rowsum, stream,
+                            "bitlinear_quantize_acts");
+}
+
+bitlinear_status bitlinear_quantize_acts_rmsnorm(const void* X, bitlinear_dtype dtype,
+                                                 int64_t M, int64_t K, const float* norm_gain,
+                                                 float norm_eps, int8_t* Xq, float* x_scale,
+                                                 int32_t* x_rowsum, void* stream) {
+  if (!norm_gain && M > 0) return fail(BITLINEAR_ERR_NULL, "norm_gain is required");
+  return quantize_acts_impl(X, dtype, M, K, norm_gain, norm_eps, Xq, x_scale, x_rowsum, stream,
+                            "bitlinear_quantize_acts_rmsnorm");
+}
+
+
+static bitlinear_status forward_impl(const void* X, bitlinear_dtype dtype, int64_t M,
+                                     int64_t K, int64_t N, const float* norm_gain,
+                                     float norm_eps, const uint8_t* packed, const float* gamma,
+                                     float* Y, bitlinear_epilogue epi,
+                                     const bitlinear_debug* dbg, void* ws, size_t ws_bytes,
+                                     void* stream, const char* name) {
   if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
     return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
   if (epi != BITLINEAR_EPI_NONE && epi != BITLINEAR_EPI_RELU2)
@@ -306,13 +341,15 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
       (xq_out && !aligned16(xq_out)) || (xs_out && !aligned16(xs_out)) ||
       (acc_out && !aligned16(acc_out)))
     return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  st = check_norm(norm_gain, norm_eps);
+  if (st != BITLINEAR_OK) return st;
   const bool relu2 = epi == BITLINEAR_EPI_RELU2;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (bl_gemv_supports(M, K))
     return from_hip(bl_launch_gemv(X, (int)dtype, M, K, N, packed, gamma, Y, relu2, xq_out,
-                                   xs_out, acc_out, s),
-                    "bitlinear_forward");
+                                   xs_out, acc_out, s, norm_gain, norm_eps),
+                    name);
 
   const size_t need = forward_workspace(M, K, N);
   if (!ws || ws_bytes < need)
@@ -328,15 +365,36 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
   // The quantization launch also clears the GEMM's counters, so the
   // workspace's contents on entry do not matter.
   hipError_t e = bl_launch_quant_acts(X, (int)dtype, M, K, xq, sx, rs, gemm_ws,
-                                      (int)(bl_gemm_counter_bytes() / sizeof(int)), s);
+                                      (int)(bl_gemm_counter_bytes() / sizeof(int)), s,
+                                      norm_gain, norm_eps);
   if (e == hipSuccess && xq_out)
     e = hipMemcpyAsync(xq_out, xq, (size_t)M * (size_t)K, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess && xs_out)
     e = hipMemcpyAsync(xs_out, sx, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = bl_launch_gemm_q(xq, sx, rs, M, K, N, packed, gamma, Y, relu2, acc_out, gemm_ws, s);
-  return from_hip(e, "bitlinear_forward");
+  return from_hip(e, name);
 }
+
+bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t M, int64_t K,
+                                   int64_t N, const uint8_t* packed, const float* gamma,
+                                   float* Y, bitlinear_epilogue epi, const bitlinear_debug* dbg,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(X, dtype, M, K, N, nullptr, 0.0f, packed, gamma, Y, epi, dbg, ws,
+                      ws_bytes, stream, "bitlinear_forward");
+}
+
+bitlinear_status bitlinear_forward_rmsnorm(const void* X, bitlinear_dtype dtype, int64_t M,
+                                           int64_t K, int64_t N, const float* norm_gain,
+                                           float norm_eps, const uint8_t* packed,
+                                           const float* gamma, float* Y,
+                                           bitlinear_epilogue epi, const bitlinear_debug* dbg,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  if (!norm_gain && M > 0) return fail(BITLINEAR_ERR_NULL, "norm_gain is required");
+  return forward_impl(X, dtype, M, K, N, norm_gain, norm_eps, packed, gamma, Y, epi, dbg, ws,
+                      ws_bytes, stream, "bitlinear_forward_rmsnorm");
+}
+
 
 bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      const int32_t* x_rowsum, int64_t M, int64_t K, int64_t N,
@@ -393,6 +451,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   std::vector<GroupOp> table((size_t)n_ops);
   int64_t item = 0, xq_off = 0;
   int max_k = 0;
+  bool norm = false;
   for (int i = 0; i < n_ops; ++i) {
     const bitlinear_group_op& o = ops[i];
     GroupOp& t = table[(size_t)i];
@@ -406,6 +465,9 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     t.dtype = (int32_t)o.dtype;
     t.relu2 = o.epi == BITLINEAR_EPI_RELU2 ? 1 : 0;
     t.item_begin = (int32_t)item;
+    t.norm_gain = o.norm_gain;
+    t.norm_eps = o.norm_eps;
+    if (o.norm_gain) norm = true;
     t.xq_off = xq_off;
     xq_off += (int64_t)align256((size_t)M * (size_t)o.K);
     // Work items: 16-row weight tiles (skinny) or output tiles of the GEMM;
@@ -419,7 +481,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   // work units from the queue; GEMM: output tiles strided).
   int threads = 256, per_cu = 1;
   if (skinny) {
-    e = bl_group_plan((int)M, max_k, &threads, &per_cu);
+    e = bl_group_plan((int)M, max_k, norm, &threads, &per_cu);
     if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   } else {
     per_cu = bl_group_gemm_blocks_per_cu((int)M);
@@ -478,6 +540,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->G = G;
   g->max_k = max_k;
   g->threads = threads;
+  g->norm = norm;
   g->gemm = !skinny;
   g->n_items = (int)item;
   g->n_units = (int)L.n_units;
@@ -502,7 +565,8 @@ bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream)
     return from_hip(e, "bitlinear_group_forward");
   }
   return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->units, g->n_units,
-                                  g->queue, g->G, g->max_k, g->threads, g->xq, g->sx, g->rs,
+                                  g->queue, g->G, g->max_k, g->threads, g->norm, g->xq, g->sx,
+                                  g->rs,
                                   static_cast<hipStream_t>(stream)),
                   "bitlinear_group_forward");
 }

@@ -90,6 +90,19 @@ __device__ __forceinline__ int wave_sum(int v) {
          __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
+// Sum over the wave in double (the subln sum of squares).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// subln's RMS factor of a row whose squares sum to S (double): one rounding
+// of 1 / sqrt(S / K + eps) to float, the rest in double.
+__device__ __forceinline__ float rms_factor(double S, int64_t K, float eps) {
+  return (float)(1.0 / sqrt(S / (double)K + (double)eps));
+}
+
 // rint(v) clamped to [-127, 127] as an int; v is x * qs.
 __device__ __forceinline__ int quant_i8(float v) {
   float r = __builtin_rintf(v);
@@ -129,16 +142,19 @@ hipError_t bl_launch_pack(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packe
 hipError_t bl_launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
                             hipStream_t s);
 // Per-token activation quantization; also zeroes n_zero ints at `zero`
-// (may be null) for the launch that follows.
+// (may be null) for the launch that follows.  norm_gain (float [K], 16-byte
+// aligned) selects subln first (RMSNorm with that gain and norm_eps).
 hipError_t bl_launch_quant_acts(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
                                 float* x_scale, int32_t* x_rowsum, int* zero, int n_zero,
-                                hipStream_t s);
+                                hipStream_t s, const float* norm_gain = nullptr,
+                                float norm_eps = 0.0f);
 // Small-M fused forward (activation quantization inside the kernel).
 bool bl_gemv_supports(int64_t M, int64_t K);
 hipError_t bl_launch_gemv(const void* X, int dtype, int64_t M, int64_t K, int64_t N,
                           const uint8_t* packed, const float* gamma, float* Y, bool relu2,
                           int8_t* xq_out, float* xscale_out, int32_t* acc_out,
-                          hipStream_t s);
+                          hipStream_t s, const float* norm_gain = nullptr,
+                          float norm_eps = 0.0f);
 // Forward from quantized activations on the int8 MFMA units.  gemm_ws
 // (bl_gemm_workspace_bytes, its first bl_gemm_counter_bytes zero on entry
 // and left zero) lets the last, partial round of tiles be shared along K;

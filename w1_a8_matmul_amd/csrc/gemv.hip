@@ -35,11 +35,12 @@ constexpr int kMaxLoadsPerLane = 12;
 // (fewer workgroups, less repeated quantization) and eight-wave workgroups
 // were slower on both decode projections, and this form of the kernel was
 // faster than one written for a single tile (3.2 vs 3.5 us for 2560->6912).
-template <int M, int DT, int L, int TPW>
+template <int M, int DT, int L, int TPW, bool NORM>
 __global__ __launch_bounds__(kNT) void gemv_kernel(
     const void* __restrict__ X, int K, int64_t N, const uint8_t* __restrict__ packed,
     const float* __restrict__ gamma_p, float* __restrict__ Y, int relu2,
-    int8_t* __restrict__ xq_out, float* __restrict__ xscale_out, int32_t* __restrict__ acc_out) {
+    int8_t* __restrict__ xq_out, float* __restrict__ xscale_out, int32_t* __restrict__ acc_out,
+    const float* __restrict__ norm_gain, float norm_eps) {
   constexpr int W = kNT / kWave;
   constexpr int KCH = (L + 1) / 2;
   constexpr int kRegsPerRow = KCH * (DT == 1 ? 4 : 8);
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(
   extern __shared__ __align__(16) int8_t xs[];  // [M][K] int8 activations
   __shared__ float red_f[W];
   __shared__ int red_i[W];
+  __shared__ double red_d[W];
   __shared__ float s_scale[M];
   __shared__ int s_rowsum[M];
   __shared__ int partial[TPW][M][W][kWave];
@@ -54,10 +56,13 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ntiles = N / kTileRows;
   const int kblocks = K / kTileCols;
-  // 1) activation rows 0..P-1, then 2) every weight load of this lane.
+  // 1) activation rows 0..P-1 (and the subln gains), then 2) every weight
+  // load of this lane.
   Chunk<DT> pre[P > 0 ? P : 1][KCH];
 #pragma unroll
   for (int m = 0; m < P; ++m) load_row<DT, kNT, KCH>(X, m, K, pre[m]);
+  Gains<kNT, KCH> gn;
+  if constexpr (NORM) load_gains<kNT, KCH>(norm_gain, K, gn);
   uint4 wv[TPW][L];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
@@ -70,12 +75,13 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     if (m < P) {
-      quantize_row<DT, kNT, KCH>(pre[m < P ? m : 0], K, xs + m * K, red_f, red_i, s_scale + m,
-                                 s_rowsum + m);
+      quantize_row<DT, kNT, KCH, NORM>(pre[m < P ? m : 0], K, xs + m * K, red_f, red_i,
+                                       s_scale + m, s_rowsum + m, &gn, true, norm_eps, red_d);
     } else {
       Chunk<DT> ch[KCH];
       load_row<DT, kNT, KCH>(X, m, K, ch);
-      quantize_row<DT, kNT, KCH>(ch, K, xs + m * K, red_f, red_i, s_scale + m, s_rowsum + m);
+      quantize_row<DT, kNT, KCH, NORM>(ch, K, xs + m * K, red_f, red_i, s_scale + m,
+                                       s_rowsum + m, &gn, true, norm_eps, red_d);
     }
   }
   __syncthreads();
@@ -114,26 +120,43 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(
   }
 }
 
+// Arguments every launch passes through.
+struct GemvArgs {
+  const void* X;
+  int64_t K, N;
+  const uint8_t* packed;
+  const float* gamma;
+  float* Y;
+  bool relu2;
+  int8_t* xq;
+  float* xs;
+  int32_t* acc;
+  const float* norm_gain;
+  float norm_eps;
+};
+
 template <int M, int DT, int L>
-hipError_t launch_one(const void* X, int64_t K, int64_t N, const uint8_t* packed,
-                      const float* gamma, float* Y, bool relu2, int8_t* xq, float* xs,
-                      int32_t* acc, hipStream_t s) {
-  const size_t lds = (size_t)M * (size_t)K;
+hipError_t launch_one(const GemvArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)M * (size_t)a.K;
   constexpr int kTilesPerWorkgroup = 1;
-  hipLaunchKernelGGL((gemv_kernel<M, DT, L, kTilesPerWorkgroup>),
-                     dim3((unsigned)(N / kTileRows / kTilesPerWorkgroup)), dim3(kNT), lds,
-                     s, X, (int)K, N, packed, gamma, Y, relu2 ? 1 : 0, xq, xs, acc);
+  const dim3 grid((unsigned)(a.N / kTileRows / kTilesPerWorkgroup)), block(kNT);
+  if (a.norm_gain)
+    hipLaunchKernelGGL((gemv_kernel<M, DT, L, kTilesPerWorkgroup, true>), grid, block, lds, s,
+                       a.X, (int)a.K, a.N, a.packed, a.gamma, a.Y, a.relu2 ? 1 : 0, a.xq, a.xs,
+                       a.acc, a.norm_gain, a.norm_eps);
+  else
+    hipLaunchKernelGGL((gemv_kernel<M, DT, L, kTilesPerWorkgroup, false>), grid, block, lds, s,
+                       a.X, (int)a.K, a.N, a.packed, a.gamma, a.Y, a.relu2 ? 1 : 0, a.xq, a.xs,
+                       a.acc, a.norm_gain, a.norm_eps);
   return hipGetLastError();
 }
 
 // L = ceil(kblocks / 4), rounded up to an instantiated count.
 template <int M, int DT>
-hipError_t launch_m(const void* X, int64_t K, int64_t N, const uint8_t* packed,
-                    const float* gamma, float* Y, bool relu2, int8_t* xq, float* xs,
-                    int32_t* acc, hipStream_t s) {
-  const int64_t loads = (K / kTileCols + 3) / 4;
+hipError_t launch_m(const GemvArgs& a, hipStream_t s) {
+  const int64_t loads = (a.K / kTileCols + 3) / 4;
 #define BL_GEMV_CASE(n) \
-  if (loads <= n) return launch_one<M, DT, n>(X, K, N, packed, gamma, Y, relu2, xq, xs, acc, s);
+  if (loads <= n) return launch_one<M, DT, n>(a, s);
   BL_GEMV_CASE(1)
   BL_GEMV_CASE(2)
   BL_GEMV_CASE(3)
@@ -149,14 +172,12 @@ hipError_t launch_m(const void* X, int64_t K, int64_t N, const uint8_t* packed,
 }
 
 template <int DT>
-hipError_t launch_dt(const void* X, int64_t M, int64_t K, int64_t N, const uint8_t* packed,
-                     const float* gamma, float* Y, bool relu2, int8_t* xq, float* xs,
-                     int32_t* acc, hipStream_t s) {
+hipError_t launch_dt(int64_t M, const GemvArgs& a, hipStream_t s) {
   switch (M) {
-    case 1: return launch_m<1, DT>(X, K, N, packed, gamma, Y, relu2, xq, xs, acc, s);
-    case 2: return launch_m<2, DT>(X, K, N, packed, gamma, Y, relu2, xq, xs, acc, s);
-    case 3: return launch_m<3, DT>(X, K, N, packed, gamma, Y, relu2, xq, xs, acc, s);
-    case 4: return launch_m<4, DT>(X, K, N, packed, gamma, Y, relu2, xq, xs, acc, s);
+    case 1: return launch_m<1, DT>(a, s);
+    case 2: return launch_m<2, DT>(a, s);
+    case 3: return launch_m<3, DT>(a, s);
+    case 4: return launch_m<4, DT>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -170,8 +191,9 @@ bool bl_gemv_supports(int64_t M, int64_t K) {
 
 hipError_t bl_launch_gemv(const void* X, int dtype, int64_t M, int64_t K, int64_t N,
                           const uint8_t* packed, const float* gamma, float* Y, bool relu2,
-                          int8_t* xq_out, float* xscale_out, int32_t* acc_out, hipStream_t s) {
-  if (dtype == 1)
-    return launch_dt<1>(X, M, K, N, packed, gamma, Y, relu2, xq_out, xscale_out, acc_out, s);
-  return launch_dt<0>(X, M, K, N, packed, gamma, Y, relu2, xq_out, xscale_out, acc_out, s);
+                          int8_t* xq_out, float* xscale_out, int32_t* acc_out, hipStream_t s,
+                          const float* norm_gain, float norm_eps) {
+  const GemvArgs a{X, K, N, packed, gamma, Y, relu2, xq_out, xscale_out, acc_out, norm_gain,
+                   norm_eps};
+  return dtype == 1 ? launch_dt<1>(M, a, s) : launch_dt<0>(M, a, s);
 }

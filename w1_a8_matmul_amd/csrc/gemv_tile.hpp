@@ -65,12 +65,38 @@ __device__ __forceinline__ void widen(const Chunk<DT>& c, float v[8]) {
   }
 }
 
+// subln gains (float [K]) of the columns this thread's activation chunks
+// cover, loaded with the activation row so that waiting for them never
+// waits for the weight loads issued after it.  Gains past K read as zero.
+template <int NT, int KCH>
+struct Gains {
+  uint4 lo[KCH], hi[KCH];
+};
+
+template <int NT, int KCH>
+__device__ __forceinline__ void load_gains(const float* __restrict__ g, int K,
+                                           Gains<NT, KCH>& gn) {
+  const auto r = make_rsrc(g, g ? (uint32_t)K * 4u : 0u);
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    const uint32_t off = (threadIdx.x + c * NT) * 32u;
+    gn.lo[c] = buf_load16(r, off, 0);
+    gn.hi[c] = buf_load16(r, off + 16, 0);
+  }
+}
+
 // Quantizes one row held in registers into xs[0..K); the scale and row sum
-// go to s_scale / s_rowsum.  All NT threads take part.
-template <int DT, int NT, int KCH>
+// go to s_scale / s_rowsum.  All NT threads take part.  With NORM and
+// gain_on, subln first: the codes are those of u = x * g and the scale
+// carries the row's RMS factor (from the double sum of x^2; red_d holds
+// NT/64 doubles of LDS).
+template <int DT, int NT, int KCH, bool NORM = false>
 __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int8_t* xs,
                                              float* red_f, int* red_i, float* s_scale,
-                                             int* s_rowsum) {
+                                             int* s_rowsum,
+                                             const Gains<NT, KCH>* gn = nullptr,
+                                             bool gain_on = false, float eps = 0.0f,
+                                             double* red_d = nullptr) {
   constexpr int W = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Every chunk is used unconditionally (chunks past the row are zeros and
@@ -78,18 +104,41 @@ __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int
   // were issued instead of sinking them past the weight loads.
   float v[KCH][8];
   float amax = 0.0f;
+  double ss = 0.0;
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
     widen<DT>(ch[c], v[c]);
+    if constexpr (NORM) {
+      const float gv[8] = {__uint_as_float(gn->lo[c].x), __uint_as_float(gn->lo[c].y),
+                           __uint_as_float(gn->lo[c].z), __uint_as_float(gn->lo[c].w),
+                           __uint_as_float(gn->hi[c].x), __uint_as_float(gn->hi[c].y),
+                           __uint_as_float(gn->hi[c].z), __uint_as_float(gn->hi[c].w)};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ss += (double)v[c][i] * (double)v[c][i];
+        if (gain_on) v[c][i] = v[c][i] * gv[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
   }
   amax = wave_max(amax);
-  if (lane == 0) red_f[wave] = amax;
+  if constexpr (NORM) ss = wave_sum_f64(ss);
+  if (lane == 0) {
+    red_f[wave] = amax;
+    if constexpr (NORM) red_d[wave] = ss;
+  }
   __syncthreads();
   float a = red_f[0];
 #pragma unroll
   for (int w = 1; w < W; ++w) a = fmaxf(a, red_f[w]);
+  float rfac = 1.0f;
+  if constexpr (NORM) {
+    double S = red_d[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) S += red_d[w];
+    if (gain_on) rfac = rms_factor(S, K, eps);
+  }
   const float a_c = a > kEps ? a : kEps;
   const float qs = kQmax / a_c;
   int sum = 0;
@@ -117,7 +166,8 @@ __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int
     int t = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) t += red_i[w];
-    *s_scale = a_c / kQmax;
+    const float sc = a_c / kQmax;
+    *s_scale = NORM && gain_on ? sc * rfac : sc;
     *s_rowsum = t;
   }
 }

@@ -54,6 +54,7 @@ template <int NT>
 struct Smem {
   float red_f[NT / kWave];
   int red_i[NT / kWave];
+  double red_d[NT / kWave];
 };
 
 // One layer segment: tiles first, first+stride, ... < last of layer o for
@@ -62,7 +63,9 @@ struct Smem {
 // buffer range and read zeros.
 // PREQ: the activations were quantized by the separate launch; the
 // segment copies its layer's int8 rows, scales and row sums into LDS instead.
-template <int NT, int KCH, int DT, bool PREQ>
+// NORM (inline quantization only): layers with a subln gain get it applied
+// before their quantization.
+template <int NT, int KCH, int DT, bool PREQ, bool NORM>
 __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, int last,
                                             bool quantize, int8_t* xs, int xstride,
                                             float* s_sx, int* s_rs, float* s_y, Smem<NT>& sm,
@@ -144,13 +147,18 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   } else if (quantize) {
     Chunk<DT> ch[KCH];
     load_row<DT, kThreads, KCH>(o.X, 0, K, ch);
+    Gains<kThreads, KCH> gn;
+    if constexpr (NORM) load_gains<kThreads, KCH>(o.norm_gain, K, gn);
+    const bool gain_on = NORM && o.norm_gain != nullptr;
     issue(bufA, 0, qi);
-    quantize_row<DT, kThreads, KCH>(ch, K, xs, sm.red_f, sm.red_i, s_sx, s_rs);
+    quantize_row<DT, kThreads, KCH, NORM>(ch, K, xs, sm.red_f, sm.red_i, s_sx, s_rs, &gn,
+                                          gain_on, o.norm_eps, sm.red_d);
     for (int m = 1; m < M; ++m) {
       Chunk<DT> chm[KCH];
       load_row<DT, kThreads, KCH>(o.X, m, K, chm);
-      quantize_row<DT, kThreads, KCH>(chm, K, xs + m * xstride, sm.red_f, sm.red_i, s_sx + m,
-                                      s_rs + m);
+      quantize_row<DT, kThreads, KCH, NORM>(chm, K, xs + m * xstride, sm.red_f, sm.red_i,
+                                            s_sx + m, s_rs + m, &gn, gain_on, o.norm_eps,
+                                            sm.red_d);
     }
   } else {
     issue(bufA, 0, qi);
@@ -235,7 +243,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
 // counts the workgroups that found the queue empty; the last of them puts
 // both back to zero for the next launch.  A layer's int8 activations are
 // quantized (or copied) whenever a workgroup moves to a new layer.
-template <int NT, int KCH, bool PREQ>
+template <int NT, int KCH, bool PREQ, bool NORM>
 __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops, int n_ops,
                                                    int M, int max_k,
                                                    const int* __restrict__ wg_begin,
@@ -263,13 +271,13 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
     const GroupOp o = ops[op];
     const bool quantize = quantized_op != op;
     if (PREQ)
-      run_segment<NT, KCH, 0, true>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+      run_segment<NT, KCH, 0, true, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
                                     sm, xq, sx, rs, op, wave, lane);
     else if (o.dtype == 1)
-      run_segment<NT, KCH, 1, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+      run_segment<NT, KCH, 1, false, NORM>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
                                      sm, xq, sx, rs, op, wave, lane);
     else
-      run_segment<NT, KCH, 0, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+      run_segment<NT, KCH, 0, false, NORM>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
                                      sm, xq, sx, rs, op, wave, lane);
     __syncthreads();  // before the next segment overwrites xs, the scales, s_y or s_unit
     quantized_op = op;
@@ -314,12 +322,20 @@ __global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restr
                                                           int* __restrict__ rs) {
   __shared__ float red_f[4];
   __shared__ int red_i[4];
+  __shared__ double red_d[4];
   const int op = blockIdx.x / M, m = blockIdx.x % M;
   const GroupOp o = ops[op];
   int8_t* dst = xq + o.xq_off + (int64_t)m * o.K;
+  const float* g = o.norm_gain;
   RowQuant q;
   int sum;
-  if (o.dtype == 1) {
+  if (g && o.dtype == 1) {
+    q = row_absmax_scale<1, 256, true>(o.X, m, o.K, red_f, g, o.norm_eps, red_d);
+    sum = row_quantize_to<1, 256, true>(o.X, m, o.K, q.qs, dst, red_i, g);
+  } else if (g) {
+    q = row_absmax_scale<0, 256, true>(o.X, m, o.K, red_f, g, o.norm_eps, red_d);
+    sum = row_quantize_to<0, 256, true>(o.X, m, o.K, q.qs, dst, red_i, g);
+  } else if (o.dtype == 1) {
     q = row_absmax_scale<1, 256>(o.X, m, o.K, red_f);
     sum = row_quantize_to<1, 256>(o.X, m, o.K, q.qs, dst, red_i);
   } else {
@@ -327,43 +343,69 @@ __global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restr
     sum = row_quantize_to<0, 256>(o.X, m, o.K, q.qs, dst, red_i);
   }
   if (threadIdx.x == 0) {
-    sx[op * M + m] = q.a_c / kQmax;
+    const float sc = q.a_c / kQmax;
+    sx[op * M + m] = g ? sc * q.r : sc;
     rs[op * M + m] = sum;
   }
 }
 
 // Activation chunks per thread: each covers NT * 8 elements of a row.
-template <int NT, bool PREQ>
+// Kernel modes: pre-quantized (the quantization launch applies any subln);
+// inline quantization without or with subln gains.
+template <int NT, bool PREQ, bool NORM>
 const void* kernel_for(int max_k) {
-  if (max_k <= NT * 8 * 2) return reinterpret_cast<const void*>(&group_kernel<NT, 2, PREQ>);
-  if (max_k <= NT * 8 * 4) return reinterpret_cast<const void*>(&group_kernel<NT, 4, PREQ>);
-  return reinterpret_cast<const void*>(&group_kernel<NT, 6, PREQ>);
+  if (max_k <= NT * 8 * 2)
+    return reinterpret_cast<const void*>(&group_kernel<NT, 2, PREQ, NORM>);
+  if (max_k <= NT * 8 * 4)
+    return reinterpret_cast<const void*>(&group_kernel<NT, 4, PREQ, NORM>);
+  return reinterpret_cast<const void*>(&group_kernel<NT, 6, PREQ, NORM>);
 }
 
-const void* kernel_for(int threads, bool preq, int max_k) {
-  if (threads == 512) return preq ? kernel_for<512, true>(max_k) : kernel_for<512, false>(max_k);
-  return preq ? kernel_for<256, true>(max_k) : kernel_for<256, false>(max_k);
+template <int NT>
+const void* kernel_for(bool preq, bool norm, int max_k) {
+  if (preq) return kernel_for<NT, true, false>(max_k);
+  return norm ? kernel_for<NT, false, true>(max_k) : kernel_for<NT, false, false>(max_k);
 }
 
-template <int NT, bool PREQ>
+const void* kernel_for(int threads, bool preq, bool norm, int max_k) {
+  return threads == 512 ? kernel_for<512>(preq, norm, max_k)
+                        : kernel_for<256>(preq, norm, max_k);
+}
+
+template <int NT, bool PREQ, bool NORM>
 void launch(const GroupOp* ops, int n_ops, int M, const int* wg_begin, const GroupUnit* units,
             int n_units, int* queue, int G, int max_k, size_t lds, const int8_t* xq,
             const float* sx, const int* rs, hipStream_t s) {
   if (max_k <= NT * 8 * 2)
-    hipLaunchKernelGGL((group_kernel<NT, 2, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
-                       max_k, wg_begin, units, n_units, queue, xq, sx, rs);
+    hipLaunchKernelGGL((group_kernel<NT, 2, PREQ, NORM>), dim3(G), dim3(NT), lds, s, ops,
+                       n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else if (max_k <= NT * 8 * 4)
-    hipLaunchKernelGGL((group_kernel<NT, 4, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
-                       max_k, wg_begin, units, n_units, queue, xq, sx, rs);
+    hipLaunchKernelGGL((group_kernel<NT, 4, PREQ, NORM>), dim3(G), dim3(NT), lds, s, ops,
+                       n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else
-    hipLaunchKernelGGL((group_kernel<NT, 6, PREQ>), dim3(G), dim3(NT), lds, s, ops, n_ops, M,
-                       max_k, wg_begin, units, n_units, queue, xq, sx, rs);
+    hipLaunchKernelGGL((group_kernel<NT, 6, PREQ, NORM>), dim3(G), dim3(NT), lds, s, ops,
+                       n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
 }
 
-int blocks_per_cu(int threads, bool preq, size_t lds, int max_k) {
+template <int NT>
+void launch(bool preq, bool norm, const GroupOp* ops, int n_ops, int M, const int* wg_begin,
+            const GroupUnit* units, int n_units, int* queue, int G, int max_k, size_t lds,
+            const int8_t* xq, const float* sx, const int* rs, hipStream_t s) {
+  if (preq)
+    launch<NT, true, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                            sx, rs, s);
+  else if (norm)
+    launch<NT, false, true>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                            sx, rs, s);
+  else
+    launch<NT, false, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                             sx, rs, s);
+}
+
+int blocks_per_cu(int threads, bool preq, bool norm, size_t lds, int max_k) {
   int blocks = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks, kernel_for(threads, preq, max_k), threads, lds);
+      &blocks, kernel_for(threads, preq, norm, max_k), threads, lds);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
@@ -382,33 +424,35 @@ size_t bl_group_lds_bytes(int M, int max_k) {
   return (size_t)M * (size_t)(max_k + 16) + (size_t)M * kSegTiles * kTileRows * sizeof(float);
 }
 
-hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu) {
+hipError_t bl_group_plan(int M, int max_k, bool norm, int* threads, int* per_cu) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
   const bool preq = bl_group_prequantizes(M);
   for (int nt : {256, 512}) {
     if (lds > 64 * 1024) {
-      const hipError_t e = hipFuncSetAttribute(
-          kernel_for(nt, preq, max_k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      const hipError_t e =
+          hipFuncSetAttribute(kernel_for(nt, preq, norm, max_k),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
   }
   // Four-wave workgroups while at least two fit on a compute unit (more,
   // shorter weight streams); eight-wave ones when the activations take so
   // much LDS that only one does.
-  const int b256 = blocks_per_cu(256, preq, lds, max_k);
+  const int b256 = blocks_per_cu(256, preq, norm, lds, max_k);
   if (b256 >= 2) {
     *threads = 256;
     *per_cu = b256;
   } else {
     *threads = 512;
-    *per_cu = blocks_per_cu(512, preq, lds, max_k);
+    *per_cu = blocks_per_cu(512, preq, norm, lds, max_k);
   }
   return hipSuccess;
 }
 
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin,
                            const GroupUnit* units, int n_units, int* queue, int G, int max_k,
-                           int threads, int8_t* xq, float* sx, int* rs, hipStream_t s) {
+                           int threads, bool norm, int8_t* xq, float* sx, int* rs,
+                           hipStream_t s) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
   const bool preq = bl_group_prequantizes(M);
   if (preq) {
@@ -416,14 +460,10 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
     if (e != hipSuccess) return e;
   }
   if (threads == 512)
-    preq ? launch<512, true>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                             sx, rs, s)
-         : launch<512, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                              sx, rs, s);
+    launch<512>(preq, norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                sx, rs, s);
   else
-    preq ? launch<256, true>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                             sx, rs, s)
-         : launch<256, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                              sx, rs, s);
+    launch<256>(preq, norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                sx, rs, s);
   return hipGetLastError();
 }

@@ -1,4 +1,4 @@
-// Device descriptor of one layer in a grouped decode forward (64 bytes),
+// Device descriptor of one layer in a grouped decode forward (80 bytes),
 // shared by the ABI layer (which fills the table) and the kernel.
 #pragma once
 
@@ -6,17 +6,19 @@
 #include <stdint.h>
 
 struct GroupOp {
-  const void* X;          // [M][K] activations (float or bf16)
-  const uint8_t* packed;  // packed ternary weights, [N/16][K/256] tiles of 1 KiB
-  const float* gamma;     // gamma_c (one float)
-  float* Y;               // [M][N] output
-  int64_t xq_off;         // byte offset of this layer's int8 [M][K] in the workspace
+  const void* X;           // [M][K] activations (float or bf16)
+  const uint8_t* packed;   // packed ternary weights, [N/16][K/256] tiles of 1 KiB
+  const float* gamma;      // gamma_c (one float)
+  float* Y;                // [M][N] output
+  const float* norm_gain;  // subln gain [K] before the quantization, or null
+  int64_t xq_off;          // byte offset of this layer's int8 [M][K] in the workspace
   int32_t K, N;
   int32_t dtype, relu2;
-  int32_t item_begin;     // index of this layer's first 16-row tile in the flat list
-  int32_t pad;
+  int32_t item_begin;      // index of this layer's first 16-row tile in the flat list
+  float norm_eps;          // subln epsilon
+  int32_t pad[2];
 };
-static_assert(sizeof(GroupOp) == 64, "GroupOp must stay 64 bytes");
+static_assert(sizeof(GroupOp) == 80, "GroupOp must stay 80 bytes");
 
 // A unit of grouped work: tiles first..end-1 (indices into the concatenation
 // of every layer's 16-row tiles) of layer op.
@@ -57,17 +59,18 @@ size_t bl_group_lds_bytes(int M, int max_k);
 
 // Chooses the workgroup size (256 or 512 threads) and reports how many
 // workgroups fit on one compute unit; also allows the kernel the dynamic
-// LDS it needs.
-hipError_t bl_group_plan(int M, int max_k, int* threads, int* per_cu);
+// LDS it needs.  norm: some layer has a subln gain.
+hipError_t bl_group_plan(int M, int max_k, bool norm, int* threads, int* per_cu);
 
 // Grouped forward: G workgroups of `threads` threads; workgroup g first runs
 // tiles wg_begin[g] .. wg_begin[g+1]-1, then takes the n_units units from the
 // queue (two ints, zero on entry and left zero); max_k the largest K.  xq,
 // sx, rs: the quantized activations, scales and row sums (used when
-// bl_group_prequantizes(M)).
+// bl_group_prequantizes(M)); norm as for bl_group_plan.
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin,
                            const GroupUnit* units, int n_units, int* queue, int G, int max_k,
-                           int threads, int8_t* xq, float* sx, int* rs, hipStream_t s);
+                           int threads, bool norm, int8_t* xq, float* sx, int* rs,
+                           hipStream_t s);
 
 // Above kGroupMaxM tokens a group runs as one persistent tiled int8 GEMM over
 // the output tiles of all its layers (activations quantized beforehand).

@@ -8,8 +8,9 @@
 namespace bl {
 
 struct RowQuant {
-  float a_c;  // max(max_k |x|, eps)
+  float a_c;  // max(max_k |u|, eps), u = x (or x * g with subln)
   float qs;   // 127 / a_c
+  float r;    // subln's RMS factor of the row (1 without subln)
 };
 
 // Eight consecutive activations as floats (bf16 is widened exactly).
@@ -31,39 +32,73 @@ __device__ __forceinline__ void load8(const void* __restrict__ X, int64_t idx, f
   }
 }
 
-// max |x| over row m with NT threads; red has NT/64 floats of LDS.
-template <int DT, int NT>
+// max |u| over row m with NT threads; red has NT/64 floats of LDS.  With
+// NORM (subln, an RMSNorm with gain g and epsilon eps): u = x * g, and the
+// row's RMS factor from the double sum of x^2 (red_d: NT/64 doubles of LDS).
+// Absmax quantization cannot see the factor, so it only scales s_x.
+template <int DT, int NT, bool NORM = false>
 __device__ __forceinline__ RowQuant row_absmax_scale(const void* __restrict__ X, int64_t m,
-                                                     int64_t K, float* red) {
+                                                     int64_t K, float* red,
+                                                     const float* __restrict__ g = nullptr,
+                                                     float eps = 0.0f,
+                                                     double* red_d = nullptr) {
   float amax = 0.0f;
+  double ss = 0.0;
   for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += NT * 8) {
     float v[8];
     load8<DT>(X, m * K + k, v);
+    if constexpr (NORM) {
+      float gv[8];
+      load8<0>(g, k, gv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ss += (double)v[i] * (double)v[i];
+        v[i] = v[i] * gv[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
   amax = wave_max(amax);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  if constexpr (NORM) ss = wave_sum_f64(ss);
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6] = amax;
+    if constexpr (NORM) red_d[threadIdx.x >> 6] = ss;
+  }
   __syncthreads();
   float a = red[0];
 #pragma unroll
   for (int w = 1; w < NT / 64; ++w) a = fmaxf(a, red[w]);
-  __syncthreads();
   RowQuant r;
+  r.r = 1.0f;
+  if constexpr (NORM) {
+    double S = red_d[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) S += red_d[w];
+    r.r = rms_factor(S, K, eps);
+  }
+  __syncthreads();
   r.a_c = a > kEps ? a : kEps;
   r.qs = kQmax / r.a_c;
   return r;
 }
 
-// Writes the int8 codes of row m to dst[0..K) and returns their sum (in
-// every thread).  red has NT/64 ints of LDS.
-template <int DT, int NT>
+// Writes the int8 codes of row m (of u = x, or x * g with NORM) to dst[0..K)
+// and returns their sum (in every thread).  red has NT/64 ints of LDS.
+template <int DT, int NT, bool NORM = false>
 __device__ __forceinline__ int row_quantize_to(const void* __restrict__ X, int64_t m, int64_t K,
-                                               float qs, int8_t* dst, int* red) {
+                                               float qs, int8_t* dst, int* red,
+                                               const float* __restrict__ g = nullptr) {
   int sum = 0;
   for (int64_t k = (int64_t)threadIdx.x * 8; k < K; k += NT * 8) {
     float v[8];
     load8<DT>(X, m * K + k, v);
+    if constexpr (NORM) {
+      float gv[8];
+      load8<0>(g, k, gv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * gv[i];
+    }
     uint32_t lo = 0, hi = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

@@ -137,6 +137,13 @@ def gen_acts_f32(seed: int, M: int, K: int, kind: str) -> np.ndarray:
     raise ValueError(f"unknown activation kind {kind!r}")
 
 
+def gen_gain(seed: int, K: int) -> np.ndarray:
+    """float32 [K] subln gains, uniform on [0.5, 1.5) (a trained norm's gains
+    sit around 1; the spread makes every feature's gain matter)."""
+    rng = np.random.default_rng(seed)
+    return rng.uniform(0.5, 1.5, K).astype(np.float32)
+
+
 def to_bf16_bits(X: np.ndarray) -> np.ndarray:
     """Round float32 to bf16 (nearest even, via torch) and return uint16 bits."""
     import torch
