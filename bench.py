@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-launches", type=int, default=400,
                    help="launches of the dominant kernel timed for the roofline")
+    p.add_argument("--subln", action="store_true",
+                   help="give every linear a subln gain (RMSNorm fused into its quantization)")
     p.add_argument("--grouped", action="store_true",
                    help="run all linears of a step as one grouped forward (M <= 4)")
     p.add_argument("--probes", action="store_true",
@@ -78,7 +80,7 @@ def parse():
 # Workload runners: allocate everything up front; step(i) only launches.
 # ---------------------------------------------------------------------------
 class Linear:
-    def __init__(self, bl, torch, dev, N, K, M, x_dtype, seed, sparse, copies):
+    def __init__(self, bl, torch, dev, N, K, M, x_dtype, seed, sparse, copies, subln=False):
         self.N, self.K, self.M = N, K, M
         gen = torch.Generator(device=dev)
         self.packed, self.gamma = [], []
@@ -99,13 +101,18 @@ class Linear:
         X = torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32)
         self.X = X.to(x_dtype) if x_dtype is not None else X
         self.Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        self.gain = None
+        if subln:  # gains uniform on [0.5, 1.5)
+            gen.manual_seed(seed * 131 + 8888)
+            self.gain = torch.rand(K, generator=gen, device=dev, dtype=torch.float32) + 0.5
         ws = bl.workspace_bytes(M, K, N)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev) if ws > 0 else None
 
     def bytes(self):
-        """Algorithmic bytes of one forward: packed W + X in + Y out + gamma."""
+        """Algorithmic bytes of one forward: packed W + X in + Y out + gamma
+        (+ the subln gain)."""
         return (self.N * self.K // 4 + self.X.numel() * self.X.element_size()
-                + self.Y.numel() * 4 + 4)
+                + self.Y.numel() * 4 + 4 + (self.K * 4 if self.gain is not None else 0))
 
     def ops(self):
         return 2 * self.M * self.N * self.K
@@ -124,7 +131,8 @@ def build_runner(args, bl, torch, wl, dev):
     lins = []
     for layer, li, shape in wl.step_linears(wk):
         lins.append(Linear(bl, torch, dev, shape.N, shape.K, M, x_dtype,
-                           wl.weight_seed(wk.key, layer, li), wk.weight_sparse_frac, copies))
+                           wl.weight_seed(wk.key, layer, li), wk.weight_sparse_frac, copies,
+                           subln=args.subln))
     if wk.chain_relu2:
         # up (ReLU^2) feeds down: down's input is up's float output
         up, down = lins
@@ -134,7 +142,8 @@ def build_runner(args, bl, torch, wl, dev):
     if args.grouped:
         if wk.chain_relu2:
             raise SystemExit("--grouped needs independent linears")
-        groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, None, l.Y) for l in lins])
+        groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, None, l.Y, l.gain)
+                            for l in lins])
                   for c in range(copies)]
 
     def step(i):
@@ -145,13 +154,13 @@ def build_runner(args, bl, torch, wl, dev):
         if wk.chain_relu2:
             up, down = lins
             bl.forward(up.X, up.packed[c], up.gamma[c], up.N, epilogue="relu2", out=up.Y,
-                       workspace=up.ws)
+                       workspace=up.ws, norm_gain=up.gain)
             bl.forward(down.X, down.packed[c], down.gamma[c], down.N, out=down.Y,
-                       workspace=down.ws)
+                       workspace=down.ws, norm_gain=down.gain)
         else:
             for lin in lins:
                 bl.forward(lin.X, lin.packed[c], lin.gamma[c], lin.N, out=lin.Y,
-                           workspace=lin.ws)
+                           workspace=lin.ws, norm_gain=lin.gain)
 
     return wk, M, lins, copies, step, groups
 
@@ -195,7 +204,7 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
         # The GEMM launch alone, from activations quantized beforehand (the
         # forward's other launch, the per-token quantization, is not the
         # contraction being measured).
-        Xq, sx, rs = bl.quantize_acts(dom.X)
+        Xq, sx, rs = bl.quantize_acts(dom.X, norm_gain=dom.gain)
         qws = bl.forward_q_workspace(dom.M, dom.K, dom.N, dom.X.device)
 
     def dom_step(i):
@@ -205,7 +214,7 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
                          out=dom.Y, workspace=qws)
         else:
             bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
-                       workspace=dom.ws)
+                       workspace=dom.ws, norm_gain=dom.gain)
 
     us = time_graph(torch, dom_step, n)
     if metric_kind == "tops":
@@ -257,7 +266,7 @@ def roofline_grouped(args, torch, step, bytes_step, ops_step, wk, M, n_lin, metr
 # ---------------------------------------------------------------------------
 # CPU oracle baseline (bounded sample)
 # ---------------------------------------------------------------------------
-def cpu_baseline(args, wk, M, lins_shapes, metric_kind, budget_s):
+def cpu_baseline(args, wk, M, lins_shapes, metric_kind, budget_s, subln=False):
     import numpy as np
 
     import oracle
@@ -275,17 +284,24 @@ def cpu_baseline(args, wk, M, lins_shapes, metric_kind, budget_s):
         _, gc, qw = orc.quantize_weights(W)
         del W
         X, is_bf16 = wl.gen_acts(rng_seed + 100 + li, Ms, lin.K, wk.x_kind)
-        prepared.append((lin, qw, gc, X, is_bf16))
+        g = wl.gen_gain(rng_seed + 200 + li, lin.K) if subln else None
+        prepared.append((lin, qw, gc, X, is_bf16, g))
+
+    def fwd(X, qw, gc, bf16, g):
+        if g is None:
+            y, *_ = orc.forward(X, qw, gc, bf16=bf16)
+            return y
+        q, s, _ = orc.quant_acts_rmsnorm(X, g, 1e-5, bf16=bf16)
+        return orc.rescale(orc.int_matmul(q, qw), s, gc)
 
     def one_pass():
         if wk.chain_relu2:
-            (lu, qu, gu, Xu, bu), (ld, qd, gd, _, _) = prepared
-            y, *_ = orc.forward(Xu, qu, gu, bf16=bu)
-            h = orc.relu2(y)
-            orc.forward(h, qd, gd)
+            (lu, qu, gu, Xu, bu, guu), (ld, qd, gd, _, _, gdd) = prepared
+            h = orc.relu2(fwd(Xu, qu, gu, bu, guu))
+            fwd(h, qd, gd, False, gdd)
         else:
-            for lin, qw, gc, X, is_bf16 in prepared:
-                orc.forward(X, qw, gc, bf16=is_bf16)
+            for lin, qw, gc, X, is_bf16, g in prepared:
+                fwd(X, qw, gc, is_bf16, g)
 
     one_pass()
     n = 0
@@ -298,8 +314,10 @@ def cpu_baseline(args, wk, M, lins_shapes, metric_kind, budget_s):
             break
     per_pass = el / n
     layer_bytes = sum(lin.N * lin.K // 4 + Ms * lin.K * (2 if is_bf16 else 4) + Ms * lin.N * 4 + 4
-                      for lin, _, _, _, is_bf16 in prepared)
+                      for lin, _, _, _, is_bf16, _ in prepared)
     layer_ops = sum(2 * Ms * lin.N * lin.K for lin, *_ in prepared)
+    if subln:
+        layer_bytes += sum(lin.K * 4 for lin, *_ in prepared)
     if metric_kind == "tops":
         value, unit = layer_ops / per_pass / 1e12, "TOPS"
     else:
@@ -488,7 +506,8 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(args, wk, M, wk.linears, metric_kind, args.cpu_seconds)
+        cpu = cpu_baseline(args, wk, M, wk.linears, metric_kind, args.cpu_seconds,
+                           subln=args.subln)
         log(f"cpu oracle: {cpu}")
 
     out = {
@@ -516,6 +535,7 @@ def main():
             "gpu_event_ms_per_step": round(gpu_ms / args.steps, 6),
             "offline_weight_quant_ms": round(quant_s * 1e3 / copies, 3),
             "grouped": groups is not None,
+            "subln": bool(args.subln),
         },
         "roofline": roof,
         "cpu_baseline": cpu,

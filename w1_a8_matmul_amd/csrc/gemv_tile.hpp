@@ -115,7 +115,7 @@ __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int
                            __uint_as_float(gn->hi[c].z), __uint_as_float(gn->hi[c].w)};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ss += (double)v[c][i] * (double)v[c][i];
+        ss = __builtin_fma((double)v[c][i], (double)v[c][i], ss);  // exact square: one rounding
         if (gain_on) v[c][i] = v[c][i] * gv[i];
       }
     }
@@ -123,22 +123,11 @@ __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
   }
   amax = wave_max(amax);
-  if constexpr (NORM) ss = wave_sum_f64(ss);
-  if (lane == 0) {
-    red_f[wave] = amax;
-    if constexpr (NORM) red_d[wave] = ss;
-  }
+  if (lane == 0) red_f[wave] = amax;
   __syncthreads();
   float a = red_f[0];
 #pragma unroll
   for (int w = 1; w < W; ++w) a = fmaxf(a, red_f[w]);
-  float rfac = 1.0f;
-  if constexpr (NORM) {
-    double S = red_d[0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) S += red_d[w];
-    if (gain_on) rfac = rms_factor(S, K, eps);
-  }
   const float a_c = a > kEps ? a : kEps;
   const float qs = kQmax / a_c;
   int sum = 0;
@@ -160,13 +149,25 @@ __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int
     }
   }
   sum = wave_sum(sum);
-  if (lane == 0) red_i[wave] = sum;
+  // The sum of squares is needed only for the scale: reduced after the codes.
+  if constexpr (NORM) ss = wave_sum_f64(ss);
+  if (lane == 0) {
+    red_i[wave] = sum;
+    if constexpr (NORM) red_d[wave] = ss;
+  }
   __syncthreads();  // also keeps the next row's red_f write after the reads above
   if (tid == 0) {
     int t = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) t += red_i[w];
     const float sc = a_c / kQmax;
+    float rfac = 1.0f;
+    if constexpr (NORM) {
+      double S = red_d[0];
+#pragma unroll
+      for (int w = 1; w < W; ++w) S += red_d[w];
+      if (gain_on) rfac = rms_factor(S, K, eps);
+    }
     *s_scale = NORM && gain_on ? sc * rfac : sc;
     *s_rowsum = t;
   }

@@ -52,7 +52,7 @@ __device__ __forceinline__ RowQuant row_absmax_scale(const void* __restrict__ X,
       load8<0>(g, k, gv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ss += (double)v[i] * (double)v[i];
+        ss = __builtin_fma((double)v[i], (double)v[i], ss);  // exact square: one rounding
         v[i] = v[i] * gv[i];
       }
     }
