@@ -81,6 +81,9 @@ class Oracle:
         lib.oracle_int_dot_samples.argtypes = [_p, _p, _i64, _p, _p, _i64, _p]
         lib.oracle_rescale.argtypes = [_p, _p, ctypes.c_float, _i64, _i64, _p]
         lib.oracle_relu2.argtypes = [_p, _i64, _p]
+        lib.oracle_pack_glu.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_pack_glu.restype = ctypes.c_int
+        lib.oracle_glu_relu2.argtypes = [_p, _i64, _i64, _p]
         lib.oracle_forward.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p,
                                        ctypes.c_float, _p, _p, _p, _p]
         lib.oracle_forward.restype = ctypes.c_int
@@ -151,6 +154,25 @@ class Oracle:
         fn = self.lib.oracle_quant_acts_bf16 if bf16 else self.lib.oracle_quant_acts_f32
         fn(_ptr(X), M, K, _ptr(q), _ptr(s), _ptr(r))
         return q, s, r
+
+    # -- R12: gated squared ReLU of a fused gate+up matrix ------------------
+    def pack_glu(self, q: np.ndarray) -> np.ndarray:
+        """Packs q [N][K] (gate rows, then up rows) with the halves interleaved
+        per 16-row tile: tile t = gate rows 8t..8t+7, up rows F+8t..F+8t+7."""
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        N, K = q.shape
+        out = np.empty(self.packed_bytes(N, K), np.uint8)
+        if self.lib.oracle_pack_glu(_ptr(q), N, K, _ptr(out)) != 0:
+            raise ValueError("bad shape or non-ternary value")
+        return out
+
+    def glu_relu2(self, y: np.ndarray) -> np.ndarray:
+        """h [M][N/2] = max(y_gate, 0)^2 * y_up for y [M][N] = [gate | up]."""
+        y = np.ascontiguousarray(y, dtype=np.float32)
+        M, N = y.shape
+        h = np.empty((M, N // 2), np.float32)
+        self.lib.oracle_glu_relu2(_ptr(y), M, N, _ptr(h))
+        return h
 
     # -- R8: subln (RMSNorm with gain) before the absmax quantization --------
     def quant_acts_rmsnorm(self, X: np.ndarray, g: np.ndarray, eps: float = 1e-5,

@@ -44,6 +44,13 @@
  *                scale only: s_x = (float)(s_x(u) * r).  The sum of squares is
  *                taken in double in index order; r = (float)(1 / sqrt(S / K +
  *                eps_n)) in double.  The 1e-5 guard of R4 applies to u.
+ *   R12 gated FFN = the workload's fused gate+up matrix [N][K] holds the gate
+ *                rows 0..F-1 and the up rows F..2F-1 (F = N/2), with one gamma;
+ *                h = (r * r) * y_up, r = max(y_gate, 0), left to right, float,
+ *                no fused multiply-add; h is [M][F].  The pages give ReLU^2 as
+ *                the FFN activation and no formula for the gating.  The packed
+ *                layout of such a matrix interleaves the halves: 16-row tile t
+ *                holds gate rows 8t..8t+7, then up rows F+8t..F+8t+7.
  *
  * All float arithmetic here is IEEE binary32/binary64 with round-to-nearest-
  * even; the file must be compiled without fast-math and with
@@ -309,6 +316,38 @@ void oracle_relu2(const float* y, int64_t count, float* h) {
   for (i = 0; i < count; ++i) {
     float r = y[i] > 0.0f ? y[i] : 0.0f;
     h[i] = r * r;
+  }
+}
+
+/* R12: the gated squared ReLU of a fused gate+up output, and the packing of
+ * such a matrix ([TR] Method Adaptation; [FA] FFN activation: ReLU^2).     */
+static int64_t glu_source_row(int64_t p, int64_t N) {
+  int64_t t = p / 16, i = p % 16;
+  return i < 8 ? 8 * t + i : N / 2 + 8 * t + (i - 8);
+}
+
+/* Packs q [N][K] (gate rows first) in the interleaved row order; 0, or -1
+ * as oracle_pack.                                                          */
+int oracle_pack_glu(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
+  if (N % 16 != 0 || K % 256 != 0) return -1;
+  int8_t* perm = (int8_t*)malloc((size_t)(N * K > 0 ? N * K : 1));
+  for (int64_t p = 0; p < N; ++p)
+    memcpy(perm + p * K, q + glu_source_row(p, N) * K, (size_t)K);
+  int r = oracle_pack(perm, N, K, packed);
+  free(perm);
+  return r;
+}
+
+void oracle_glu_relu2(const float* y, int64_t M, int64_t N, float* h) {
+  int64_t F = N / 2, m;
+#pragma omp parallel for schedule(static)
+  for (m = 0; m < M; ++m) {
+    for (int64_t f = 0; f < F; ++f) {
+      float g = y[m * N + f];
+      float r = g > 0.0f ? g : 0.0f;
+      float t = r * r;
+      h[m * F + f] = t * y[m * N + F + f];
+    }
   }
 }
 

@@ -44,6 +44,10 @@ MUTANTS = {
     "norm_eps_outside": ("float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));",
                          "float r = (float)(1.0 / (sqrt(S / (double)K) + (double)eps_n));"),
     "norm_scale_missing": ("  *s_x = *s_x * r;", "  (void)r;"),
+    "glu_halves_swapped": ("      float g = y[m * N + f];", "      float g = y[m * N + F + f];"),
+    "glu_not_squared": ("      float t = r * r;", "      float t = r;"),
+    "glu_pack_rows": ("  return i < 8 ? 8 * t + i : N / 2 + 8 * t + (i - 8);",
+                      "  return i < 8 ? 16 * t + i : N / 2 + 8 * t + (i - 8);"),
 }
 
 

@@ -1,6 +1,6 @@
 """Pins of the CPU oracle against facts that do not come from the oracle itself.
 
-Each group of tests names the reading (R1..R8, stated in oracle/bitlinear_oracle.c)
+Each group of tests names the reading (R1..R8 and R12, stated in oracle/bitlinear_oracle.c)
 and what pins it: exact rational arithmetic, closed forms, hand-worked cases
 from tests/golden/, invariants, a library routine, or brute force.  Sources:
 "BitNet b1.58 2B4T Technical Report" card (ai-papers.xuzou.cn), Method
@@ -552,3 +552,38 @@ def test_rmsnorm_bf16_matches_widened_f32(orc):
     qa, sa, ra = orc.quant_acts_rmsnorm(bits, g, 1e-5, bf16=True)
     qb, sb, rb = orc.quant_acts_rmsnorm(widened, g, 1e-5)
     assert np.array_equal(qa, qb) and np.array_equal(sa, sb) and np.array_equal(ra, rb)
+
+
+# --------------------------------------------------------------------------
+# R12: gated squared ReLU of a fused gate+up output, and the interleaved
+# packing of such a matrix.  Pins: the row order of a 32-row matrix worked
+# by hand; hand-computed outputs on small integers (exact in float); the
+# up = 1 case is R7; a non-positive gate gives a zero.
+# --------------------------------------------------------------------------
+def test_glu_pack_row_order_by_hand(orc):
+    N, K = 32, 256
+    q = np.zeros((N, K), np.int8)
+    q[np.arange(N), np.arange(N)] = 1  # row r is marked in column r
+    got = orc.unpack(orc.pack_glu(q), N, K)
+    order = [int(np.argmax(got[r])) for r in range(N)]
+    # tile 0: gate rows 0..7 then up rows 16..23; tile 1: gate 8..15, up 24..31
+    assert order == list(range(0, 8)) + list(range(16, 24)) + list(range(8, 16)) + \
+        list(range(24, 32))
+    q2 = _rng(121).integers(-1, 2, (48, 512)).astype(np.int8)
+    assert np.array_equal(np.sort(orc.unpack(orc.pack_glu(q2), 48, 512), axis=0),
+                          np.sort(q2, axis=0))  # a permutation of whole rows
+
+
+def test_glu_relu2_by_hand(orc):
+    y = np.array([[1, -2, 3, 4, 5, 6, 7, 8],
+                  [-1, 0, 2, -3, 9, -4, -5, 10]], np.float32)
+    h = orc.glu_relu2(y)
+    assert np.array_equal(h, np.array([[5, 0, 63, 128], [0, 0, -20, 0]], np.float32))
+
+
+def test_glu_relu2_unit_up_is_relu2_and_nonpositive_gate(orc):
+    g = _acts(122, 3, 64)
+    y = np.concatenate([g, np.ones_like(g)], axis=1)
+    assert np.array_equal(orc.glu_relu2(y), orc.relu2(g))
+    y2 = np.concatenate([-np.abs(g), _acts(123, 3, 64)], axis=1)
+    assert np.all(orc.glu_relu2(y2) == 0)
