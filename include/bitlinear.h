@@ -87,9 +87,17 @@ typedef enum {
 
 typedef enum {
   BITLINEAR_EPI_NONE = 0,  /* Y = y */
-  BITLINEAR_EPI_RELU2 = 1  /* Y = max(y, 0)^2 (the squared-ReLU FFN
+  BITLINEAR_EPI_RELU2 = 1, /* Y = max(y, 0)^2 (the squared-ReLU FFN
                               activation, "BitNet b1.58 2B4T Technical
                               Report" card, Method Adaptation) */
+  BITLINEAR_EPI_RELU2_GLU = 2
+  /* Gated squared ReLU of a fused gate+up matrix packed by
+     bitlinear_quantize_weights_glu: with y = [gate | up] (N columns),
+     Y [M][N/2] = max(gate, 0)^2 * up, left to right, no fused multiply-add.
+     The pages give ReLU^2 as the FFN activation (same card) and no gating
+     formula; the gate+up shape of the decode workload is read as gate rows
+     then up rows.  Only valid with weights packed that way; dbg->acc_out
+     then stays [M][N] in the unpermuted row order. */
 } bitlinear_epilogue;
 
 /* Optional extra outputs of bitlinear_forward, for checking the integer
@@ -132,6 +140,15 @@ size_t bitlinear_forward_q_workspace_bytes(int64_t M, int64_t K, int64_t N);
 bitlinear_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
                                             uint8_t* packed, float* gamma, void* ws,
                                             size_t ws_bytes, void* stream);
+
+/* The same for a fused gate+up matrix W [N][K] (gate rows 0..N/2-1, then
+ * the up rows; one gamma over the whole matrix), packed with its halves
+ * interleaved: 16-row tile t holds gate rows 8t..8t+7, then up rows
+ * N/2+8t..N/2+8t+7, so that every kernel finds a gate row and its up row in
+ * one tile.  Use with BITLINEAR_EPI_RELU2_GLU. */
+bitlinear_status bitlinear_quantize_weights_glu(const float* W, int64_t N, int64_t K,
+                                                uint8_t* packed, float* gamma, void* ws,
+                                                size_t ws_bytes, void* stream);
 
 /* Packs already-ternary int8 q_w [N][K].  Values should be in {-1,0,1};
  * any other value is clamped into that range before it is stored. */
@@ -227,7 +244,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
 typedef struct {
   const void* X;          /* [M][K] activations, device, 16-byte aligned */
   bitlinear_dtype dtype;  /* BITLINEAR_F32 or BITLINEAR_BF16 */
-  bitlinear_epilogue epi; /* BITLINEAR_EPI_NONE or BITLINEAR_EPI_RELU2 */
+  bitlinear_epilogue epi; /* any epilogue; RELU2_GLU writes Y [M][N/2] */
   int64_t K, N;           /* N % 16 == 0, K % 256 == 0, K <= 8388608,
                              N <= 4194304; for M <= 16 also K <= 12288
                              and M * (max K + 16) + M * 2048 <= 160 KiB */

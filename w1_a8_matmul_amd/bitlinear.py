@@ -20,7 +20,12 @@ HEADER = os.path.join(ROOT, "include", "bitlinear.h")
 
 OK = 0
 F32, BF16 = 0, 1
-EPI = {"none": 0, None: 0, "relu2": 1}
+EPI = {"none": 0, None: 0, "relu2": 1, "relu2_glu": 2}
+
+
+def _out_cols(N: int, epilogue) -> int:
+    """Columns of Y: the gated epilogue writes N/2."""
+    return N // 2 if EPI[epilogue] == 2 else N
 
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -68,6 +73,7 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward_q_workspace_bytes.argtypes = [_i64, _i64, _i64]
     L.bitlinear_forward_q_workspace_bytes.restype = _sz
     L.bitlinear_quantize_weights.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
+    L.bitlinear_quantize_weights_glu.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
     L.bitlinear_pack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_unpack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_quantize_acts.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
@@ -153,10 +159,11 @@ def _empty_bytes(n: int, device) -> torch.Tensor:
 # -- weights ----------------------------------------------------------------
 def quantize_weights(W: torch.Tensor, packed: Optional[torch.Tensor] = None,
                      gamma: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None):
+                     workspace: Optional[torch.Tensor] = None, glu: bool = False):
     """Absmean ternary quantization + packing of float32 W [N][K].
 
-    Returns (packed uint8 [N*K/4], gamma_c float32 [1])."""
+    Returns (packed uint8 [N*K/4], gamma_c float32 [1]).  ``glu=True`` packs a
+    fused gate+up matrix (gate rows first) for the "relu2_glu" epilogue."""
     N, K = W.shape
     if W.dtype != torch.float32:
         raise BitLinearError("W must be float32")
@@ -167,9 +174,10 @@ def quantize_weights(W: torch.Tensor, packed: Optional[torch.Tensor] = None,
         gamma = torch.empty(4, dtype=torch.float32, device=W.device)[:1]
     if workspace is None:
         workspace = _empty_bytes(weights_workspace_bytes(N, K), W.device)
-    st = lib().bitlinear_quantize_weights(_ptr(W), N, K, _ptr(packed), _ptr(gamma),
-                                          _ptr(workspace), workspace.numel(), _stream())
-    check(st, "bitlinear_quantize_weights")
+    fn = lib().bitlinear_quantize_weights_glu if glu else lib().bitlinear_quantize_weights
+    st = fn(_ptr(W), N, K, _ptr(packed), _ptr(gamma), _ptr(workspace), workspace.numel(),
+            _stream())
+    check(st, "bitlinear_quantize_weights_glu" if glu else "bitlinear_quantize_weights")
     return packed, gamma
 
 
@@ -221,7 +229,7 @@ def forward(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
     ``norm_gain`` (float32 [K]) subln runs first, fused into the quantization."""
     M, K = X.shape
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+        out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.float32, device=X.device)
     ws_need = workspace_bytes(M, K, N)
     if ws_need == ctypes.c_size_t(-1).value:
         ws_need = 0  # the call itself reports the bad shape
@@ -266,7 +274,8 @@ def forward_q(Xq: torch.Tensor, x_scale: torch.Tensor, x_rowsum: torch.Tensor,
     split_remainder=False runs one workgroup per tile without it."""
     M, K = Xq.shape
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+        out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.float32,
+                          device=Xq.device)
     if workspace is None and split_remainder:
         workspace = forward_q_workspace(M, K, N, Xq.device)
     ws = workspace if split_remainder else None
@@ -304,7 +313,8 @@ class Group:
             if m != M:
                 raise BitLinearError("all layers of a group need the same M")
             if Y is None:
-                Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+                Y = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.float32,
+                                device=X.device)
             arr[i] = GroupOp(_ptr(X), _dtype_code(X), EPI[epilogue], K, N, _ptr(packed),
                              _ptr(gamma), _ptr(Y), _ptr(gain), eps if gain is not None else 0.0)
             self.keep += [X, packed, gamma] + ([gain] if gain is not None else [])

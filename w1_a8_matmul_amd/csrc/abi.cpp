@@ -142,6 +142,10 @@ GroupLayout group_layout(const bitlinear_group_op* ops, int n_ops, int64_t M) {
   return L;
 }
 
+bool valid_epi(int epi) {
+  return epi == BITLINEAR_EPI_NONE || epi == BITLINEAR_EPI_RELU2 || epi == BITLINEAR_EPI_RELU2_GLU;
+}
+
 // subln arguments: the gain is optional (NULL: none); when given it must be
 // 16-byte aligned device memory and the epsilon finite and non-negative.
 bitlinear_status check_norm(const float* norm_gain, float norm_eps) {
@@ -163,7 +167,7 @@ bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M
     const bitlinear_group_op& o = ops[i];
     if (o.dtype != BITLINEAR_F32 && o.dtype != BITLINEAR_BF16)
       return fail(BITLINEAR_ERR_DTYPE, "op %d: unknown dtype %d", i, (int)o.dtype);
-    if (o.epi != BITLINEAR_EPI_NONE && o.epi != BITLINEAR_EPI_RELU2)
+    if (!valid_epi(o.epi))
       return fail(BITLINEAR_ERR_ARG, "op %d: unknown epilogue %d", i, (int)o.epi);
     bitlinear_status st = check_nk(o.N, o.K);
     if (st != BITLINEAR_OK) return st;
@@ -235,9 +239,10 @@ size_t bitlinear_forward_q_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   return bl_gemm_workspace_bytes(M, K, N);
 }
 
-bitlinear_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
-                                            uint8_t* packed, float* gamma, void* ws,
-                                            size_t ws_bytes, void* stream) {
+static bitlinear_status quantize_weights_impl(const float* W, int64_t N, int64_t K,
+                                              uint8_t* packed, float* gamma, void* ws,
+                                              size_t ws_bytes, void* stream, bool glu,
+                                              const char* name) {
   if (!W || !packed || !gamma) return fail(BITLINEAR_ERR_NULL, "W, packed and gamma are required");
   bitlinear_status st = check_nk(N, K);
   if (st != BITLINEAR_OK) return st;
@@ -252,8 +257,22 @@ bitlinear_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K
   double* row_sum = static_cast<double*>(ws);
   hipError_t e = bl_launch_absmean_rows(W, N, K, row_sum, s);
   if (e == hipSuccess) e = bl_launch_absmean_final(row_sum, N, K, gamma, s);
-  if (e == hipSuccess) e = bl_launch_quant_pack(W, N, K, gamma, packed, s);
-  return from_hip(e, "bitlinear_quantize_weights");
+  if (e == hipSuccess) e = bl_launch_quant_pack(W, N, K, gamma, packed, s, glu);
+  return from_hip(e, name);
+}
+
+bitlinear_status bitlinear_quantize_weights(const float* W, int64_t N, int64_t K,
+                                            uint8_t* packed, float* gamma, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  return quantize_weights_impl(W, N, K, packed, gamma, ws, ws_bytes, stream, false,
+                               "bitlinear_quantize_weights");
+}
+
+bitlinear_status bitlinear_quantize_weights_glu(const float* W, int64_t N, int64_t K,
+                                                uint8_t* packed, float* gamma, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  return quantize_weights_impl(W, N, K, packed, gamma, ws, ws_bytes, stream, true,
+                               "bitlinear_quantize_weights_glu");
 }
 
 bitlinear_status bitlinear_pack_ternary(const int8_t* Wq, int64_t N, int64_t K,
@@ -325,7 +344,7 @@ static bitlinear_status forward_impl(const void* X, bitlinear_dtype dtype, int64
                                      void* stream, const char* name) {
   if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
     return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
-  if (epi != BITLINEAR_EPI_NONE && epi != BITLINEAR_EPI_RELU2)
+  if (!valid_epi(epi))
     return fail(BITLINEAR_ERR_ARG, "unknown epilogue %d", (int)epi);
   if (M < 0) return fail(BITLINEAR_ERR_SHAPE, "M=%lld is negative", (long long)M);
   bitlinear_status st = check_nk(N, K);
@@ -343,11 +362,10 @@ static bitlinear_status forward_impl(const void* X, bitlinear_dtype dtype, int64
     return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
   st = check_norm(norm_gain, norm_eps);
   if (st != BITLINEAR_OK) return st;
-  const bool relu2 = epi == BITLINEAR_EPI_RELU2;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (bl_gemv_supports(M, K))
-    return from_hip(bl_launch_gemv(X, (int)dtype, M, K, N, packed, gamma, Y, relu2, xq_out,
+    return from_hip(bl_launch_gemv(X, (int)dtype, M, K, N, packed, gamma, Y, (int)epi, xq_out,
                                    xs_out, acc_out, s, norm_gain, norm_eps),
                     name);
 
@@ -372,7 +390,8 @@ static bitlinear_status forward_impl(const void* X, bitlinear_dtype dtype, int64
   if (e == hipSuccess && xs_out)
     e = hipMemcpyAsync(xs_out, sx, (size_t)M * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
-    e = bl_launch_gemm_q(xq, sx, rs, M, K, N, packed, gamma, Y, relu2, acc_out, gemm_ws, s);
+    e = bl_launch_gemm_q(xq, sx, rs, M, K, N, packed, gamma, Y, (int)epi, acc_out, gemm_ws,
+                         s);
   return from_hip(e, name);
 }
 
@@ -401,7 +420,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      const uint8_t* packed, const float* gamma, float* Y,
                                      bitlinear_epilogue epi, void* ws, size_t ws_bytes,
                                      void* stream) {
-  if (epi != BITLINEAR_EPI_NONE && epi != BITLINEAR_EPI_RELU2)
+  if (!valid_epi(epi))
     return fail(BITLINEAR_ERR_ARG, "unknown epilogue %d", (int)epi);
   if (M < 0) return fail(BITLINEAR_ERR_SHAPE, "M=%lld is negative", (long long)M);
   bitlinear_status st = check_nk(N, K);
@@ -421,7 +440,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
     if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
   return from_hip(bl_launch_gemm_q(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
-                                   epi == BITLINEAR_EPI_RELU2, nullptr, ws,
+                                   (int)epi, nullptr, ws,
                                    static_cast<hipStream_t>(stream)),
                   "bitlinear_forward_q");
 }
@@ -463,7 +482,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     t.K = (int32_t)o.K;
     t.N = (int32_t)o.N;
     t.dtype = (int32_t)o.dtype;
-    t.relu2 = o.epi == BITLINEAR_EPI_RELU2 ? 1 : 0;
+    t.epi = (int32_t)o.epi;
     t.item_begin = (int32_t)item;
     t.norm_gain = o.norm_gain;
     t.norm_eps = o.norm_eps;

@@ -129,6 +129,24 @@ __device__ __forceinline__ int quant_i8(float v) {
   return (int)r;
 }
 
+// Epilogue modes: none, ReLU^2, and the gated ReLU^2 of a fused gate+up
+// matrix packed with its halves interleaved (16-row tile t: gate rows
+// 8t..8t+7, then their up rows), whose output has N/2 columns.
+constexpr int kEpiNone = 0, kEpiRelu2 = 1, kEpiGlu = 2;
+
+// h = max(gate, 0)^2 * up, left to right (no fused multiply-add).
+__device__ __forceinline__ float glu_relu2(float yg, float yu) {
+  const float r = yg > 0.0f ? yg : 0.0f;
+  const float t = r * r;
+  return t * yu;
+}
+
+// Row of the unpermuted gate+up matrix held at interleaved packed row n.
+__device__ __forceinline__ int64_t glu_source_row(int64_t n, int64_t N) {
+  const int64_t t = n / 16, i = n % 16;
+  return i < 8 ? 8 * t + i : N / 2 + 8 * t + (i - 8);
+}
+
 // Epilogue: ((float)acc * s_x) * gamma, then the optional ReLU^2.  Written as
 // separate statements; the library is compiled with -ffp-contract=off.
 __device__ __forceinline__ float rescale(int acc, float sx, float gamma, bool relu2) {
@@ -155,7 +173,8 @@ hipError_t bl_launch_absmean_rows(const float* W, int64_t N, int64_t K, double* 
 hipError_t bl_launch_absmean_final(const double* row_sum, int64_t N, int64_t K,
                                    float* gamma, hipStream_t s);
 hipError_t bl_launch_quant_pack(const float* W, int64_t N, int64_t K, const float* gamma,
-                                uint8_t* packed, hipStream_t s);
+                                uint8_t* packed, hipStream_t s,
+                                bool glu = false);
 hipError_t bl_launch_pack(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packed,
                           hipStream_t s);
 hipError_t bl_launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
@@ -170,7 +189,7 @@ hipError_t bl_launch_quant_acts(const void* X, int dtype, int64_t M, int64_t K, 
 // Small-M fused forward (activation quantization inside the kernel).
 bool bl_gemv_supports(int64_t M, int64_t K);
 hipError_t bl_launch_gemv(const void* X, int dtype, int64_t M, int64_t K, int64_t N,
-                          const uint8_t* packed, const float* gamma, float* Y, bool relu2,
+                          const uint8_t* packed, const float* gamma, float* Y, int epi,
                           int8_t* xq_out, float* xscale_out, int32_t* acc_out,
                           hipStream_t s, const float* norm_gain = nullptr,
                           float norm_eps = 0.0f);
@@ -182,5 +201,5 @@ size_t bl_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 size_t bl_gemm_counter_bytes();
 hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
-                            const float* gamma, float* Y, bool relu2, int32_t* acc_out,
+                            const float* gamma, float* Y, int epi, int32_t* acc_out,
                             void* gemm_ws, hipStream_t s);

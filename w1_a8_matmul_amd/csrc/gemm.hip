@@ -309,7 +309,7 @@ __device__ __forceinline__ RowScale load_row_scale(const float* __restrict__ x_s
 template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
 __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM][TN],
                                               RowScale own, float gamma, int M, int N,
-                                              float* __restrict__ Y, int relu2,
+                                              float* __restrict__ Y, int epi,
                                               int32_t* __restrict__ acc_out, int tm, int tn) {
   using T = Tile<WM, WN, TM, TN, S>;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -340,7 +340,13 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
   // measured 1-7% faster over the prefill shapes.
   const uint32_t row_bytes = (uint32_t)N * 4u;
   const uint32_t rows_here = (uint32_t)min(T::BM, M - m0);
-  const auto y_r = make_rsrc(Y + (int64_t)m0 * N, rows_here * row_bytes);
+  // The gated epilogue (interleaved gate+up tiles) writes N/2 columns: lane
+  // column c < 8 of each 16-column group holds a gate, its up is column c+8,
+  // one DPP row rotation away (row_ror:8 within the 16-lane DPP row).
+  const bool glu = epi == kEpiGlu;
+  const int64_t ny = glu ? N / 2 : N;
+  const uint32_t yrow_bytes = (uint32_t)ny * 4u;
+  const auto y_r = make_rsrc(Y + (int64_t)m0 * ny, rows_here * yrow_bytes);
   const auto a_r = make_rsrc(acc_out + (int64_t)m0 * N, DEBUG ? rows_here * row_bytes : 0u);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -356,13 +362,25 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int n = nt0 * kTileRows + (wn * TN + j) * 32 + r32;
-          const uint32_t off = n < N ? (uint32_t)(r + q) * row_bytes + (uint32_t)n * 4u
-                                     : 0x80000000u;
           const int v = acc[i][j][4 * g + q] - rsv[q];
-          __builtin_amdgcn_raw_buffer_store_b32(
-              __float_as_uint(rescale(v, sxv[q], gamma, relu2 != 0)), y_r, (int)off, 0, 2);
-          if constexpr (DEBUG)
-            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, a_r, (int)off, 0, 0);
+          float y = rescale(v, sxv[q], gamma, epi == kEpiRelu2);
+          uint32_t off;
+          if (glu) {
+            const float up = __int_as_float(dpp<0x128>(__float_as_int(y)));
+            y = glu_relu2(y, up);
+            const int f = (n >> 4) * 8 + (n & 7);
+            off = n < N && (r32 & 8) == 0 ? (uint32_t)(r + q) * yrow_bytes + (uint32_t)f * 4u
+                                          : 0x80000000u;
+          } else {
+            off = n < N ? (uint32_t)(r + q) * yrow_bytes + (uint32_t)n * 4u : 0x80000000u;
+          }
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), y_r, (int)off, 0, 2);
+          if constexpr (DEBUG) {
+            const int64_t col = glu ? glu_source_row(n, N) : n;
+            const uint32_t aoff =
+                n < N ? (uint32_t)(r + q) * row_bytes + (uint32_t)col * 4u : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, a_r, (int)aoff, 0, 0);
+          }
         }
       }
     }
@@ -375,13 +393,13 @@ __device__ __forceinline__ void gemm_tile(
     int8_t* ring, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
-    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tm, int tn) {
+    float* __restrict__ Y, int epi, int32_t* __restrict__ acc_out, int tm, int tn) {
   const RowScale own = load_row_scale<WM, WN, TM, TN, S>(x_scale, x_rowsum, M, tm);
   const float gamma = *gamma_p;
   v16i acc[TM][TN];
   tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, 0, K / kStepCols,
                                           true, acc);
-  tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, relu2, acc_out, tm,
+  tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
                                           tn);
 }
 
@@ -507,7 +525,7 @@ __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
-    float* __restrict__ Y, int relu2, int32_t* __restrict__ acc_out, int tiles_n,
+    float* __restrict__ Y, int epi, int32_t* __restrict__ acc_out, int tiles_n,
     SkPlan plan, int* __restrict__ sk_ws) {
   using T = Tile<WM, WN, TM, TN, S>;
   __shared__ __align__(1024) int8_t ring[S * T::kStageBytes];
@@ -538,7 +556,7 @@ __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
   tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, k0, k1, !split, acc);
   if constexpr (LEVEL) __builtin_amdgcn_s_setprio(0);
   if (!split || sk_contribute<WM, WN, TM, TN, S>(ring, acc, plan, sk_ws, t, g))
-    tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, relu2, acc_out, tm,
+    tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
                                             tn);
 }
 
@@ -570,7 +588,7 @@ __global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
     if (!first) lds_barrier();  // every wave is past the previous tile's LDS reads
     first = false;
     gemm_tile<WM, WN, TM, TN, S, false, true>(ring, xq + o.xq_off, sx + op * M, rs + op * M, M,
-                                              o.K, o.N, o.packed, o.gamma, o.Y, o.relu2, nullptr,
+                                              o.K, o.N, o.packed, o.gamma, o.Y, o.epi, nullptr,
                                               tm, tn);
   }
 }
@@ -608,7 +626,7 @@ int resident_per_cu() {
 template <int WM, int WN, int TM, int TN, int S>
 hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M,
                       int64_t K, int64_t N, const uint8_t* packed, const float* gamma, float* Y,
-                      bool relu2, int32_t* acc_out, int* sk_ws, hipStream_t s) {
+                      int epi, int32_t* acc_out, int* sk_ws, hipStream_t s) {
   using T = Tile<WM, WN, TM, TN, S>;
   const int tiles_m = (int)((M + T::BM - 1) / T::BM);
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
@@ -640,15 +658,15 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
   if (acc_out)
     hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, true, false>), dim3(grid),
                        dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma,
-                       Y, relu2 ? 1 : 0, acc_out, tiles_n, plan, sk_ws);
+                       Y, epi, acc_out, tiles_n, plan, sk_ws);
   else if (level)
     hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, false, true>), dim3(grid),
                        dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma,
-                       Y, relu2 ? 1 : 0, acc_out, tiles_n, plan, sk_ws);
+                       Y, epi, acc_out, tiles_n, plan, sk_ws);
   else
     hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, false, false>), dim3(grid),
                        dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma,
-                       Y, relu2 ? 1 : 0, acc_out, tiles_n, plan, sk_ws);
+                       Y, epi, acc_out, tiles_n, plan, sk_ws);
   return hipGetLastError();
 }
 
@@ -703,11 +721,11 @@ size_t bl_gemm_counter_bytes() { return kSkCounterInts * sizeof(int); }
 
 hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
                             int64_t M, int64_t K, int64_t N, const uint8_t* packed,
-                            const float* gamma, float* Y, bool relu2, int32_t* acc_out,
+                            const float* gamma, float* Y, int epi, int32_t* acc_out,
                             void* gemm_ws, hipStream_t s) {
   if (M <= kSmallM)
-    return launch_cfg<2, 2, 1, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
+    return launch_cfg<2, 2, 1, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
                                      acc_out, static_cast<int*>(gemm_ws), s);
-  return launch_cfg<2, 2, 2, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, relu2,
+  return launch_cfg<2, 2, 2, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
                                    acc_out, static_cast<int*>(gemm_ws), s);
 }

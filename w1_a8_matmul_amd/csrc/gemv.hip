@@ -38,7 +38,7 @@ constexpr int kMaxLoadsPerLane = 12;
 template <int M, int DT, int L, int TPW, bool NORM>
 __global__ __launch_bounds__(kNT) void gemv_kernel(
     const void* __restrict__ X, int K, int64_t N, const uint8_t* __restrict__ packed,
-    const float* __restrict__ gamma_p, float* __restrict__ Y, int relu2,
+    const float* __restrict__ gamma_p, float* __restrict__ Y, int epi,
     int8_t* __restrict__ xq_out, float* __restrict__ xscale_out, int32_t* __restrict__ acc_out,
     const float* __restrict__ norm_gain, float norm_eps) {
   constexpr int W = kNT / kWave;
@@ -109,8 +109,23 @@ __global__ __launch_bounds__(kNT) void gemv_kernel(
     if (tile < ntiles) {
       const int acc_true = s - s_rowsum[m];
       const int64_t n = tile * kTileRows + i;
-      Y[m * N + n] = rescale(acc_true, s_scale[m], *gamma_p, relu2 != 0);
-      if (acc_out) acc_out[m * N + n] = acc_true;
+      if (epi == kEpiGlu) {
+        // rows i < 8 of the tile are gates, rows i + 8 their up rows
+        if (i < 8) {
+          int su = 0;
+#pragma unroll
+          for (int w = 0; w < W; ++w)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) su += partial[t][m][w][q * 16 + i + 8];
+          const float yg = rescale(acc_true, s_scale[m], *gamma_p, false);
+          const float yu = rescale(su - s_rowsum[m], s_scale[m], *gamma_p, false);
+          Y[m * (N / 2) + tile * 8 + i] = glu_relu2(yg, yu);
+        }
+        if (acc_out) acc_out[m * N + glu_source_row(n, N)] = acc_true;
+      } else {
+        Y[m * N + n] = rescale(acc_true, s_scale[m], *gamma_p, epi == kEpiRelu2);
+        if (acc_out) acc_out[m * N + n] = acc_true;
+      }
     }
   }
   if (blockIdx.x == 0) {
@@ -127,7 +142,7 @@ struct GemvArgs {
   const uint8_t* packed;
   const float* gamma;
   float* Y;
-  bool relu2;
+  int epi;
   int8_t* xq;
   float* xs;
   int32_t* acc;
@@ -142,11 +157,11 @@ hipError_t launch_one(const GemvArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.N / kTileRows / kTilesPerWorkgroup)), block(kNT);
   if (a.norm_gain)
     hipLaunchKernelGGL((gemv_kernel<M, DT, L, kTilesPerWorkgroup, true>), grid, block, lds, s,
-                       a.X, (int)a.K, a.N, a.packed, a.gamma, a.Y, a.relu2 ? 1 : 0, a.xq, a.xs,
+                       a.X, (int)a.K, a.N, a.packed, a.gamma, a.Y, a.epi, a.xq, a.xs,
                        a.acc, a.norm_gain, a.norm_eps);
   else
     hipLaunchKernelGGL((gemv_kernel<M, DT, L, kTilesPerWorkgroup, false>), grid, block, lds, s,
-                       a.X, (int)a.K, a.N, a.packed, a.gamma, a.Y, a.relu2 ? 1 : 0, a.xq, a.xs,
+                       a.X, (int)a.K, a.N, a.packed, a.gamma, a.Y, a.epi, a.xq, a.xs,
                        a.acc, a.norm_gain, a.norm_eps);
   return hipGetLastError();
 }
@@ -190,10 +205,10 @@ bool bl_gemv_supports(int64_t M, int64_t K) {
 }
 
 hipError_t bl_launch_gemv(const void* X, int dtype, int64_t M, int64_t K, int64_t N,
-                          const uint8_t* packed, const float* gamma, float* Y, bool relu2,
+                          const uint8_t* packed, const float* gamma, float* Y, int epi,
                           int8_t* xq_out, float* xscale_out, int32_t* acc_out, hipStream_t s,
                           const float* norm_gain, float norm_eps) {
-  const GemvArgs a{X, K, N, packed, gamma, Y, relu2, xq_out, xscale_out, acc_out, norm_gain,
+  const GemvArgs a{X, K, N, packed, gamma, Y, epi, xq_out, xscale_out, acc_out, norm_gain,
                    norm_eps};
   return dtype == 1 ? launch_dt<1>(M, a, s) : launch_dt<0>(M, a, s);
 }

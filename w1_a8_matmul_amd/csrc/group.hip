@@ -184,7 +184,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
         const int m = 4 * q16 + r;
         if (m < M && j < total)
           s_y[(m * kSegTiles + (q.it - first)) * kTileRows + (lane & 15)] =
-              rescale(d[r] - s_rs[m], s_sx[m], gamma, o.relu2 != 0);
+              rescale(d[r] - s_rs[m], s_sx[m], gamma, o.epi == kEpiRelu2);
       }
       acc0 = v4i{0, 0, 0, 0};
       acc1 = v4i{0, 0, 0, 0};
@@ -224,9 +224,20 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   __syncthreads();
   const int rows = (last - first) * kTileRows;
   const int64_t n0 = (int64_t)(first - o.item_begin) * kTileRows;
-  for (int i = threadIdx.x; i < M * rows; i += kThreads) {
-    const int m = i / rows, r = i - m * rows;
-    o.Y[m * (int64_t)o.N + n0 + r] = s_y[m * kSegTiles * kTileRows + r];
+  if (o.epi == kEpiGlu) {
+    // interleaved gate+up tiles: rows 0..7 gates, 8..15 their up rows;
+    // output row r of the segment is gate row r (tile r/8) of N/2
+    const int half = rows / 2;
+    for (int i = threadIdx.x; i < M * half; i += kThreads) {
+      const int m = i / half, r = i - m * half;
+      const float* ty = s_y + m * kSegTiles * kTileRows + (r / 8) * kTileRows + (r % 8);
+      o.Y[m * (int64_t)(o.N / 2) + n0 / 2 + r] = glu_relu2(ty[0], ty[8]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < M * rows; i += kThreads) {
+      const int m = i / rows, r = i - m * rows;
+      o.Y[m * (int64_t)o.N + n0 + r] = s_y[m * kSegTiles * kTileRows + r];
+    }
   }
 }
 

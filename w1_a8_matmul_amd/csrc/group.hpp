@@ -13,7 +13,7 @@ struct GroupOp {
   const float* norm_gain;  // subln gain [K] before the quantization, or null
   int64_t xq_off;          // byte offset of this layer's int8 [M][K] in the workspace
   int32_t K, N;
-  int32_t dtype, relu2;
+  int32_t dtype, epi;      // epi: kEpiNone, kEpiRelu2 or kEpiGlu (Y then [M][N/2])
   int32_t item_begin;      // index of this layer's first 16-row tile in the flat list
   float norm_eps;          // subln epsilon
   int32_t pad[2];

@@ -53,16 +53,25 @@ __device__ __forceinline__ void word_origin(int64_t w, int64_t K, int64_t& n, in
 }
 
 // Column offset 4f + e of a word lives in byte e, bits 2f..2f+1.
+// Row of W stored at packed row n: itself, or for a fused gate+up matrix
+// (glu) the interleaved order, 16-row tile t = gate rows 8t..8t+7, then up
+// rows N/2+8t..N/2+8t+7.
+__device__ __forceinline__ int64_t source_row(int64_t n, int64_t N, int glu) {
+  if (!glu) return n;
+  const int64_t t = n / 16, i = n % 16;
+  return i < 8 ? 8 * t + i : N / 2 + 8 * t + (i - 8);
+}
+
 __global__ __launch_bounds__(256) void quant_pack_kernel(const float* __restrict__ W,
                                                          int64_t N, int64_t K,
                                                          const float* __restrict__ gamma_p,
-                                                         uint32_t* __restrict__ out) {
+                                                         uint32_t* __restrict__ out, int glu) {
   const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (w >= N * K / 16) return;
   const float gamma = *gamma_p;
   int64_t n, k0;
   word_origin(w, K, n, k0);
-  const float4* src = reinterpret_cast<const float4*>(W + n * K + k0);
+  const float4* src = reinterpret_cast<const float4*>(W + source_row(n, N, glu) * K + k0);
   uint32_t word = 0;
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
@@ -141,10 +150,10 @@ hipError_t bl_launch_absmean_final(const double* row_sum, int64_t N, int64_t K, 
 }
 
 hipError_t bl_launch_quant_pack(const float* W, int64_t N, int64_t K, const float* gamma,
-                                uint8_t* packed, hipStream_t s) {
+                                uint8_t* packed, hipStream_t s, bool glu) {
   const int64_t words = N * K / 16;
   hipLaunchKernelGGL(quant_pack_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s, W, N, K,
-                     gamma, reinterpret_cast<uint32_t*>(packed));
+                     gamma, reinterpret_cast<uint32_t*>(packed), glu ? 1 : 0);
   return hipGetLastError();
 }
 
