@@ -201,6 +201,7 @@ struct bitlinear_group {
   int max_k;
   int threads;
   bool norm;  // some layer has a subln gain
+  bool glu;   // some layer has the gated epilogue
   bool gemm;
   int n_items;  // items over all layers (output tiles in the GEMM mode)
   int n_units;  // shared work units of the skinny kernel
@@ -470,7 +471,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   std::vector<GroupOp> table((size_t)n_ops);
   int64_t item = 0, xq_off = 0;
   int max_k = 0;
-  bool norm = false;
+  bool norm = false, glu = false;
   for (int i = 0; i < n_ops; ++i) {
     const bitlinear_group_op& o = ops[i];
     GroupOp& t = table[(size_t)i];
@@ -483,6 +484,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     t.N = (int32_t)o.N;
     t.dtype = (int32_t)o.dtype;
     t.epi = (int32_t)o.epi;
+    if (o.epi == BITLINEAR_EPI_RELU2_GLU) glu = true;
     t.item_begin = (int32_t)item;
     t.norm_gain = o.norm_gain;
     t.norm_eps = o.norm_eps;
@@ -560,6 +562,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->max_k = max_k;
   g->threads = threads;
   g->norm = norm;
+  g->glu = glu;
   g->gemm = !skinny;
   g->n_items = (int)item;
   g->n_units = (int)L.n_units;
@@ -580,7 +583,8 @@ bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = bl_launch_group_quant(g->ops, g->n_ops, g->M, g->xq, g->sx, g->rs, s);
     if (e == hipSuccess)
-      e = bl_launch_group_gemm(g->ops, g->n_ops, g->M, g->n_items, g->G, g->xq, g->sx, g->rs, s);
+      e = bl_launch_group_gemm(g->ops, g->n_ops, g->M, g->n_items, g->G, g->xq, g->sx, g->rs,
+                               g->glu, s);
     return from_hip(e, "bitlinear_group_forward");
   }
   return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->units, g->n_units,

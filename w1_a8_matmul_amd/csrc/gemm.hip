@@ -306,7 +306,7 @@ __device__ __forceinline__ RowScale load_row_scale(const float* __restrict__ x_s
 
 // Epilogue of tile (tm, tn): Y = ((acc - rowsum) * s_x) * gamma, then the
 // optional ReLU^2.  Called by every wave after its K loop.
-template <int WM, int WN, int TM, int TN, int S, bool DEBUG>
+template <int WM, int WN, int TM, int TN, int S, bool DEBUG, bool GLU>
 __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM][TN],
                                               RowScale own, float gamma, int M, int N,
                                               float* __restrict__ Y, int epi,
@@ -343,7 +343,7 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
   // The gated epilogue (interleaved gate+up tiles) writes N/2 columns: lane
   // column c < 8 of each 16-column group holds a gate, its up is column c+8,
   // one DPP row rotation away (row_ror:8 within the 16-lane DPP row).
-  const bool glu = epi == kEpiGlu;
+  const bool glu = GLU && epi == kEpiGlu;  // compiled out of the plain kernels
   const int64_t ny = glu ? N / 2 : N;
   const uint32_t yrow_bytes = (uint32_t)ny * 4u;
   const auto y_r = make_rsrc(Y + (int64_t)m0 * ny, rows_here * yrow_bytes);
@@ -388,7 +388,7 @@ __device__ __forceinline__ void tile_epilogue(int8_t* ring, const v16i (&acc)[TM
 }
 
 // One output tile, whole K: the K loop and the epilogue.
-template <int WM, int WN, int TM, int TN, int S, bool DEBUG, bool LEVEL>
+template <int WM, int WN, int TM, int TN, int S, bool DEBUG, bool LEVEL, bool GLU>
 __device__ __forceinline__ void gemm_tile(
     int8_t* ring, const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
@@ -399,7 +399,7 @@ __device__ __forceinline__ void gemm_tile(
   v16i acc[TM][TN];
   tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, 0, K / kStepCols,
                                           true, acc);
-  tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
+  tile_epilogue<WM, WN, TM, TN, S, DEBUG, GLU>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
                                           tn);
 }
 
@@ -520,7 +520,7 @@ __device__ __forceinline__ bool sk_contribute(int8_t* ring, v16i (&acc)[TM][TN],
 // One layer.  Workgroups below plan.tiles_dp take one output tile each
 // (whole K); the tiles_sk * pieces workgroups after them take one piece of
 // a remaining tile each (sk_ws: counters, then one slot per piece).
-template <int WM, int WN, int TM, int TN, int S, bool DEBUG, bool LEVEL>
+template <int WM, int WN, int TM, int TN, int S, bool DEBUG, bool LEVEL, bool GLU>
 __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
   tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, k0, k1, !split, acc);
   if constexpr (LEVEL) __builtin_amdgcn_s_setprio(0);
   if (!split || sk_contribute<WM, WN, TM, TN, S>(ring, acc, plan, sk_ws, t, g))
-    tile_epilogue<WM, WN, TM, TN, S, DEBUG>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
+    tile_epilogue<WM, WN, TM, TN, S, DEBUG, GLU>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
                                             tn);
 }
 
@@ -569,7 +569,7 @@ __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
 // XCD takes a contiguous block of the window (consecutive workgroup ids go
 // to different XCDs), so what they share stays in one L2.  Every layer's
 // items spread evenly over the workgroups, which balances the cost.
-template <int WM, int WN, int TM, int TN, int S>
+template <int WM, int WN, int TM, int TN, int S, bool GLU>
 __global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
     const GroupOp* __restrict__ ops, int n_ops, int M, int n_items,
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int* __restrict__ rs) {
@@ -587,7 +587,7 @@ __global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
     const int tn = local / tiles_m, tm = local - tn * tiles_m;  // m fastest: weights reused
     if (!first) lds_barrier();  // every wave is past the previous tile's LDS reads
     first = false;
-    gemm_tile<WM, WN, TM, TN, S, false, true>(ring, xq + o.xq_off, sx + op * M, rs + op * M, M,
+    gemm_tile<WM, WN, TM, TN, S, false, true, GLU>(ring, xq + o.xq_off, sx + op * M, rs + op * M, M,
                                               o.K, o.N, o.packed, o.gamma, o.Y, o.epi, nullptr,
                                               tm, tn);
   }
@@ -616,7 +616,7 @@ int resident_per_cu() {
   if (cached == 0) {
     int blocks = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &blocks, reinterpret_cast<const void*>(&gemm_kernel<WM, WN, TM, TN, S, false, false>),
+        &blocks, reinterpret_cast<const void*>(&gemm_kernel<WM, WN, TM, TN, S, false, false, false>),
         Tile<WM, WN, TM, TN, S>::kThreads, 0);
     cached = (e == hipSuccess && blocks > 0) ? blocks : 4;
   }
@@ -655,18 +655,22 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
   const int cus = device_cus();
   const bool level = grid <= cus * resident_per_cu<WM, WN, TM, TN, S>() &&
                      (plan.pieces == 0 || plan.tiles_dp >= 2 * cus);
-  if (acc_out)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, true, false>), dim3(grid),
-                       dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma,
-                       Y, epi, acc_out, tiles_n, plan, sk_ws);
-  else if (level)
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, false, true>), dim3(grid),
-                       dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma,
-                       Y, epi, acc_out, tiles_n, plan, sk_ws);
-  else
-    hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, false, false>), dim3(grid),
-                       dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed, gamma,
-                       Y, epi, acc_out, tiles_n, plan, sk_ws);
+  const bool glu = epi == kEpiGlu;
+#define BL_GEMM_LAUNCH(DBG, LVL, GL)                                                          \
+  hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, S, DBG, LVL, GL>), dim3(grid),             \
+                     dim3(T::kThreads), 0, s, Xq, sx, rs, (int)M, (int)K, (int)N, packed,     \
+                     gamma, Y, epi, acc_out, tiles_n, plan, sk_ws)
+  if (acc_out) {
+    if (glu) BL_GEMM_LAUNCH(true, false, true);
+    else BL_GEMM_LAUNCH(true, false, false);
+  } else if (level) {
+    if (glu) BL_GEMM_LAUNCH(false, true, true);
+    else BL_GEMM_LAUNCH(false, true, false);
+  } else {
+    if (glu) BL_GEMM_LAUNCH(false, false, true);
+    else BL_GEMM_LAUNCH(false, false, false);
+  }
+#undef BL_GEMM_LAUNCH
   return hipGetLastError();
 }
 
@@ -694,21 +698,26 @@ int bl_group_gemm_tiles(int M, int N) {
 int bl_group_gemm_blocks_per_cu(int M) {
   int blocks = 0;
   const void* k = M <= kSmallM
-                      ? reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 1, 4, 2>)
-                      : reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 2, 2>);
+                      ? reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 1, 4, 2, false>)
+                      : reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 2, 2, false>);
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 256, 0);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
-                                const int8_t* xq, const float* sx, const int* rs,
+                                const int8_t* xq, const float* sx, const int* rs, bool glu,
                                 hipStream_t s) {
-  if (M <= kSmallM)
-    hipLaunchKernelGGL((group_gemm_kernel<2, 2, 1, 4, 2>), dim3(G), dim3(GroupSmallCfg::kThreads), 0,
-                       s, ops, n_ops, M, n_items, xq, sx, rs);
-  else
-    hipLaunchKernelGGL((group_gemm_kernel<2, 2, 2, 2, 2>), dim3(G), dim3(BigCfg::kThreads), 0,
-                       s, ops, n_ops, M, n_items, xq, sx, rs);
+#define BL_GROUP_GEMM(CFG, TN, GL)                                                            \
+  hipLaunchKernelGGL((group_gemm_kernel<2, 2, CFG::BM / 64, TN, 2, GL>), dim3(G),              \
+                     dim3(CFG::kThreads), 0, s, ops, n_ops, M, n_items, xq, sx, rs)
+  if (M <= kSmallM) {
+    if (glu) BL_GROUP_GEMM(GroupSmallCfg, 4, true);
+    else BL_GROUP_GEMM(GroupSmallCfg, 4, false);
+  } else {
+    if (glu) BL_GROUP_GEMM(BigCfg, 2, true);
+    else BL_GROUP_GEMM(BigCfg, 2, false);
+  }
+#undef BL_GROUP_GEMM
   return hipGetLastError();
 }
 

@@ -79,7 +79,7 @@ int bl_group_gemm_tiles(int M, int N);
 int bl_group_gemm_blocks_per_cu(int M);
 // n_items: output tiles over all layers; G workgroups take them strided.
 hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
-                                const int8_t* xq, const float* sx, const int* rs,
+                                const int8_t* xq, const float* sx, const int* rs, bool glu,
                                 hipStream_t s);
 // The quantization launch of the grouped forward (one workgroup per layer
 // and token) into xq / sx / rs at each layer's xq_off.
