@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-launches", type=int, default=400,
                    help="launches of the dominant kernel timed for the roofline")
+    p.add_argument("--glu", action="store_true",
+                   help="gated FFN: pack each gate+up linear (N = 2 x the down projection's K) "
+                        "for the gated squared-ReLU epilogue (output N/2)")
     p.add_argument("--subln", action="store_true",
                    help="give every linear a subln gain (RMSNorm fused into its quantization)")
     p.add_argument("--grouped", action="store_true",
@@ -80,8 +83,10 @@ def parse():
 # Workload runners: allocate everything up front; step(i) only launches.
 # ---------------------------------------------------------------------------
 class Linear:
-    def __init__(self, bl, torch, dev, N, K, M, x_dtype, seed, sparse, copies, subln=False):
+    def __init__(self, bl, torch, dev, N, K, M, x_dtype, seed, sparse, copies, subln=False,
+                 glu=False):
         self.N, self.K, self.M = N, K, M
+        self.epi = "relu2_glu" if glu else None
         gen = torch.Generator(device=dev)
         self.packed, self.gamma = [], []
         t0 = time.perf_counter()
@@ -91,7 +96,7 @@ class Linear:
             if sparse > 0:
                 mask = torch.rand((N, K), generator=gen, device=dev) < sparse
                 W = torch.where(mask, W * 1e-3, W)
-            p, g = bl.quantize_weights(W)
+            p, g = bl.quantize_weights(W, glu=glu)
             self.packed.append(p)
             self.gamma.append(g)
             del W
@@ -100,7 +105,7 @@ class Linear:
         gen.manual_seed(seed * 131 + 7777)
         X = torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32)
         self.X = X.to(x_dtype) if x_dtype is not None else X
-        self.Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        self.Y = torch.empty((M, N // 2 if glu else N), dtype=torch.float32, device=dev)
         self.gain = None
         if subln:  # gains uniform on [0.5, 1.5)
             gen.manual_seed(seed * 131 + 8888)
@@ -129,10 +134,13 @@ def build_runner(args, bl, torch, wl, dev):
     copies = max(1, -(-2 * MALL_BYTES // packed_per_step))
     copies = min(copies, 64)
     lins = []
+    downs_k = {l.K for l in wk.linears}
     for layer, li, shape in wl.step_linears(wk):
+        glu = bool(args.glu) and shape.N % 2 == 0 and shape.N // 2 in downs_k and \
+            shape.N // 2 != shape.K
         lins.append(Linear(bl, torch, dev, shape.N, shape.K, M, x_dtype,
                            wl.weight_seed(wk.key, layer, li), wk.weight_sparse_frac, copies,
-                           subln=args.subln))
+                           subln=args.subln, glu=glu))
     if wk.chain_relu2:
         # up (ReLU^2) feeds down: down's input is up's float output
         up, down = lins
@@ -142,7 +150,7 @@ def build_runner(args, bl, torch, wl, dev):
     if args.grouped:
         if wk.chain_relu2:
             raise SystemExit("--grouped needs independent linears")
-        groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, None, l.Y, l.gain)
+        groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, l.epi, l.Y, l.gain)
                             for l in lins])
                   for c in range(copies)]
 
@@ -159,8 +167,8 @@ def build_runner(args, bl, torch, wl, dev):
                        workspace=down.ws, norm_gain=down.gain)
         else:
             for lin in lins:
-                bl.forward(lin.X, lin.packed[c], lin.gamma[c], lin.N, out=lin.Y,
-                           workspace=lin.ws, norm_gain=lin.gain)
+                bl.forward(lin.X, lin.packed[c], lin.gamma[c], lin.N, epilogue=lin.epi,
+                           out=lin.Y, workspace=lin.ws, norm_gain=lin.gain)
 
     return wk, M, lins, copies, step, groups
 
@@ -196,7 +204,7 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
     """The linear with the most packed bytes, launched alone back to back
     (rotating its weight copies) in a graph bracketed by HIP events."""
     dom = max(lins, key=lambda l: l.N * l.K)
-    epi = "relu2" if (wk.chain_relu2 and dom is lins[0]) else None
+    epi = "relu2" if (wk.chain_relu2 and dom is lins[0]) else dom.epi
     n = args.kernel_launches
     copies = len(dom.packed)
     gemm = metric_kind == "tops" and dom.ws is not None
@@ -536,6 +544,7 @@ def main():
             "offline_weight_quant_ms": round(quant_s * 1e3 / copies, 3),
             "grouped": groups is not None,
             "subln": bool(args.subln),
+            "glu": bool(args.glu),
         },
         "roofline": roof,
         "cpu_baseline": cpu,
