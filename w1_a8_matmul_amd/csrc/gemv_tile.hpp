@@ -35,11 +35,13 @@ struct Chunk {
 // Loads of one activation row go through a buffer resource over that row,
 // so chunks past its end read as zero without a branch (branches around
 // loads make the compiler wait for them early) and without memory traffic.
+// With valid false the range is empty and the whole row reads as zero.
 template <int DT, int NT, int KCH>
 __device__ __forceinline__ void load_row(const void* __restrict__ X, int m, int K,
-                                         Chunk<DT> ch[KCH]) {
+                                         Chunk<DT> ch[KCH], bool valid = true) {
   constexpr uint32_t elt = DT == 1 ? 2 : 4;
-  const auto r = make_rsrc(reinterpret_cast<const char*>(X) + (int64_t)m * K * elt, K * elt);
+  const auto r = make_rsrc(reinterpret_cast<const char*>(X) + (int64_t)m * K * elt,
+                           valid ? K * elt : 0u);
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
     const uint32_t off = (threadIdx.x + c * NT) * 8 * elt;

@@ -64,8 +64,9 @@ struct Smem {
 // PREQ: the activations were quantized by the separate launch; the
 // segment copies its layer's int8 rows, scales and row sums into LDS instead.
 // NORM (inline quantization only): layers with a subln gain get it applied
-// before their quantization.
-template <int NT, int KCH, int DT, bool PREQ, bool NORM>
+// before their quantization.  MR (inline quantization, M > 1): the next
+// token row is loaded while the current one is quantized.
+template <int NT, int KCH, int DT, bool PREQ, bool NORM, bool MR>
 __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, int last,
                                             bool quantize, int8_t* xs, int xstride,
                                             float* s_sx, int* s_rs, float* s_y, Smem<NT>& sm,
@@ -144,6 +145,30 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
         s_rs[threadIdx.x] = rs[op * M + threadIdx.x];
       }
     }
+  } else if (quantize && MR) {
+    // Up to four token rows (M <= kGroupInlineQuantMaxM), straight-line code:
+    // rows 0 and 1 before the first weight chunk, row m + 2 issued before
+    // row m + 1 is quantized, so no quantization waits for a round trip of
+    // its own (rows past M read zero and are not quantized).  One row at a
+    // time cost a round trip per row at every new layer.
+    static_assert(kGroupInlineQuantMaxM <= 4, "the multi-row quantization handles four rows");
+    Chunk<DT> ch[KCH], nx[KCH];
+    load_row<DT, kThreads, KCH>(o.X, 0, K, ch);
+    Gains<kThreads, KCH> gn;
+    if constexpr (NORM) load_gains<kThreads, KCH>(o.norm_gain, K, gn);
+    const bool gain_on = NORM && o.norm_gain != nullptr;
+    load_row<DT, kThreads, KCH>(o.X, 1, K, nx, M > 1);
+    issue(bufA, 0, qi);
+    auto quant = [&](const Chunk<DT>(&c)[KCH], int m) {
+      quantize_row<DT, kThreads, KCH, NORM>(c, K, xs + m * xstride, sm.red_f, sm.red_i, s_sx + m,
+                                            s_rs + m, &gn, gain_on, o.norm_eps, sm.red_d);
+    };
+    quant(ch, 0);
+    load_row<DT, kThreads, KCH>(o.X, 2, K, ch, M > 2);
+    if (M > 1) quant(nx, 1);
+    load_row<DT, kThreads, KCH>(o.X, 3, K, nx, M > 3);
+    if (M > 2) quant(ch, 2);
+    if (M > 3) quant(nx, 3);
   } else if (quantize) {
     Chunk<DT> ch[KCH];
     load_row<DT, kThreads, KCH>(o.X, 0, K, ch);
@@ -254,7 +279,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
 // counts the workgroups that found the queue empty; the last of them puts
 // both back to zero for the next launch.  A layer's int8 activations are
 // quantized (or copied) whenever a workgroup moves to a new layer.
-template <int NT, int KCH, bool PREQ, bool NORM>
+template <int NT, int KCH, bool PREQ, bool NORM, bool MR>
 __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops, int n_ops,
                                                    int M, int max_k,
                                                    const int* __restrict__ wg_begin,
@@ -282,13 +307,13 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
     const GroupOp o = ops[op];
     const bool quantize = quantized_op != op;
     if (PREQ)
-      run_segment<NT, KCH, 0, true, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+      run_segment<NT, KCH, 0, true, false, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
                                     sm, xq, sx, rs, op, wave, lane);
     else if (o.dtype == 1)
-      run_segment<NT, KCH, 1, false, NORM>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+      run_segment<NT, KCH, 1, false, NORM, MR>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
                                      sm, xq, sx, rs, op, wave, lane);
     else
-      run_segment<NT, KCH, 0, false, NORM>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
+      run_segment<NT, KCH, 0, false, NORM, MR>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
                                      sm, xq, sx, rs, op, wave, lane);
     __syncthreads();  // before the next segment overwrites xs, the scales, s_y or s_unit
     quantized_op = op;
@@ -362,61 +387,67 @@ __global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restr
 
 // Activation chunks per thread: each covers NT * 8 elements of a row.
 // Kernel modes: pre-quantized (the quantization launch applies any subln);
-// inline quantization without or with subln gains.
-template <int NT, bool PREQ, bool NORM>
+// inline quantization without or with subln gains, of one row or of several.
+template <int NT, bool PREQ, bool NORM, bool MR>
 const void* kernel_for(int max_k) {
   if (max_k <= NT * 8 * 2)
-    return reinterpret_cast<const void*>(&group_kernel<NT, 2, PREQ, NORM>);
+    return reinterpret_cast<const void*>(&group_kernel<NT, 2, PREQ, NORM, MR>);
   if (max_k <= NT * 8 * 4)
-    return reinterpret_cast<const void*>(&group_kernel<NT, 4, PREQ, NORM>);
-  return reinterpret_cast<const void*>(&group_kernel<NT, 6, PREQ, NORM>);
+    return reinterpret_cast<const void*>(&group_kernel<NT, 4, PREQ, NORM, MR>);
+  return reinterpret_cast<const void*>(&group_kernel<NT, 6, PREQ, NORM, MR>);
 }
 
-template <int NT>
-const void* kernel_for(bool preq, bool norm, int max_k) {
-  if (preq) return kernel_for<NT, true, false>(max_k);
-  return norm ? kernel_for<NT, false, true>(max_k) : kernel_for<NT, false, false>(max_k);
+template <int NT, bool NORM>
+const void* kernel_for(bool mr, int max_k) {
+  return mr ? kernel_for<NT, false, NORM, true>(max_k) : kernel_for<NT, false, NORM, false>(max_k);
 }
 
-const void* kernel_for(int threads, bool preq, bool norm, int max_k) {
-  return threads == 512 ? kernel_for<512>(preq, norm, max_k)
-                        : kernel_for<256>(preq, norm, max_k);
+// The kernel a launch for M tokens uses.
+const void* kernel_for(int threads, int M, bool norm, int max_k) {
+  const bool preq = bl_group_prequantizes(M), mr = M > 1;
+  if (threads == 512) {
+    if (preq) return kernel_for<512, true, false, false>(max_k);
+    return norm ? kernel_for<512, true>(mr, max_k) : kernel_for<512, false>(mr, max_k);
+  }
+  if (preq) return kernel_for<256, true, false, false>(max_k);
+  return norm ? kernel_for<256, true>(mr, max_k) : kernel_for<256, false>(mr, max_k);
 }
 
-template <int NT, bool PREQ, bool NORM>
+template <int NT, bool PREQ, bool NORM, bool MR>
 void launch(const GroupOp* ops, int n_ops, int M, const int* wg_begin, const GroupUnit* units,
             int n_units, int* queue, int G, int max_k, size_t lds, const int8_t* xq,
             const float* sx, const int* rs, hipStream_t s) {
   if (max_k <= NT * 8 * 2)
-    hipLaunchKernelGGL((group_kernel<NT, 2, PREQ, NORM>), dim3(G), dim3(NT), lds, s, ops,
+    hipLaunchKernelGGL((group_kernel<NT, 2, PREQ, NORM, MR>), dim3(G), dim3(NT), lds, s, ops,
                        n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else if (max_k <= NT * 8 * 4)
-    hipLaunchKernelGGL((group_kernel<NT, 4, PREQ, NORM>), dim3(G), dim3(NT), lds, s, ops,
+    hipLaunchKernelGGL((group_kernel<NT, 4, PREQ, NORM, MR>), dim3(G), dim3(NT), lds, s, ops,
                        n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else
-    hipLaunchKernelGGL((group_kernel<NT, 6, PREQ, NORM>), dim3(G), dim3(NT), lds, s, ops,
+    hipLaunchKernelGGL((group_kernel<NT, 6, PREQ, NORM, MR>), dim3(G), dim3(NT), lds, s, ops,
                        n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
 }
 
 template <int NT>
-void launch(bool preq, bool norm, const GroupOp* ops, int n_ops, int M, const int* wg_begin,
+void launch(bool norm, const GroupOp* ops, int n_ops, int M, const int* wg_begin,
             const GroupUnit* units, int n_units, int* queue, int G, int max_k, size_t lds,
             const int8_t* xq, const float* sx, const int* rs, hipStream_t s) {
-  if (preq)
-    launch<NT, true, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                            sx, rs, s);
+#define BL_GROUP_LAUNCH(P, NM, MRV)                                                      \
+  launch<NT, P, NM, MRV>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq, \
+                         sx, rs, s)
+  if (bl_group_prequantizes(M))
+    BL_GROUP_LAUNCH(true, false, false);
   else if (norm)
-    launch<NT, false, true>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                            sx, rs, s);
+    M > 1 ? BL_GROUP_LAUNCH(false, true, true) : BL_GROUP_LAUNCH(false, true, false);
   else
-    launch<NT, false, false>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                             sx, rs, s);
+    M > 1 ? BL_GROUP_LAUNCH(false, false, true) : BL_GROUP_LAUNCH(false, false, false);
+#undef BL_GROUP_LAUNCH
 }
 
-int blocks_per_cu(int threads, bool preq, bool norm, size_t lds, int max_k) {
+int blocks_per_cu(int threads, int M, bool norm, size_t lds, int max_k) {
   int blocks = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks, kernel_for(threads, preq, norm, max_k), threads, lds);
+      &blocks, kernel_for(threads, M, norm, max_k), threads, lds);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
@@ -437,11 +468,10 @@ size_t bl_group_lds_bytes(int M, int max_k) {
 
 hipError_t bl_group_plan(int M, int max_k, bool norm, int* threads, int* per_cu) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
-  const bool preq = bl_group_prequantizes(M);
   for (int nt : {256, 512}) {
     if (lds > 64 * 1024) {
       const hipError_t e =
-          hipFuncSetAttribute(kernel_for(nt, preq, norm, max_k),
+          hipFuncSetAttribute(kernel_for(nt, M, norm, max_k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
@@ -449,13 +479,13 @@ hipError_t bl_group_plan(int M, int max_k, bool norm, int* threads, int* per_cu)
   // Four-wave workgroups while at least two fit on a compute unit (more,
   // shorter weight streams); eight-wave ones when the activations take so
   // much LDS that only one does.
-  const int b256 = blocks_per_cu(256, preq, norm, lds, max_k);
+  const int b256 = blocks_per_cu(256, M, norm, lds, max_k);
   if (b256 >= 2) {
     *threads = 256;
     *per_cu = b256;
   } else {
     *threads = 512;
-    *per_cu = blocks_per_cu(512, preq, norm, lds, max_k);
+    *per_cu = blocks_per_cu(512, M, norm, lds, max_k);
   }
   return hipSuccess;
 }
@@ -471,10 +501,10 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
     if (e != hipSuccess) return e;
   }
   if (threads == 512)
-    launch<512>(preq, norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                sx, rs, s);
+    launch<512>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq, sx, rs,
+                s);
   else
-    launch<256>(preq, norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
-                sx, rs, s);
+    launch<256>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq, sx, rs,
+                s);
   return hipGetLastError();
 }
