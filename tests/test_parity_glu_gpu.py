@@ -105,7 +105,7 @@ def test_forward_q_glu_matches_forward(dev, bl, orc, M, K, N):
     assert np.array_equal(a.cpu().numpy()[rows], orc.glu_relu2(y_full))
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 64])
+@pytest.mark.parametrize("M", [1, 3, 4, 16, 64])
 def test_group_glu_matches_oracle(dev, bl, orc, M):
     # gated gate+up layers next to plain ones, in every grouped mode
     shapes = [(2560, 3840, None), (2560, 13824, "relu2_glu"), (6912, 2560, None),

@@ -129,7 +129,7 @@ def test_forward_rmsnorm_matches_oracle(dev, bl, orc, M, K, N, kind, epi):
     assert _rel(Y.cpu().numpy()[rows], y_ref) <= REL_TOL
 
 
-@pytest.mark.parametrize("M", [1, 4, 8, 16, 64])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16, 64])
 def test_group_rmsnorm_matches_oracle(dev, bl, orc, M):
     # layers with and without a gain in one group; M <= 4 applies subln in
     # the grouped kernel's own quantization, larger M in the quantization
