@@ -351,8 +351,9 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
 }
 
 // Per-token quantization of every layer's activations (one workgroup per
-// layer and token) into the workspace, for the larger token counts.
-__global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restrict__ ops, int M,
+// layer and token) into the workspace, for the larger token counts.  This
+// two-pass form serves layers wider than the one-pass kernel below takes.
+__global__ __launch_bounds__(256) void group_quant_loop_kernel(const GroupOp* __restrict__ ops, int M,
                                                           int8_t* __restrict__ xq,
                                                           float* __restrict__ sx,
                                                           int* __restrict__ rs) {
@@ -382,6 +383,47 @@ __global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restr
     const float sc = q.a_c / kQmax;
     sx[op * M + m] = g ? sc * q.r : sc;
     rs[op * M + m] = sum;
+  }
+}
+
+// One pass for layers of at most KCH * 2048 columns: the row's chunks (and
+// any subln gains) are loaded at entry and stay in registers through the
+// max reduction; same arithmetic, in the same order, as the two-pass form.
+template <int DT, int KCH>
+__device__ __forceinline__ void group_quant_row(const GroupOp& o, int m, int8_t* dst,
+                                                float* red_f, int* red_i, double* red_d,
+                                                float* s_scale, int* s_rowsum) {
+  Chunk<DT> ch[KCH];
+  load_row<DT, 256, KCH>(o.X, m, o.K, ch);
+  Gains<256, KCH> gn;
+  load_gains<256, KCH>(o.norm_gain, o.K, gn);  // no gain: an empty range, zeros
+  if (o.norm_gain)
+    quantize_row<DT, 256, KCH, true>(ch, o.K, dst, red_f, red_i, s_scale, s_rowsum, &gn, true,
+                                     o.norm_eps, red_d);
+  else
+    quantize_row<DT, 256, KCH, false>(ch, o.K, dst, red_f, red_i, s_scale, s_rowsum);
+}
+
+template <int KCH>
+__global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restrict__ ops, int M,
+                                                          int8_t* __restrict__ xq,
+                                                          float* __restrict__ sx,
+                                                          int* __restrict__ rs) {
+  __shared__ float red_f[4];
+  __shared__ int red_i[4];
+  __shared__ double red_d[4];
+  __shared__ float s_scale;
+  __shared__ int s_rowsum;
+  const int op = blockIdx.x / M, m = blockIdx.x % M;
+  const GroupOp o = ops[op];
+  int8_t* dst = xq + o.xq_off + (int64_t)m * o.K;
+  if (o.dtype == 1)
+    group_quant_row<1, KCH>(o, m, dst, red_f, red_i, red_d, &s_scale, &s_rowsum);
+  else
+    group_quant_row<0, KCH>(o, m, dst, red_f, red_i, red_d, &s_scale, &s_rowsum);
+  if (threadIdx.x == 0) {  // thread 0 wrote both
+    sx[op * M + m] = s_scale;
+    rs[op * M + m] = s_rowsum;
   }
 }
 
@@ -455,10 +497,19 @@ int blocks_per_cu(int threads, int M, bool norm, size_t lds, int max_k) {
 
 bool bl_group_prequantizes(int M) { return M > kGroupInlineQuantMaxM; }
 
-hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int8_t* xq, float* sx,
-                                 int* rs, hipStream_t s) {
-  hipLaunchKernelGGL(group_quant_kernel, dim3((unsigned)(n_ops * M)), dim3(256), 0, s, ops, M,
-                     xq, sx, rs);
+hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int max_k, int8_t* xq,
+                                 float* sx, int* rs, hipStream_t s) {
+  const dim3 grid((unsigned)(n_ops * M)), block(256);
+  if (max_k <= 2048)
+    hipLaunchKernelGGL(group_quant_kernel<1>, grid, block, 0, s, ops, M, xq, sx, rs);
+  else if (max_k <= 4096)
+    hipLaunchKernelGGL(group_quant_kernel<2>, grid, block, 0, s, ops, M, xq, sx, rs);
+  else if (max_k <= 8192)
+    hipLaunchKernelGGL(group_quant_kernel<4>, grid, block, 0, s, ops, M, xq, sx, rs);
+  else if (max_k <= 12288)
+    hipLaunchKernelGGL(group_quant_kernel<6>, grid, block, 0, s, ops, M, xq, sx, rs);
+  else
+    hipLaunchKernelGGL(group_quant_loop_kernel, grid, block, 0, s, ops, M, xq, sx, rs);
   return hipGetLastError();
 }
 
@@ -497,7 +548,7 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
   const size_t lds = bl_group_lds_bytes(M, max_k);
   const bool preq = bl_group_prequantizes(M);
   if (preq) {
-    const hipError_t e = bl_launch_group_quant(ops, n_ops, M, xq, sx, rs, s);
+    const hipError_t e = bl_launch_group_quant(ops, n_ops, M, max_k, xq, sx, rs, s);
     if (e != hipSuccess) return e;
   }
   if (threads == 512)

@@ -82,6 +82,6 @@ hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_item
                                 const int8_t* xq, const float* sx, const int* rs, bool glu,
                                 hipStream_t s);
 // The quantization launch of the grouped forward (one workgroup per layer
-// and token) into xq / sx / rs at each layer's xq_off.
-hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int8_t* xq, float* sx,
-                                 int* rs, hipStream_t s);
+// and token) into xq / sx / rs at each layer's xq_off; max_k the largest K.
+hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int max_k, int8_t* xq,
+                                 float* sx, int* rs, hipStream_t s);
