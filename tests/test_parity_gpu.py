@@ -130,7 +130,11 @@ def test_pack_unpack(dev, bl, orc, N, K):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,K,kind", [(4, 256, "normal_f32"), (1, 2560, "normal_bf16"),
                                       (16, 6912, "normal_bf16"), (2048, 2560, "outlier_bf16"),
-                                      (64, 11008, "student_t3_bf16"), (3, 4096, "normal_f32")])
+                                      (64, 11008, "student_t3_bf16"), (3, 4096, "normal_f32"),
+                                      # one-pass rows up to 16384 columns (ragged past 12288),
+                                      # the two-pass loop beyond
+                                      (2, 12304, "student_t3_bf16"), (5, 16384, "normal_bf16"),
+                                      (3, 16400, "normal_f32"), (2, 20480, "normal_bf16")])
 def test_quantize_acts_bit_exact(dev, bl, orc, M, K, kind):
     X, is_bf16 = wl.gen_acts(M * 7 + K, M, K, kind)
     if not is_bf16:

@@ -79,7 +79,8 @@ def _expected(orc, X, is_bf16, g, qw, gc, relu2):
 
 @pytest.mark.parametrize("M,K,kind", [(1, 2560, "normal_bf16"), (5, 256, "normal_f32"),
                                       (300, 6912, "outlier_bf16"), (64, 4096, "student_t3_bf16"),
-                                      (3, 11008, "normal_f32")])
+                                      (3, 11008, "normal_f32"), (2, 16384, "normal_bf16"),
+                                      (2, 20480, "normal_f32")])
 def test_quantize_acts_rmsnorm_matches_oracle(dev, bl, orc, M, K, kind):
     X, is_bf16 = wl.gen_acts(9100 + M, M, K, kind)
     g = wl.gen_gain(9200 + K, K)
