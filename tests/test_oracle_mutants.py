@@ -48,6 +48,16 @@ MUTANTS = {
     "glu_not_squared": ("      float t = r * r;", "      float t = r;"),
     "glu_pack_rows": ("  return i < 8 ? 8 * t + i : N / 2 + 8 * t + (i - 8);",
                       "  return i < 8 ? 16 * t + i : N / 2 + 8 * t + (i - 8);"),
+    # other orders of the same float operations (R4, R2, R12, R8)
+    "acts_x127_over_a": ("float v = rintf(x[k] * qs);", "float v = rintf(x[k] * 127.0f / a_c);"),
+    "acts_x_over_scale": ("float v = rintf(x[k] * qs);",
+                          "float v = rintf(x[k] / (a_c / 127.0f));"),
+    "ternary_reciprocal": ("float v = rintf(W[i] / gamma_c);",
+                           "float v = rintf(W[i] * (1.0f / gamma_c));"),
+    "glu_other_association": ("      float t = r * r;\n      h[m * F + f] = t * y[m * N + F + f];",
+                              "      float t = r * y[m * N + F + f];\n      h[m * F + f] = r * t;"),
+    "norm_factor_in_float": ("float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));",
+                             "float r = 1.0f / sqrtf((float)(S / (double)K) + eps_n);"),
 }
 
 

@@ -587,3 +587,168 @@ def test_glu_relu2_unit_up_is_relu2_and_nonpositive_gate(orc):
     assert np.array_equal(orc.glu_relu2(y), orc.relu2(g))
     y2 = np.concatenate([-np.abs(g), _acts(123, 3, 64)], axis=1)
     assert np.all(orc.glu_relu2(y2) == 0)
+
+
+# --------------------------------------------------------------------------
+# Evaluation order of the float steps (R2, R4, R12; also R8's factor).  The
+# pages give the quantizers in words; each reading fixes one order of float
+# operations.  Hand-worked separating cases (tests/golden/order_cases.txt)
+# and exact-arithmetic sweeps tell the stated order apart from the plausible
+# others: x*127/a or x/s_x for R4, a reciprocal multiply for R2, r*(r*up)
+# for R12, and a float RMS factor for R8.
+# --------------------------------------------------------------------------
+def _bits(h) -> np.float32:
+    return np.array([int(h, 16)], np.uint32).view(np.float32)[0]
+
+
+def _fl(q: Fraction) -> Fraction:
+    """One rounding of a rational to float32, nearest even (signed)."""
+    if q < 0:
+        return -Fraction(float(round_to_f32(-q)))
+    return Fraction(float(round_to_f32(q)))
+
+
+def _rint_half_even(v: Fraction) -> int:
+    return _rint_even(v)
+
+
+def _clamp127(v: int) -> int:
+    return max(-127, min(127, v))
+
+
+def test_acts_order_golden(orc):
+    kv = _read_kv("order_cases.txt")
+    a, x = _bits(kv["r4_amax_bits"][0]), _bits(kv["r4_x_bits"][0])
+    row = np.zeros((1, 16), np.float32)
+    row[0, 0], row[0, 1] = a, x
+    q, s, _ = orc.quant_acts(row)
+    assert q[0, 0] == 127
+    assert q[0, 1] == int(kv["r4_q"][0]) != int(kv["r4_q_other_orders"][0])
+    assert s[0] == np.float32(a / np.float32(127))
+
+
+def test_acts_order_sweep_exact(orc):
+    # For random row maxima a, put x at the float32 values nearest to the
+    # points where x * fl(127/a) crosses a half-integer; whenever the stated
+    # order (x times fl(127/a)) and x*127/a or x/fl(a/127) round to different
+    # codes in exact arithmetic, the oracle must give the stated order's code.
+    rng = _rng(131)
+    rows, want = [], []
+    separating = 0
+    for a in rng.uniform(0.05, 40.0, 24).astype(np.float32):
+        A = Fraction(float(a))
+        qs = _fl(Fraction(127) / A)
+        sx = _fl(A / 127)
+        xs = []
+        for j in range(0, 127, 3):
+            c = np.float32(float((Fraction(2 * j + 1, 2)) / qs))
+            for d in (-2, -1, 0, 1, 2):
+                xv = np.float32(c + np.float32(d) * np.spacing(c))
+                if not (0 < xv < a):
+                    continue
+                X_ = Fraction(float(xv))
+                mine = _clamp127(_rint_half_even(_fl(X_ * qs)))
+                o1 = _clamp127(_rint_half_even(_fl(_fl(X_ * 127) / A)))
+                o2 = _clamp127(_rint_half_even(_fl(X_ / sx)))
+                if mine != o1 or mine != o2:
+                    separating += 1
+                xs.append((xv, mine))
+        for i in range(0, len(xs), 255):
+            part = xs[i:i + 255]
+            r = np.zeros(256, np.float32)
+            r[0] = a
+            e = np.zeros(256, np.int64)
+            e[0] = 127
+            for k, (xv, mine) in enumerate(part, start=1):
+                r[k], e[k] = xv, mine
+            rows.append(r)
+            want.append(e)
+    assert separating >= 20, separating  # the sweep does tell the orders apart
+    q, _, _ = orc.quant_acts(np.array(rows))
+    assert np.array_equal(q.astype(np.int64), np.array(want))
+
+
+def test_ternary_division_golden(orc):
+    kv = _read_kv("order_cases.txt")
+    g, w = _bits(kv["r2_gamma_bits"][0]), _bits(kv["r2_w_bits"][0])
+    q = orc.ternarize(np.array([[w, -w]], np.float32), g)
+    assert q[0, 0] == int(kv["r2_q"][0]) != int(kv["r2_q_reciprocal"][0])
+    assert q[0, 1] == -int(kv["r2_q"][0])
+
+
+def test_ternary_division_sweep_near_half(orc):
+    # Many scales, and weights within 16 float32 steps of gamma/2: the codes
+    # must follow the closed form of a true division, and the sweep must hold
+    # weights where a reciprocal multiply would round to the other side.
+    rng = _rng(132)
+    straddle = 0
+    for gc in rng.uniform(1e-3, 0.1, 60).astype(np.float32):
+        half = np.float32(gc / np.float32(2))
+        vals = [np.float32(half + np.float32(d) * np.spacing(half)) for d in range(-16, 17)]
+        W = np.array(vals + [-v for v in vals], np.float32).reshape(1, -1)
+        q = orc.ternarize(W, gc)
+        assert np.array_equal(q, _closed_form_ternary(W, gc))
+        G = Fraction(float(gc))
+        inv = _fl(1 / G)
+        for v in vals:
+            V = Fraction(float(v))
+            if (_rint_half_even(_fl(V / G)) != 0) != (_rint_half_even(_fl(V * inv)) != 0):
+                straddle += 1
+    assert straddle >= 10, straddle
+
+
+def test_glu_association_golden(orc):
+    kv = _read_kv("order_cases.txt")
+    g, u = _bits(kv["r12_gate_bits"][0]), _bits(kv["r12_up_bits"][0])
+    h = orc.glu_relu2(np.array([[g, u]], np.float32))
+    assert h.view(np.uint32)[0, 0] == int(kv["r12_h_bits"][0], 16)
+    assert int(kv["r12_h_bits"][0], 16) != int(kv["r12_h_other_association_bits"][0], 16)
+
+
+def test_glu_association_random_exact(orc):
+    # Non-integer gates and ups, where the associations round differently:
+    # the result is fl(fl(r*r)*up) exactly.
+    rng = _rng(133)
+    F = 512
+    gate = rng.uniform(-0.1, 0.1, (4, F)).astype(np.float32)
+    up = rng.uniform(-2.0, 2.0, (4, F)).astype(np.float32)
+    h = orc.glu_relu2(np.concatenate([gate, up], axis=1))
+    differ = 0
+    for m in range(4):
+        for f in range(F):
+            r = Fraction(float(max(gate[m, f], np.float32(0))))
+            U = Fraction(float(up[m, f]))
+            want = _fl(_fl(r * r) * U)
+            other = _fl(r * _fl(r * U))
+            differ += want != other
+            assert Fraction(float(h[m, f])) == want
+    assert differ >= 10, differ
+
+
+def test_rmsnorm_factor_correctly_rounded(orc):
+    # With a unit gain the scale is fl(s0 * r), s0 the plain scale and r the
+    # RMS factor rounded once to float from (nearly) exact arithmetic: the
+    # double sum and square root keep it within 1e-15 of exact, far inside
+    # half a float32 step, except at near-ties, which are skipped.
+    from decimal import Decimal, getcontext
+
+    getcontext().prec = 50
+    M, K = 64, 256
+    eps = np.float32(1e-5)
+    X = _acts(134, M, K, 1.5)
+    X *= np.exp2(_rng(135).integers(-3, 4, (M, 1))).astype(np.float32)
+    q, s, _ = orc.quant_acts_rmsnorm(X, np.ones(K, np.float32), float(eps))
+    _, s0, _ = orc.quant_acts(X)
+    checked = 0
+    for m in range(M):
+        S = sum(Fraction(float(v)) ** 2 for v in X[m])
+        inner = S / K + Fraction(float(eps))
+        d = Decimal(inner.numerator) / Decimal(inner.denominator)
+        r_exact = Fraction(1 / d.sqrt())
+        r = _fl(r_exact)
+        ulp = Fraction(float(np.spacing(np.float32(float(r)))))
+        if abs(abs(r_exact - r) - ulp / 2) < ulp * Fraction(1, 1 << 20):
+            continue  # near a rounding tie
+        checked += 1
+        assert Fraction(float(s[m])) == _fl(Fraction(float(s0[m])) * r), m
+    assert checked >= M - 2
