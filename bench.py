@@ -1,26 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the W1.58A8 BitLinear forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens M]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--tokens M] [--grouped | --per-linear] [--no-sub] [--no-cpu]
 
 A step is one pass of the per-token hot path over one batch of synthetic
 input: per-token absmax int8 quantization, load + unpack of the packed
 ternary weights, the int32 contraction, the float rescale (and ReLU^2 where
 the workload has it) for every linear of the workload.  Weights are quantized
-and packed once, before timing (offline, as the packed form is what a model
-stores); that offline pass is timed separately and reported as
-``offline_weight_quant_ms``.
+and packed once, before timing (offline: the packed form is what a model
+stores); that pass is timed separately (``offline_weight_quant_ms``).
 
-Default workload: the decode GEMV pair at M=1 (up 2560->6912, ReLU^2, down
-6912->2560, bf16 activations).  Its 8.85 MB of packed weights would sit in
-the 256 MB Infinity Cache, so steps rotate over enough weight copies that
-the weights stream from HBM.
+Default line: the whole decode step of the 2B-shape model at M = 1 -- 30
+layers of QKV 2560->3840, O 2560->2560, gate+up 2560->13824 and down
+6912->2560, 120 linears, 521 MB of packed weights -- run as one grouped
+forward per step ("µs/token for all linears").  Two weight sets alternate, so
+no step finds its weights in the 256 MB Infinity Cache.  The same JSON line
+carries keyed sub-records (``sub``) for the decode GEMV pair (M = 1, up ->
+ReLU^2 -> down, 61 rotating weight copies), the 2B step at M = 4 and 16, and
+the prefill GEMMs at M = 2048 (int8 TOPS).
 
-The K timed steps run as one HIP graph replay on torch's stream, bracketed
-by synchronizations; the JSON line carries whole-step throughput (``value``),
-the roofline of the dominant kernel (timed with HIP events around a graph of
-back-to-back launches of that kernel alone), and the CPU oracle timed on a
-bounded sample of the same workload on this host.
+Timing: W warm-up steps, then exactly K steps, each as one HIP graph replay
+on torch's stream, bracketed by synchronizations; HIP events around the
+timed replay give ``ms_per_step``, the host clock gives the wall time
+(reported beside it).  Weight copies are indexed from the warm-up's end, so
+the timed steps read copies the warm-up did not.  The ``roofline`` object is
+that of the dominant kernel: for the default line the grouped decode kernel
+(one launch per step, so its average launch time is the event time of the
+timed region divided by K).  ``cpu_baseline`` is the CPU oracle timed on a
+bounded sample of the same workload on this host, with all the host's
+threads and with one.
 """
 from __future__ import annotations
 
@@ -55,20 +64,26 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="decode_gemv_pair_m1")
+    p.add_argument("--workload", default="decode_step_2b")
     p.add_argument("--tokens", type=int, default=None, help="M for multi-M workloads")
-    p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="time budget of the CPU oracle sample")
+    mode = p.add_mutually_exclusive_group()
+    mode.add_argument("--grouped", dest="grouped", action="store_true", default=None,
+                      help="run all linears of a step as one grouped forward (the default "
+                           "for the multi-layer decode steps)")
+    mode.add_argument("--per-linear", dest="grouped", action="store_false",
+                      help="one forward call per linear")
+    p.add_argument("--no-sub", action="store_true",
+                   help="only the main line: skip the keyed sub-records")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="time budget of each CPU oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-launches", type=int, default=400,
-                   help="launches of the dominant kernel timed for the roofline")
+                   help="launches of the dominant kernel timed for a per-linear roofline")
     p.add_argument("--glu", action="store_true",
                    help="gated FFN: pack each gate+up linear (N = 2 x the down projection's K) "
                         "for the gated squared-ReLU epilogue (output N/2)")
     p.add_argument("--subln", action="store_true",
                    help="give every linear a subln gain (RMSNorm fused into its quantization)")
-    p.add_argument("--grouped", action="store_true",
-                   help="run all linears of a step as one grouped forward (M <= 4)")
     p.add_argument("--probes", action="store_true",
                    help="only run the context probes: streaming-read bandwidth (1 GiB, a "
                         "2B decode step's 521 MB, one 4.4 MB GEMV's worth) and the int8 "
@@ -80,37 +95,42 @@ def parse():
 
 
 # ---------------------------------------------------------------------------
-# Workload runners: allocate everything up front; step(i) only launches.
+# Workloads: allocate everything up front; step(i) only launches.
 # ---------------------------------------------------------------------------
+def weight_copies(packed_bytes_per_step):
+    """Weight sets to rotate: enough that the bytes between two reads of one
+    set exceed twice the Infinity Cache (at least two sets)."""
+    return int(min(64, max(2, -(-2 * MALL_BYTES // packed_bytes_per_step))))
+
+
 class Linear:
-    def __init__(self, bl, torch, dev, N, K, M, x_dtype, seed, sparse, copies, subln=False,
+    """One linear of a step: `copies` packed weight sets, its activations
+    (the workload's distribution), its output and workspace."""
+
+    def __init__(self, bl, torch, wl, dev, wk, layer, li, shape, M, copies, subln=False,
                  glu=False):
-        self.N, self.K, self.M = N, K, M
+        self.N, self.K, self.M = shape.N, shape.K, M
         self.epi = "relu2_glu" if glu else None
-        gen = torch.Generator(device=dev)
         self.packed, self.gamma = [], []
         t0 = time.perf_counter()
         for c in range(copies):
-            gen.manual_seed(seed * 131 + c)
-            W = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
-            if sparse > 0:
-                mask = torch.rand((N, K), generator=gen, device=dev) < sparse
-                W = torch.where(mask, W * 1e-3, W)
+            # copy 0 uses the seed the parity tests use; the others differ
+            seed = wl.weight_seed(wk.key, layer, li) + 100003 * c
+            W = wl.gen_weight_device(seed, self.N, self.K, wk.weight_sparse_frac, dev)
             p, g = bl.quantize_weights(W, glu=glu)
             self.packed.append(p)
             self.gamma.append(g)
             del W
         torch.cuda.synchronize()
         self.quant_s = time.perf_counter() - t0
-        gen.manual_seed(seed * 131 + 7777)
-        X = torch.randn((M, K), generator=gen, device=dev, dtype=torch.float32)
-        self.X = X.to(x_dtype) if x_dtype is not None else X
-        self.Y = torch.empty((M, N // 2 if glu else N), dtype=torch.float32, device=dev)
+        self.seed_x = wl.act_seed(wk.key, layer, li)
+        self.X = make_acts(torch, wl, self.seed_x, M, self.K, wk.x_kind, dev)
+        self.Y = torch.empty((M, self.N // 2 if glu else self.N), dtype=torch.float32,
+                             device=dev)
         self.gain = None
         if subln:  # gains uniform on [0.5, 1.5)
-            gen.manual_seed(seed * 131 + 8888)
-            self.gain = torch.rand(K, generator=gen, device=dev, dtype=torch.float32) + 0.5
-        ws = bl.workspace_bytes(M, K, N)
+            self.gain = torch.from_numpy(wl.gen_gain(self.seed_x + 1, self.K)).to(dev)
+        ws = bl.workspace_bytes(M, self.K, self.N)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev) if ws > 0 else None
 
     def bytes(self):
@@ -123,68 +143,121 @@ class Linear:
         return 2 * self.M * self.N * self.K
 
 
-def build_runner(args, bl, torch, wl, dev):
-    wk = wl.WORKLOADS[args.workload]
-    M = args.tokens if args.tokens is not None else wk.tokens[0]
-    if M not in wk.tokens:
-        log(f"note: M={M} is not one of the workload's token counts {wk.tokens}")
-    x_dtype = torch.bfloat16 if wk.x_kind.endswith("bf16") else None
-    packed_per_step = wk.weights_per_step // 4
-    # weight copies: enough that the bytes cycled through exceed 2x the MALL
-    copies = max(1, -(-2 * MALL_BYTES // packed_per_step))
-    copies = min(copies, 64)
-    lins = []
-    downs_k = {l.K for l in wk.linears}
-    for layer, li, shape in wl.step_linears(wk):
-        glu = bool(args.glu) and shape.N % 2 == 0 and shape.N // 2 in downs_k and \
-            shape.N // 2 != shape.K
-        lins.append(Linear(bl, torch, dev, shape.N, shape.K, M, x_dtype,
-                           wl.weight_seed(wk.key, layer, li), wk.weight_sparse_frac, copies,
-                           subln=args.subln, glu=glu))
-    if wk.chain_relu2:
-        # up (ReLU^2) feeds down: down's input is up's float output
-        up, down = lins
-        down.X = up.Y
+def make_acts(torch, wl, seed, M, K, x_kind, dev):
+    """Activations of the workload's kind (bf16 as torch.bfloat16)."""
+    X, is_bf16 = wl.gen_acts(seed, M, K, x_kind)
+    t = torch.from_numpy(X).to(dev)
+    return t.view(torch.bfloat16) if is_bf16 else t
 
-    groups = None
-    if args.grouped:
-        if wk.chain_relu2:
-            raise SystemExit("--grouped needs independent linears")
-        groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, l.epi, l.Y, l.gain)
-                            for l in lins])
-                  for c in range(copies)]
 
-    def step(i):
-        c = i % copies
-        if groups is not None:
-            groups[c].forward()
-            return
+class Runner:
+    """A workload at M tokens: its linears and a step function."""
+
+    def __init__(self, bl, torch, wl, dev, key, M, grouped, copies=None, subln=False,
+                 glu=False, share_weights=None):
+        wk = wl.WORKLOADS[key]
+        self.wk, self.M = wk, M
+        self.copies = copies or weight_copies(wk.weights_per_step // 4)
+        downs_k = {l.K for l in wk.linears}
+        self.lins = []
+        for idx, (layer, li, shape) in enumerate(wl.step_linears(wk)):
+            g = bool(glu) and shape.N % 2 == 0 and shape.N // 2 in downs_k and \
+                shape.N // 2 != shape.K
+            if share_weights is not None:
+                lin = Linear.__new__(Linear)
+                src = share_weights.lins[idx]
+                lin.N, lin.K, lin.M, lin.epi = src.N, src.K, M, src.epi
+                lin.packed, lin.gamma, lin.quant_s = src.packed, src.gamma, 0.0
+                lin.seed_x = src.seed_x + 100 * M
+                lin.X = make_acts(torch, wl, lin.seed_x, M, lin.K, wk.x_kind, dev)
+                lin.Y = torch.empty((M, src.Y.shape[1]), dtype=torch.float32, device=dev)
+                lin.gain = None
+                if src.gain is not None:
+                    lin.gain = src.gain
+                ws = bl.workspace_bytes(M, lin.K, lin.N)
+                lin.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev) if ws > 0 else None
+            else:
+                lin = Linear(bl, torch, wl, dev, wk, layer, li, shape, M, self.copies,
+                             subln=subln, glu=g)
+            self.lins.append(lin)
+        if share_weights is not None:
+            self.copies = share_weights.copies
         if wk.chain_relu2:
-            up, down = lins
+            up, down = self.lins  # up's float output feeds down
+            down.X = up.Y
+        self.groups = None
+        if grouped:
+            if wk.chain_relu2:
+                raise SystemExit("a grouped forward needs independent linears")
+            self.groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, l.epi, l.Y, l.gain)
+                                     for l in self.lins])
+                           for c in range(self.copies)]
+        self.bl = bl
+        self.offset = 0  # first copy of the timed region
+
+    def step(self, i):
+        bl = self.bl
+        c = (i + self.offset) % self.copies
+        if self.groups is not None:
+            self.groups[c].forward()
+        elif self.wk.chain_relu2:
+            up, down = self.lins
             bl.forward(up.X, up.packed[c], up.gamma[c], up.N, epilogue="relu2", out=up.Y,
                        workspace=up.ws, norm_gain=up.gain)
             bl.forward(down.X, down.packed[c], down.gamma[c], down.N, out=down.Y,
                        workspace=down.ws, norm_gain=down.gain)
         else:
-            for lin in lins:
+            for lin in self.lins:
                 bl.forward(lin.X, lin.packed[c], lin.gamma[c], lin.N, epilogue=lin.epi,
                            out=lin.Y, workspace=lin.ws, norm_gain=lin.gain)
 
-    return wk, M, lins, copies, step, groups
+    def bytes_step(self):
+        # In the ReLU^2 chain the hidden vector counts twice: written by the up
+        # projection and read by the down projection, as on the device.
+        return sum(l.bytes() for l in self.lins)
+
+    def ops_step(self):
+        return sum(l.ops() for l in self.lins)
+
+    def quant_ms(self):
+        return sum(l.quant_s for l in self.lins) * 1e3 / self.copies
 
 
-def capture(torch, fn, count):
+def capture(torch, fn, count, first=0):
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        fn(0)  # one eager pass to settle any lazy initialisation
+        fn(first)  # one eager pass to settle any lazy initialisation
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        for i in range(count):
+        for i in range(first, first + count):
             fn(i)
     return g
+
+
+def time_steps(torch, runner, steps, warmup):
+    """W warm-up steps (copies 0..W-1), then exactly K timed steps (copies
+    from W on) as one graph replay between synchronizations.  Returns
+    (event ms per step, wall ms per step)."""
+    runner.offset = 0
+    if warmup > 0:
+        gw = capture(torch, runner.step, warmup)
+        gw.replay()
+        torch.cuda.synchronize()
+        del gw
+    runner.offset = warmup
+    g = capture(torch, runner.step, steps)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall * 1e3 / steps
 
 
 def time_graph(torch, fn, count):
@@ -200,18 +273,33 @@ def time_graph(torch, fn, count):
     return e0.elapsed_time(e1) * 1e3 / count
 
 
-def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
+def hbm_roof(bytes_, us, key, src):
+    achieved = bytes_ / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(source_hash(src), key), "kernel": key,
+            "kernel_us": round(us, 3)}
+
+
+def mfma_roof(ops, us, key, src):
+    achieved = ops / (us * 1e-6) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
+            "traffic": traffic_from_profile(source_hash(src), key), "kernel": key,
+            "kernel_us": round(us, 3)}
+
+
+def roofline_single(args, torch, bl, runner, metric_kind):
     """The linear with the most packed bytes, launched alone back to back
-    (rotating its weight copies) in a graph bracketed by HIP events."""
+    (rotating its weight copies) in a graph bracketed by HIP events.  For the
+    MFMA-bound case, the GEMM launch alone (activations quantized
+    beforehand)."""
+    wk, lins, M = runner.wk, runner.lins, runner.M
     dom = max(lins, key=lambda l: l.N * l.K)
     epi = "relu2" if (wk.chain_relu2 and dom is lins[0]) else dom.epi
-    n = args.kernel_launches
     copies = len(dom.packed)
     gemm = metric_kind == "tops" and dom.ws is not None
     if gemm:
-        # The GEMM launch alone, from activations quantized beforehand (the
-        # forward's other launch, the per-token quantization, is not the
-        # contraction being measured).
         Xq, sx, rs = bl.quantize_acts(dom.X, norm_gain=dom.gain)
         qws = bl.forward_q_workspace(dom.M, dom.K, dom.N, dom.X.device)
 
@@ -224,81 +312,55 @@ def roofline_single(args, torch, bl, wk, M, lins, metric_kind):
             bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
                        workspace=dom.ws, norm_gain=dom.gain)
 
-    us = time_graph(torch, dom_step, n)
+    us = time_graph(torch, dom_step, args.kernel_launches)
     if metric_kind == "tops":
-        achieved = dom.ops() / (us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-        key = f"gemm_q_{dom.K}x{dom.N}_m{M}"
-        src = source_hash(GEMM_SOURCES)
+        roof = mfma_roof(dom.ops(), us, f"gemm_q_{dom.K}x{dom.N}_m{M}", GEMM_SOURCES)
+        roof["launches_timed"] = "gemm only (forward_q)"
     else:
-        achieved = dom.bytes() / (us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        key = f"gemv_{dom.K}x{dom.N}_m{M}"
-        src = source_hash(GEMV_SOURCES)
-    roof["traffic"] = traffic_from_profile(src, key)
-    roof["kernel"] = key
-    roof["kernel_us"] = round(us, 3)
-    roof["launches_timed"] = "gemm only (forward_q)" if gemm else (
-        "quantization + gemm" if dom.ws is not None else "one fused launch")
-    log(f"dominant forward {key}: {us:.3f} us per call")
-    return roof
-
-
-def roofline_grouped(args, torch, step, bytes_step, ops_step, wk, M, n_lin, metric_kind):
-    """The grouped forward of a whole step (quantization included).  Up to 16
-    tokens it streams the weights (HBM roof); above, it is one tiled int8 GEMM
-    over all linears, and from 128 tokens on (where the step's ops per weight
-    byte pass the chip's 625) the matrix cores bound it."""
-    n = max(4, args.kernel_launches // 20)
-    us = time_graph(torch, step, n)
-    if metric_kind == "tops":
-        achieved = ops_step / (us * 1e-6) / 1e12
-        key = f"group_gemm_{wk.key}_m{M}"
-        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": INT8_PEAK_TOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4),
-                "traffic": traffic_from_profile(source_hash(GEMM_SOURCES), key)}
-    else:
-        achieved = bytes_step / (us * 1e-6) / 1e9
-        key = f"group_gemv_{wk.key}_m{M}"
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_from_profile(source_hash(GROUP_SOURCES), key)}
-    roof.update({"kernel": key, "kernel_us": round(us, 3),
-                 "launches_per_forward": 1 if M <= 4 else 2})
-    log(f"grouped forward: {us:.3f} us per step ({n_lin} linears)")
+        roof = hbm_roof(dom.bytes(), us, f"gemv_{dom.K}x{dom.N}_m{M}", GEMV_SOURCES)
+        roof["launches_timed"] = "one fused launch" if dom.ws is None else \
+            "quantization + gemm"
+    log(f"dominant forward {roof['kernel']}: {us:.3f} us per call")
     return roof
 
 
 # ---------------------------------------------------------------------------
-# CPU oracle baseline (bounded sample)
+# CPU oracle baseline (bounded samples, all threads and one)
 # ---------------------------------------------------------------------------
-def cpu_baseline(args, wk, M, lins_shapes, metric_kind, budget_s, subln=False):
-    import numpy as np
+def host_description():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    threads = affinity
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        threads = min(threads, int(env))  # the host share this process may use
+    return model, affinity, threads
 
-    import oracle
-    from w1_a8_matmul_amd import workloads as wl
 
-    orc = oracle.get()
-    threads = orc.max_threads()
-    rng_seed = 424242
-    # one layer's linears (the sample); weights quantized by the oracle itself
-    shapes = list(wk.linears)
-    Ms = M if metric_kind != "tops" else min(M, 16)  # prefill: a sample of token rows
+def cpu_sample(orc, wl, wk, Ms, budget_s, subln, seed0=424242):
+    """One layer's linears of the workload at Ms token rows, on the oracle
+    (weights quantized by the oracle itself).  Returns (pass_fn, bytes, ops)."""
     prepared = []
-    for li, lin in enumerate(shapes):
-        W = wl.gen_weight(rng_seed + li, lin.N, lin.K, wk.weight_sparse_frac)
-        _, gc, qw = orc.quantize_weights(W)
+    for li, lin in enumerate(wk.linears):
+        W = wl.gen_weight(seed0 + li, lin.N, lin.K, wk.weight_sparse_frac)
+        _, gc = orc.absmean(W)
+        qw = orc.ternarize(W, gc)
         del W
-        X, is_bf16 = wl.gen_acts(rng_seed + 100 + li, Ms, lin.K, wk.x_kind)
-        g = wl.gen_gain(rng_seed + 200 + li, lin.K) if subln else None
+        X, is_bf16 = wl.gen_acts(seed0 + 100 + li, Ms, lin.K, wk.x_kind)
+        g = wl.gen_gain(seed0 + 200 + li, lin.K) if subln else None
         prepared.append((lin, qw, gc, X, is_bf16, g))
 
     def fwd(X, qw, gc, bf16, g):
         if g is None:
-            y, *_ = orc.forward(X, qw, gc, bf16=bf16)
-            return y
+            return orc.forward(X, qw, gc, bf16=bf16)[0]
         q, s, _ = orc.quant_acts_rmsnorm(X, g, 1e-5, bf16=bf16)
         return orc.rescale(orc.int_matmul(q, qw), s, gc)
 
@@ -311,31 +373,64 @@ def cpu_baseline(args, wk, M, lins_shapes, metric_kind, budget_s, subln=False):
             for lin, qw, gc, X, is_bf16, g in prepared:
                 fwd(X, qw, gc, is_bf16, g)
 
+    nbytes = sum(lin.N * lin.K // 4 + Ms * lin.K * (2 if is_bf16 else 4) + Ms * lin.N * 4 + 4
+                 + (lin.K * 4 if subln else 0) for lin, _, _, _, is_bf16, _ in prepared)
+    if wk.chain_relu2:  # h written and read, as on the device
+        nbytes = sum(lin.N * lin.K // 4 + 4 for lin, *_ in prepared) + \
+            Ms * prepared[0][0].K * 2 + 2 * Ms * prepared[0][0].N * 4 + Ms * prepared[1][0].N * 4
+    ops = sum(2 * Ms * lin.N * lin.K for lin, *_ in prepared)
+    return one_pass, nbytes, ops
+
+
+def time_cpu(one_pass, budget_s):
     one_pass()
-    n = 0
-    t0 = time.perf_counter()
+    n, t0 = 0, time.perf_counter()
     while True:
         one_pass()
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 100000:
-            break
-    per_pass = el / n
-    layer_bytes = sum(lin.N * lin.K // 4 + Ms * lin.K * (2 if is_bf16 else 4) + Ms * lin.N * 4 + 4
-                      for lin, _, _, _, is_bf16, _ in prepared)
-    layer_ops = sum(2 * Ms * lin.N * lin.K for lin, *_ in prepared)
-    if subln:
-        layer_bytes += sum(lin.K * 4 for lin, *_ in prepared)
-    if metric_kind == "tops":
-        value, unit = layer_ops / per_pass / 1e12, "TOPS"
-    else:
-        value, unit = layer_bytes / per_pass / 1e9, "GB/s"
-    sample = (f"{n} passes over one layer's linears ({', '.join(f'{l.K}->{l.N}' for l in shapes)})"
-              f" at M={Ms}, {el:.1f} s; oracle on unpacked int8 weights, OpenMP over outputs")
-    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": sample, "us_per_layer_pass": round(per_pass * 1e6, 1)}
+            return el / n, n, el
 
 
+def cpu_baseline(wl, wk, M, metric_kind, budget_s, subln=False):
+    """The oracle as it stands on this host: all the threads this process may
+    use, then one thread.  Decode: one layer's linears at M; prefill (TOPS):
+    the full M with all threads, a 128-row sample with one thread."""
+    import oracle
+
+    orc = oracle.get()
+    model, affinity, threads = host_description()
+    out = {"kind": "oracle", "cpu_model": model, "host_cpus_in_affinity": affinity}
+    layers = wk.layers
+    runs = []
+    for nthreads in (threads, 1):
+        Ms = M if (metric_kind != "tops" or nthreads > 1) else min(M, 128)
+        orc.set_threads(nthreads)
+        one_pass, nbytes, ops = cpu_sample(orc, wl, wk, Ms, budget_s, subln)
+        per, n, el = time_cpu(one_pass, budget_s)
+        if metric_kind == "tops":
+            value, unit = ops / per / 1e12, "TOPS"
+        else:
+            value, unit = nbytes / per / 1e9, "GB/s"
+        rec = {"value": round(value, 4), "unit": unit, "cores": nthreads,
+               "sample": (f"{n} passes over one layer's linears "
+                          f"({', '.join(f'{l.K}->{l.N}' for l in wk.linears)}) at M={Ms}, "
+                          f"{el:.1f} s; oracle on unpacked int8 weights"
+                          + (", OpenMP over outputs" if nthreads > 1 else "")),
+               "us_per_layer_pass": round(per * 1e6, 1)}
+        if metric_kind != "tops":
+            rec["us_per_token_all_linears"] = round(per * 1e6 * layers / Ms, 1)
+        runs.append(rec)
+    orc.set_threads(threads)
+    out.update(runs[0])
+    out["one_thread"] = runs[1]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Counter summaries, probes
+# ---------------------------------------------------------------------------
 def traffic_from_profile(kernel_src_hash, kernel_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when it is missing or was taken on another version of the kernel."""
@@ -446,6 +541,80 @@ def context_probes(torch):
     print(json.dumps(out), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# Records
+# ---------------------------------------------------------------------------
+def step_record(runner, ev_ms, wall_ms, metric_kind):
+    """Throughput of one workload line from its per-step event time."""
+    bytes_step, ops_step = runner.bytes_step(), runner.ops_step()
+    step_s = ev_ms / 1e3
+    if metric_kind == "tops":
+        value, unit = ops_step / step_s / 1e12, "TOPS"
+    else:
+        value, unit = bytes_step / step_s / 1e9, "GB/s"
+    return {"value": round(value, 3), "unit": unit, "ms_per_step": round(ev_ms, 6),
+            "wall_ms_per_step": round(wall_ms, 6), "us_per_step": round(ev_ms * 1e3, 3),
+            "us_per_token": round(ev_ms * 1e3 / runner.M, 3), "bytes_per_step": bytes_step,
+            "ops_per_step": ops_step, "linears_per_step": len(runner.lins),
+            "weight_copies_rotated": runner.copies,
+            "frac_of_hbm_peak" if metric_kind != "tops" else "frac_of_int8_peak":
+                round(value / (HBM_PEAK_GBS if metric_kind != "tops" else INT8_PEAK_TOPS), 4)}
+
+
+def sub_records(args, torch, bl, wl, dev, main_runner):
+    """Keyed sub-records: decode GEMV pair; the 2B step at M = 4 and 16 (on the
+    main line's weights when it is the 2B step); prefill GEMMs at M = 2048."""
+    subs = {}
+    steps, warmup = max(20, args.steps // 2), max(5, args.warmup // 2)
+
+    # decode GEMV pair, M = 1 (two launches: up with ReLU^2, then down)
+    r = Runner(bl, torch, wl, dev, "decode_gemv_pair_m1", 1, grouped=False, copies=61)
+    ev, wall = time_steps(torch, r, max(steps, 61), warmup)
+    rec = step_record(r, ev, wall, "hbm")
+    rec["roofline"] = roofline_single(args, torch, bl, r, "hbm")
+    rec["launches_per_step"] = 2
+    subs["decode_gemv_pair_m1"] = rec
+    del r
+
+    # 2B step at M = 4 and 16, grouped
+    share = main_runner if (main_runner.wk.key == "decode_step_2b" and
+                            main_runner.groups is not None) else None
+    for M in (4, 16):
+        r = Runner(bl, torch, wl, dev, "decode_step_2b", M, grouped=True, share_weights=share)
+        ev, wall = time_steps(torch, r, steps, warmup)
+        rec = step_record(r, ev, wall, "hbm")
+        rec["launches_per_step"] = 1 if M <= 4 else 2
+        subs[f"decode_step_2b_m{M}"] = rec
+        del r
+    torch.cuda.empty_cache()
+
+    # prefill, M = 2048: the whole step (two quantizations + two GEMMs) and each
+    # GEMM launch alone
+    r = Runner(bl, torch, wl, dev, "prefill_m2048", 2048, grouped=False, copies=2)
+    ev, wall = time_steps(torch, r, steps, warmup)
+    rec = step_record(r, ev, wall, "tops")
+    for lin in r.lins:
+        Xq, sx, rs = bl.quantize_acts(lin.X)
+        qws = bl.forward_q_workspace(lin.M, lin.K, lin.N, dev)
+
+        def one(i, lin=lin, Xq=Xq, sx=sx, rs=rs, qws=qws):
+            c = i % len(lin.packed)
+            bl.forward_q(Xq, sx, rs, lin.packed[c], lin.gamma[c], lin.N, out=lin.Y,
+                         workspace=qws)
+
+        us = time_graph(torch, one, 100)
+        rec[f"gemm_{lin.K}x{lin.N}"] = mfma_roof(lin.ops(), us, f"gemm_q_{lin.K}x{lin.N}_m2048",
+                                                 GEMM_SOURCES)
+    subs["prefill_m2048"] = rec
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, r.wk, 2048, "tops", args.cpu_seconds / 2)
+        rec["cpu_baseline"] = cpu
+        log(f"cpu oracle (prefill): {cpu}")
+    del r
+    torch.cuda.empty_cache()
+    return subs
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -469,63 +638,58 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    wk, M, lins, copies, step, groups = build_runner(args, bl, torch, wl, dev)
-    quant_s = sum(l.quant_s for l in lins)
-    n_weights = sum(l.N * l.K for l in lins) * copies
-    log(f"workload {wk.key} M={M}: {len(lins)} linears, {copies} weight copies, "
-        f"offline quantization {quant_s*1e3:.1f} ms for {n_weights/1e6:.1f} M weights")
-
-    # In the ReLU^2 chain the hidden vector h counts twice: written by the up
-    # projection and read by the down projection, as it is on the device.
-    bytes_step = sum(l.bytes() for l in lins)
-    ops_step = sum(l.ops() for l in lins)
+    wk = wl.WORKLOADS[args.workload]
+    M = args.tokens if args.tokens is not None else wk.tokens[0]
+    if M not in wk.tokens:
+        log(f"note: M={M} is not one of the workload's token counts {wk.tokens}")
+    grouped = args.grouped
+    if grouped is None:  # default: grouped for the multi-layer decode steps
+        grouped = wk.layers > 1 and M <= 64 and not wk.chain_relu2
+    runner = Runner(bl, torch, wl, dev, args.workload, M, grouped, subln=args.subln,
+                    glu=args.glu)
+    log(f"workload {wk.key} M={M}: {len(runner.lins)} linears, {runner.copies} weight "
+        f"copies, offline quantization {runner.quant_ms():.1f} ms per weight set")
     metric_kind = "tops" if M >= 128 else "hbm"
 
-    # warmup
-    if args.warmup > 0:
-        gw = capture(torch, step, args.warmup)
-        gw.replay()
-        torch.cuda.synchronize()
-        log(f"warmup {args.warmup} steps done")
-    g = capture(torch, step, args.steps)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    g.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = wall * 1e3 / args.steps
-    log(f"timed {args.steps} steps: wall {wall*1e3:.3f} ms, events {gpu_ms:.3f} ms")
+    ev_ms, wall_ms = time_steps(torch, runner, args.steps, args.warmup)
+    log(f"timed {args.steps} steps: events {ev_ms * 1e3:.3f} us/step, wall "
+        f"{wall_ms * 1e3:.3f} us/step")
+    rec = step_record(runner, ev_ms, wall_ms, metric_kind)
 
-    if groups is not None:
-        roof = roofline_grouped(args, torch, step, bytes_step, ops_step, wk, M, len(lins),
-                                metric_kind)
+    if runner.groups is not None:
+        # The dominant kernel is the grouped kernel; up to four tokens it is
+        # the step's only launch, so its average duration is the timed
+        # region's event time per step.
+        key = (f"group_gemm_{wk.key}_m{M}" if M > 16 else f"group_gemv_{wk.key}_m{M}")
+        if metric_kind == "tops":
+            roof = mfma_roof(runner.ops_step(), ev_ms * 1e3, key, GEMM_SOURCES)
+        else:
+            roof = hbm_roof(runner.bytes_step(), ev_ms * 1e3, key,
+                            GEMM_SOURCES if M > 16 else GROUP_SOURCES)
+        roof["launches_per_step"] = 1 if M <= 4 else 2
+        roof["timed_over"] = (f"the timed region: {args.steps} steps, HIP events on torch's "
+                              "stream" + ("" if M <= 4 else "; includes the quantization "
+                                          "launch"))
     else:
-        roof = roofline_single(args, torch, bl, wk, M, lins, metric_kind)
+        roof = roofline_single(args, torch, bl, runner, metric_kind)
 
-    step_s = ms_per_step / 1e3
-    if metric_kind == "tops":
-        value, unit = ops_step / step_s / 1e12, "TOPS"
-    else:
-        value, unit = bytes_step / step_s / 1e9, "GB/s"
+    subs = None
+    if not args.no_sub:
+        subs = sub_records(args, torch, bl, wl, dev, runner)
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(args, wk, M, wk.linears, metric_kind, args.cpu_seconds,
-                           subln=args.subln)
+        cpu = cpu_baseline(wl, wk, M, metric_kind, args.cpu_seconds, subln=args.subln)
         log(f"cpu oracle: {cpu}")
 
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": unit,
+        "value": rec["value"],
+        "unit": rec["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -535,19 +699,20 @@ def main():
             "workload": wk.key,
             "description": wk.description,
             "tokens": M,
-            "linears_per_step": len(lins),
-            "weight_copies_rotated": copies,
-            "bytes_per_step": bytes_step,
-            "ops_per_step": ops_step,
-            "us_per_token": round(ms_per_step * 1e3 / M, 3),
-            "gpu_event_ms_per_step": round(gpu_ms / args.steps, 6),
-            "offline_weight_quant_ms": round(quant_s * 1e3 / copies, 3),
-            "grouped": groups is not None,
+            "grouped": runner.groups is not None,
+            "us_per_token": rec["us_per_token"],
+            "wall_ms_per_step": rec["wall_ms_per_step"],
+            "linears_per_step": rec["linears_per_step"],
+            "weight_copies_rotated": runner.copies,
+            "bytes_per_step": rec["bytes_per_step"],
+            "ops_per_step": rec["ops_per_step"],
+            "offline_weight_quant_ms": round(runner.quant_ms(), 3),
             "subln": bool(args.subln),
             "glu": bool(args.glu),
         },
         "roofline": roof,
         "cpu_baseline": cpu,
+        "sub": subs,
     }
     print(json.dumps(out), flush=True)
 

@@ -117,6 +117,25 @@ def gen_weight(seed: int, N: int, K: int, sparse_frac: float = 0.0) -> np.ndarra
     return W
 
 
+def gen_weight_device(seed: int, N: int, K: int, sparse_frac: float, device):
+    """The same distribution as ``gen_weight``, drawn by torch's seeded
+    generator on ``device`` (a torch tensor, float32 [N][K]): N(0, 0.02^2),
+    and a uniform ``sparse_frac`` of entries multiplied by 1e-3.  For the
+    full-size workloads (up to 6.5 G weights per step), where drawing on the
+    host takes minutes; a check copies the same tensor to the host for the
+    oracle."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    W = torch.randn((N, K), generator=gen, device=device, dtype=torch.float32)
+    W *= float(WEIGHT_STD)
+    if sparse_frac > 0.0:
+        mask = torch.rand((N, K), generator=gen, device=device) < sparse_frac
+        W = torch.where(mask, W * 1e-3, W)
+    return W
+
+
 def gen_acts_f32(seed: int, M: int, K: int, kind: str) -> np.ndarray:
     """float32 [M][K] activations before any bf16 rounding.
 
