@@ -150,13 +150,20 @@ bitlinear_status bitlinear_quantize_weights_glu(const float* W, int64_t N, int64
                                                 uint8_t* packed, float* gamma, void* ws,
                                                 size_t ws_bytes, void* stream);
 
-/* Packs already-ternary int8 q_w [N][K].  Values should be in {-1,0,1};
- * any other value is clamped into that range before it is stored. */
+/* Packs already-ternary int8 q_w [N][K] into the layout above: four 2-bit
+ * codes per byte ("BitNet b1.58 2B4T Technical Report" card, Method
+ * Adaptation: four ternary weights are stored in one int8; dignews.cc
+ * article, section 2).  `packed` receives bitlinear_packed_bytes(N,K) bytes.
+ * Values should be in {-1,0,1}; any other value is clamped into that range
+ * before it is stored.  Errors: NULL pointers, bad shapes or misaligned
+ * pointers are rejected before anything is enqueued. */
 bitlinear_status bitlinear_pack_ternary(const int8_t* Wq, int64_t N, int64_t K,
                                         uint8_t* packed, void* stream);
 
-/* Inverse of the packing: int8 q_w [N][K] from the packed bytes.  A code 3
- * (never written by this library) unpacks as 0. */
+/* Inverse of the packing (same passages as bitlinear_pack_ternary): int8
+ * q_w [N][K], caller-allocated, from bitlinear_packed_bytes(N,K) packed
+ * bytes.  A code 3 (never written by this library) unpacks as 0.  Errors as
+ * bitlinear_pack_ternary. */
 bitlinear_status bitlinear_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K,
                                           int8_t* Wq, void* stream);
 
@@ -183,8 +190,11 @@ bitlinear_status bitlinear_quantize_acts_rmsnorm(const void* X, bitlinear_dtype 
                                                  float norm_eps, int8_t* Xq, float* x_scale,
                                                  int32_t* x_rowsum, void* stream);
 
-/* The BitLinear forward: Y [M][N] (float) from X [M][K] (dtype), the packed
- * ternary weights and gamma_c (device float, as written by
+/* The BitLinear forward ("BitNet b1.58 2B4T Technical Report" card, Method
+ * Adaptation and Compute Setup: the packed weights are loaded, unpacked just
+ * before the product and multiplied with per-token int8 activations; fishai
+ * digest, the BitLinear items): Y [M][N] (float) from X [M][K] (dtype), the
+ * packed ternary weights and gamma_c (device float, as written by
  * bitlinear_quantize_weights).  Quantizes X per token, contracts in int32,
  * rescales, then applies `epi`.  `dbg` may be NULL.  `ws` holds at least
  * bitlinear_workspace_bytes(M, K, N) bytes (NULL allowed when that is 0).
@@ -213,7 +223,8 @@ bitlinear_status bitlinear_forward_rmsnorm(const void* X, bitlinear_dtype dtype,
                                            void* ws, size_t ws_bytes, void* stream);
 
 /* The same forward from activations already quantized by
- * bitlinear_quantize_acts: Xq [M][K], x_scale [M], x_rowsum [M] (all three
+ * bitlinear_quantize_acts (the int8 matmul and rescale of the same card,
+ * Method Adaptation): Xq [M][K], x_scale [M], x_rowsum [M] (all three
  * required).  The output tiles (128 x 128) are spread over the compute
  * units one workgroup each; when they do not divide evenly, each tile of the
  * last, partial round is instead cut along K into pieces, one workgroup

@@ -543,16 +543,22 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     }
     while (g <= G) wg_begin[(size_t)g++] = (int)split;
   }
+  // The table, the schedule and the cleared queue go to the device on the
+  // null stream; waiting for that stream alone (not the whole device) makes
+  // them visible to launches on any stream afterwards.
   char* base = static_cast<char*>(ws);
-  e = hipMemcpy(base + L.table, table.data(), table.size() * sizeof(GroupOp), hipMemcpyHostToDevice);
+  const int zeros[64] = {};
+  e = hipMemcpyAsync(base + L.table, table.data(), table.size() * sizeof(GroupOp),
+                     hipMemcpyHostToDevice, nullptr);
   if (e == hipSuccess)
-    e = hipMemcpy(base + L.wg_begin, wg_begin.data(), wg_begin.size() * sizeof(int),
-                  hipMemcpyHostToDevice);
+    e = hipMemcpyAsync(base + L.wg_begin, wg_begin.data(), wg_begin.size() * sizeof(int),
+                       hipMemcpyHostToDevice, nullptr);
   if (e == hipSuccess && !units.empty())
-    e = hipMemcpy(base + L.units, units.data(), units.size() * sizeof(GroupUnit),
-                  hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(base + L.queue, 0, 256);  // the kernel leaves it zero
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+    e = hipMemcpyAsync(base + L.units, units.data(), units.size() * sizeof(GroupUnit),
+                       hipMemcpyHostToDevice, nullptr);
+  if (e == hipSuccess)  // the kernel leaves the queue zero again
+    e = hipMemcpyAsync(base + L.queue, zeros, sizeof zeros, hipMemcpyHostToDevice, nullptr);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   bitlinear_group* g = new (std::nothrow) bitlinear_group;
   if (!g) return fail(BITLINEAR_ERR_ARG, "out of host memory");

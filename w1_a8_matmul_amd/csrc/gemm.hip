@@ -28,6 +28,7 @@
 // b1.58 2B4T Technical Report" card, section "Method Adaptation"; the tiling
 // is this library's own, for gfx950.
 #include <algorithm>
+#include <atomic>
 
 #include "common.hpp"
 #include "group.hpp"
@@ -593,34 +594,38 @@ __global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
   }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device).  Callers on any
+// thread may race to fill an entry: they compute the same value, and the
+// atomics make the race well defined.
 int device_cus() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kSkMaxGroups;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
       return kSkMaxGroups;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
 // Workgroups of gemm_kernel<WM,WN,TM,TN,S> that fit on one CU at once
 // (cached per configuration).
 template <int WM, int WN, int TM, int TN, int S>
 int resident_per_cu() {
-  static int cached = 0;
-  if (cached == 0) {
+  static std::atomic<int> cached{0};  // same idempotent race as device_cus
+  int v = cached.load(std::memory_order_relaxed);
+  if (v == 0) {
     int blocks = 0;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &blocks, reinterpret_cast<const void*>(&gemm_kernel<WM, WN, TM, TN, S, false, false, false>),
         Tile<WM, WN, TM, TN, S>::kThreads, 0);
-    cached = (e == hipSuccess && blocks > 0) ? blocks : 4;
+    v = (e == hipSuccess && blocks > 0) ? blocks : 4;
+    cached.store(v, std::memory_order_relaxed);
   }
-  return cached;
+  return v;
 }
 
 template <int WM, int WN, int TM, int TN, int S>
