@@ -222,6 +222,29 @@ bitlinear_status bitlinear_forward_rmsnorm(const void* X, bitlinear_dtype dtype,
                                            bitlinear_epilogue epi, const bitlinear_debug* dbg,
                                            void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Forward that allocates nothing -------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * bitlinear_forward without the workspace argument: where the forward needs
+ * a workspace (M > 4), it uses a fixed scratch array of
+ * BITLINEAR_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  It calls no allocating routine.
+ * A forward whose workspace (bitlinear_workspace_bytes) exceeds that size
+ * returns BITLINEAR_ERR_WORKSPACE before anything is enqueued; the shapes of
+ * the 2B and 7B workloads fit (the largest, 2048 tokens of 6912 -> 2560,
+ * needs 29.5 MiB).  Every call on one GPU shares that GPU's array and leaves
+ * its contents behind: calls that overlap on one GPU (on different streams,
+ * or from different threads without ordering) race and give undefined
+ * results.  The first call on a device looks up the array's device address
+ * (a host-side query, no allocation).  Results are bit-identical to
+ * bitlinear_forward; arguments and other errors as there. */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+bitlinear_status bitlinear_forward_noalloc(const void* X, bitlinear_dtype dtype, int64_t M,
+                                           int64_t K, int64_t N, const uint8_t* packed,
+                                           const float* gamma, float* Y,
+                                           bitlinear_epilogue epi, const bitlinear_debug* dbg,
+                                           void* stream);
+
 /* The same forward from activations already quantized by
  * bitlinear_quantize_acts (the int8 matmul and rescale of the same card,
  * Method Adaptation): Xq [M][K], x_scale [M], x_rowsum [M] (all three

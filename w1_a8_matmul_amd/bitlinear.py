@@ -86,9 +86,11 @@ def lib() -> ctypes.CDLL:
                                             _sz, _p]
     L.bitlinear_forward_q.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p,
                                       ctypes.c_int, _p, _sz, _p]
+    L.bitlinear_forward_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p,
+                                            ctypes.c_int, ctypes.POINTER(Debug), _p]
     for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
                  "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
-                 "bitlinear_forward_q"):
+                 "bitlinear_forward_q", "bitlinear_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     L.bitlinear_group_workspace_bytes.argtypes = [ctypes.POINTER(GroupOp), ctypes.c_int, _i64]
     L.bitlinear_group_workspace_bytes.restype = _sz
@@ -255,6 +257,34 @@ def forward(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
             _ptr(gamma), _ptr(out), EPI[epilogue], dbg_arg, _ptr(workspace), ws_n, _stream())
         check(st, "bitlinear_forward_rmsnorm")
     return (out, dbg) if debug else out
+
+
+def forward_noalloc(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
+                    epilogue: Optional[str] = None, out: Optional[torch.Tensor] = None,
+                    debug: bool = False):
+    """The forward without a workspace argument: the library's fixed
+    per-GPU scratch array (NOALLOC_SCRATCH_BYTES) serves as workspace.  The
+    library allocates nothing; ``out`` (and the debug tensors) are the
+    caller's.  Calls that overlap on one GPU race (they share the array)."""
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.float32, device=X.device)
+    dbg = None
+    dbg_struct = None
+    if debug:
+        dbg = {"xq": torch.empty((M, K), dtype=torch.int8, device=X.device),
+               "x_scale": torch.empty(M, dtype=torch.float32, device=X.device),
+               "acc": torch.empty((M, N), dtype=torch.int32, device=X.device)}
+        dbg_struct = Debug(_ptr(dbg["xq"]), _ptr(dbg["x_scale"]), _ptr(dbg["acc"]))
+    dbg_arg = ctypes.byref(dbg_struct) if dbg_struct is not None else None
+    st = lib().bitlinear_forward_noalloc(_ptr(X), _dtype_code(X), M, K, N, _ptr(packed),
+                                         _ptr(gamma), _ptr(out), EPI[epilogue], dbg_arg,
+                                         _stream())
+    check(st, "bitlinear_forward_noalloc")
+    return (out, dbg) if debug else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # BITLINEAR_NOALLOC_SCRATCH_BYTES
 
 
 def forward_q_workspace(M: int, K: int, N: int, device) -> torch.Tensor:

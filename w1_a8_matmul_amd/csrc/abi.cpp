@@ -8,6 +8,7 @@
 
 #include <new>
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/bitlinear.h"
@@ -189,6 +190,41 @@ bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M
     return fail(BITLINEAR_ERR_SHAPE,
                 "M=%lld tokens of K=%lld activations do not fit in LDS (M * (K + 16) + M * 2048 "
                 "bytes must stay within %zu)", (long long)M, (long long)max_k, kGroupMaxLds);
+  return BITLINEAR_OK;
+}
+
+}  // namespace
+
+// ---- Scratch of the forward that allocates nothing ----
+// One fixed device array (BITLINEAR_NOALLOC_SCRATCH_BYTES) per GPU, for
+// callers that cannot allocate.  In host code `scratch` is only a host-side
+// stand-in: its device address on each GPU comes from hipGetSymbolAddress,
+// looked up once per device (with that device current) and kept here.
+static __device__ __align__(256) unsigned char scratch[BITLINEAR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array.
+bitlinear_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "bitlinear_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BITLINEAR_ERR_ARG, "device %d is beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e, "bitlinear_forward_noalloc: hipGetSymbolAddress");
+    if (!ptr) return fail(BITLINEAR_ERR_HIP, "bitlinear_forward_noalloc: no scratch address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return BITLINEAR_OK;
 }
 
@@ -415,6 +451,33 @@ bitlinear_status bitlinear_forward_rmsnorm(const void* X, bitlinear_dtype dtype,
                       ws_bytes, stream, "bitlinear_forward_rmsnorm");
 }
 
+
+bitlinear_status bitlinear_forward_noalloc(const void* X, bitlinear_dtype dtype, int64_t M,
+                                           int64_t K, int64_t N, const uint8_t* packed,
+                                           const float* gamma, float* Y,
+                                           bitlinear_epilogue epi, const bitlinear_debug* dbg,
+                                           void* stream) {
+  // The workspace bitlinear_forward would need; (size_t)-1 on a bad shape,
+  // which forward_impl then reports.
+  const size_t need = bitlinear_workspace_bytes(M, K, N);
+  void* ws = nullptr;
+  if (need != (size_t)-1 && M > 0 && need > 0) {
+    if (need > (size_t)BITLINEAR_NOALLOC_SCRATCH_BYTES)
+      return fail(BITLINEAR_ERR_WORKSPACE,
+                  "M=%lld K=%lld N=%lld needs %zu bytes of scratch; the no-allocation forward "
+                  "has %zu (use bitlinear_forward with a workspace)",
+                  (long long)M, (long long)K, (long long)N, need,
+                  (size_t)BITLINEAR_NOALLOC_SCRATCH_BYTES);
+    const bitlinear_status st = scratch_for_current_device(&ws);
+    if (st != BITLINEAR_OK) return st;
+  }
+  // Same kernels as bitlinear_forward.  Its quantization launch clears the
+  // GEMM's tile counters in the scratch itself, so the contents a previous
+  // call left there do not matter.
+  return forward_impl(X, dtype, M, K, N, nullptr, 0.0f, packed, gamma, Y, epi, dbg, ws,
+                      ws ? (size_t)BITLINEAR_NOALLOC_SCRATCH_BYTES : 0, stream,
+                      "bitlinear_forward_noalloc");
+}
 
 bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      const int32_t* x_rowsum, int64_t M, int64_t K, int64_t N,
