@@ -81,6 +81,12 @@ class Oracle:
         lib.oracle_int_dot_samples.argtypes = [_p, _p, _i64, _p, _p, _i64, _p]
         lib.oracle_rescale.argtypes = [_p, _p, ctypes.c_float, _i64, _i64, _p]
         lib.oracle_relu2.argtypes = [_p, _i64, _p]
+        lib.oracle_packed_bytes_b3.argtypes = [_i64, _i64]
+        lib.oracle_packed_bytes_b3.restype = _i64
+        lib.oracle_pack_b3.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_pack_b3.restype = ctypes.c_int
+        lib.oracle_unpack_b3.argtypes = [_p, _i64, _i64, _p]
+        lib.oracle_unpack_b3.restype = ctypes.c_int
         lib.oracle_pack_glu.argtypes = [_p, _i64, _i64, _p]
         lib.oracle_pack_glu.restype = ctypes.c_int
         lib.oracle_glu_relu2.argtypes = [_p, _i64, _i64, _p]
@@ -130,6 +136,27 @@ class Oracle:
         q = np.empty((N, K), np.int8)
         if self.lib.oracle_unpack(_ptr(packed), N, K, _ptr(q)) != 0:
             raise ValueError("oracle_unpack: bad shape or invalid code 3")
+        return q
+
+    # -- R13: base-3 layout, five codes per byte --------------------------------
+    def packed_bytes_b3(self, N: int, K: int) -> int:
+        return int(self.lib.oracle_packed_bytes_b3(N, K))
+
+    def pack_b3(self, q: np.ndarray) -> np.ndarray:
+        """Five ternary codes per byte in 16 x 320 tiles (K padded to 320)."""
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        N, K = q.shape
+        out = np.empty(self.packed_bytes_b3(N, K), np.uint8)
+        if self.lib.oracle_pack_b3(_ptr(q), N, K, _ptr(out)) != 0:
+            raise ValueError("oracle_pack_b3: shape outside the layout or non-ternary value")
+        return out
+
+    def unpack_b3(self, packed: np.ndarray, N: int, K: int) -> np.ndarray:
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        assert packed.size == self.packed_bytes_b3(N, K)
+        q = np.empty((N, K), np.int8)
+        if self.lib.oracle_unpack_b3(_ptr(packed), N, K, _ptr(q)) != 0:
+            raise ValueError("oracle_unpack_b3: bad shape, byte above 242 or nonzero padding")
         return q
 
     def quantize_weights(self, W: np.ndarray):

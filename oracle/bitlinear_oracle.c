@@ -44,6 +44,8 @@
  *                scale only: s_x = (float)(s_x(u) * r).  The sum of squares is
  *                taken in double in index order; r = (float)(1 / sqrt(S / K +
  *                eps_n)) in double.  The 1e-5 guard of R4 applies to u.
+ *   R13 base-3 = the denser layout: five codes per byte as a base-3 number,
+ *                in tiles of 16 rows by 320 columns (see oracle_pack_b3).
  *   R12 gated FFN = the workload's fused gate+up matrix [N][K] holds the gate
  *                rows 0..F-1 and the up rows F..2F-1 (F = N/2), with one gamma;
  *                h = (r * r) * y_up, r = max(y_gate, 0), left to right, float,
@@ -167,6 +169,78 @@ int oracle_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
       int64_t at = packed_byte_index(n, k, K, &shift);
       int code = (packed[at] >> shift) & 3;
       if (code == 3) return -1;
+      q[n * K + k] = (int8_t)(code - 1);
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* R13: the denser packed layout, five ternary codes per byte.  A ternary
+ * weight carries log2(3), about 1.58 bits ([WP] introduction); the 2B
+ * model's weights take 0.4 GB at that density ([TR] Evidence).  Five codes
+ * c = q + 1 in {0, 1, 2} fit one byte as the base-3 number
+ * c_0 + 3 c_1 + 9 c_2 + 27 c_3 + 81 c_4 (0..242), 1.6 bits per weight.  The
+ * layout is this library's own: K is padded up to Kp, a multiple of 320,
+ * and the matrix is cut into tiles of 16 rows by 320 columns (1024 bytes),
+ * ordered row-tile major, then by column block.  Inside a tile, 16-byte
+ * chunk c holds row (c mod 16) and the 80 columns 80*(c div 16) .. +79 of
+ * the block; inside a chunk, byte b (0..3) of 32-bit word j (0..3) holds
+ * the codes of columns 20j + 4i + b, i = 0..4, digit i being column
+ * 20j + 4i + b.  Padding columns (K <= k < Kp) hold code 0.                */
+static int64_t b3_padded_k(int64_t K) { return (K + 319) / 320 * 320; }
+
+int64_t oracle_packed_bytes_b3(int64_t N, int64_t K) { return N * b3_padded_k(K) / 5; }
+
+/* Byte index and digit of weight (n, k) in the base-3 layout (k < Kp).     */
+static int64_t b3_byte_index(int64_t n, int64_t k, int64_t Kp, int* digit) {
+  int64_t tile_row = n / 16, row_in_tile = n % 16;
+  int64_t kblock = k / 320, kb = k % 320;
+  int64_t quarter = kb / 80, t = kb % 80;      /* chunk column offset 0..79 */
+  int64_t word = t / 20, u = t % 20;           /* u = 4i + b                */
+  int64_t byte_in_word = u % 4;
+  int64_t chunk = quarter * 16 + row_in_tile;
+  int64_t tile = tile_row * (Kp / 320) + kblock;
+  *digit = (int)(u / 4);
+  return tile * 1024 + chunk * 16 + word * 4 + byte_in_word;
+}
+
+/* Returns 0 on success, -1 if N % 16 != 0, K % 16 != 0 or a value is not
+ * ternary.                                                                 */
+int oracle_pack_b3(const int8_t* q, int64_t N, int64_t K, uint8_t* packed) {
+  if (N % 16 != 0 || K % 16 != 0 || N < 0 || K < 0) return -1;
+  const int64_t Kp = b3_padded_k(K);
+  const int pow3[5] = {1, 3, 9, 27, 81};
+  memset(packed, 0, (size_t)(N * Kp / 5));
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t k = 0; k < K; ++k) {
+      int8_t v = q[n * K + k];
+      if (v < -1 || v > 1) return -1;
+      int digit;
+      int64_t at = b3_byte_index(n, k, Kp, &digit);
+      packed[at] = (uint8_t)(packed[at] + (v + 1) * pow3[digit]);
+    }
+  }
+  return 0;
+}
+
+/* Returns 0 on success, -1 on a bad shape, a byte above 242 or a padding
+ * column whose code is not 0.                                              */
+int oracle_unpack_b3(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
+  if (N % 16 != 0 || K % 16 != 0 || N < 0 || K < 0) return -1;
+  const int64_t Kp = b3_padded_k(K);
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t k = 0; k < Kp; ++k) {
+      int digit;
+      int64_t at = b3_byte_index(n, k, Kp, &digit);
+      int v = packed[at];
+      if (v > 242) return -1;
+      for (int i = 0; i < digit; ++i) v /= 3;
+      int code = v % 3;
+      if (k >= K) {
+        if (code != 0) return -1;
+        continue;
+      }
       q[n * K + k] = (int8_t)(code - 1);
     }
   }

@@ -33,6 +33,9 @@ void oracle_rescale(const int32_t* acc, const float* s_x, float gamma_c, int64_t
                     float* y);
 void oracle_relu2(const float* y, int64_t count, float* h);
 int oracle_pack_glu(const int8_t* q, int64_t N, int64_t K, uint8_t* packed);
+int64_t oracle_packed_bytes_b3(int64_t N, int64_t K);
+int oracle_pack_b3(const int8_t* q, int64_t N, int64_t K, uint8_t* packed);
+int oracle_unpack_b3(const uint8_t* packed, int64_t N, int64_t K, int8_t* q);
 void oracle_glu_relu2(const float* y, int64_t M, int64_t N, float* h);
 int oracle_forward(const void* X, int dtype, int64_t M, int64_t K, int64_t N, const int8_t* qw,
                    float gamma_c, float* y, int8_t* xq_out, float* sx_out, int32_t* acc_out);
@@ -97,6 +100,19 @@ static void one_shape(int64_t M, int64_t N, int64_t K) {
     CHECK(oracle_unpack(p, N, K, q2) == -1);
     CHECK(oracle_pack_glu(q, N, K, p) == -1);
   }
+  {
+    const int64_t nb = oracle_packed_bytes_b3(N, K);
+    uint8_t* p3 = malloc((size_t)(nb > 0 ? nb : 1));
+    if (N % 16 == 0 && K % 16 == 0) {
+      CHECK(oracle_pack_b3(q, N, K, p3) == 0);
+      CHECK(oracle_unpack_b3(p3, N, K, q2) == 0);
+      CHECK(memcmp(q, q2, (size_t)nk) == 0);
+    } else {
+      CHECK(oracle_pack_b3(q, N, K, p3) == -1);
+      CHECK(oracle_unpack_b3(p3, N, K, q2) == -1);
+    }
+    free(p3);
+  }
   oracle_quant_acts_f32(X, M, K, xq, sx, rs);
   oracle_quant_acts_f32(X, M, K, xq, sx, NULL);
   oracle_quant_acts_bf16(Xb, M, K, xq, sx, rs);
@@ -125,7 +141,7 @@ static void one_shape(int64_t M, int64_t N, int64_t K) {
 int main(void) {
   const int64_t shapes[][3] = {{4, 256, 256}, {1, 16, 256}, {3, 48, 768}, {0, 16, 256},
                                {2, 16, 0},    {5, 15, 256}, {2, 16, 100}, {7, 32, 512},
-                               {1, 0, 256}};
+                               {1, 0, 256},   {2, 16, 336}, {3, 32, 6912}};
   for (size_t i = 0; i < sizeof shapes / sizeof shapes[0]; ++i)
     one_shape(shapes[i][0], shapes[i][1], shapes[i][2]);
   /* invalid codes: a byte with code 3 must be rejected */

@@ -58,6 +58,19 @@ MUTANTS = {
                               "      float t = r * y[m * N + F + f];\n      h[m * F + f] = r * t;"),
     "norm_factor_in_float": ("float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));",
                              "float r = 1.0f / sqrtf((float)(S / (double)K) + eps_n);"),
+    # base-3 layout (R13)
+    "b3_digit_order_reversed": ("  *digit = (int)(u / 4);", "  *digit = (int)(4 - u / 4);"),
+    "b3_columns_grouped_by_five": (
+        "  int64_t byte_in_word = u % 4;\n  int64_t chunk = quarter * 16 + row_in_tile;\n"
+        "  int64_t tile = tile_row * (Kp / 320) + kblock;\n  *digit = (int)(u / 4);",
+        "  int64_t byte_in_word = u / 5;\n  int64_t chunk = quarter * 16 + row_in_tile;\n"
+        "  int64_t tile = tile_row * (Kp / 320) + kblock;\n  *digit = (int)(u % 5);"),
+    "b3_chunk_transposed": ("  int64_t chunk = quarter * 16 + row_in_tile;",
+                            "  int64_t chunk = row_in_tile * 4 + quarter;"),
+    "b3_padding_not_zero": ("  memset(packed, 0, (size_t)(N * Kp / 5));",
+                            "  memset(packed, 1, (size_t)(N * Kp / 5));"),
+    "b3_pad_to_256": ("static int64_t b3_padded_k(int64_t K) { return (K + 319) / 320 * 320; }",
+                      "static int64_t b3_padded_k(int64_t K) { return (K + 255) / 256 * 256; }"),
 }
 
 

@@ -752,3 +752,103 @@ def test_rmsnorm_factor_correctly_rounded(orc):
         checked += 1
         assert Fraction(float(s[m])) == _fl(Fraction(float(s0[m])) * r), m
     assert checked >= M - 2
+
+
+# --------------------------------------------------------------------------
+# R13: the base-3 layout, five codes per byte in 16 x 320 tiles (K padded to
+# a multiple of 320 with code 0).  Pins: hand-worked positions
+# (tests/golden/pack_b3_positions.txt); an all-zero matrix packs to bytes of
+# 1+3+9+27+81 = 121; a hand-worked padding case; every one of the 243
+# five-code patterns in every byte slot; the 2B footprint.
+# --------------------------------------------------------------------------
+def test_pack_b3_positions_golden(orc):
+    with open(os.path.join(GOLDEN, "pack_b3_positions.txt")) as f:
+        rows = [list(map(int, l.split())) for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) >= 10
+    for N, K, n, k, byte, digit in rows:
+        q = np.zeros((N, K), np.int8)
+        assert np.all(orc.pack_b3(q) == 121)  # code 1 in all five digits
+        q[n, k] = 1  # code 2 at (n, k)
+        p = orc.pack_b3(q)
+        expect = np.full(N * K // 5, 121, np.uint8)
+        expect[byte] = 121 + 3 ** digit
+        assert np.array_equal(p, expect), (N, K, n, k)
+
+
+def test_pack_b3_padding_by_hand(orc):
+    # K = 336 pads to 640: tile 0 holds columns 0..319 (all code 1, bytes of
+    # 121); tile 1 holds columns 320..335, which are the first 16 columns of
+    # quarter 0: word 0, bytes 0..3, digits 0..3 (u = 0..15) of each row's
+    # chunk.  Those bytes are 1+3+9+27 = 40 (digit 4 is padding, code 0);
+    # every other byte of tile 1 is all padding, 0.
+    q = np.zeros((16, 336), np.int8)
+    p = orc.pack_b3(q)
+    assert p.size == 16 * 640 // 5 == orc.packed_bytes_b3(16, 336)
+    assert np.all(p[:1024] == 121)
+    t1 = p[1024:].reshape(64, 16)
+    assert np.all(t1[:16, :4] == 40) and np.all(t1[:16, 4:] == 0) and np.all(t1[16:] == 0)
+    assert np.array_equal(orc.unpack_b3(p, 16, 336), q)
+    bad = p.copy()
+    bad[1024 + 4] = 1  # a padding code that is not 0
+    with pytest.raises(ValueError):
+        orc.unpack_b3(bad, 16, 336)
+
+
+def test_pack_b3_all_243_patterns(orc):
+    # every five-code pattern (as a base-3 number, digit i = code of column
+    # 20j + 4i + b) lands as that number in every byte slot (j, b)
+    pats = np.array(np.meshgrid(*[[0, 1, 2]] * 5, indexing="ij")).reshape(5, -1).T  # 243 x 5
+    value = (pats * np.array([1, 3, 9, 27, 81])).sum(axis=1)
+    N, K = 16, 320
+    for off in range(0, 243, 61):
+        q = np.zeros((N, K), np.int8)
+        expect = np.zeros(N * K // 5, np.int64)
+        s = off
+        for n in range(N):
+            for quarter in range(4):
+                for j in range(4):
+                    for b in range(4):
+                        pat = s % 243
+                        s += 1
+                        for i in range(5):
+                            q[n, 80 * quarter + 20 * j + 4 * i + b] = pats[pat, i] - 1
+                        expect[(quarter * 16 + n) * 16 + 4 * j + b] = value[pat]
+        p = orc.pack_b3(q)
+        assert np.array_equal(p.astype(np.int64), expect)
+        assert np.array_equal(orc.unpack_b3(p, N, K), q)
+
+
+@pytest.mark.parametrize("N,K", [(16, 320), (48, 656), (32, 2560), (16, 6912)])
+def test_pack_b3_roundtrip_and_range(orc, N, K):
+    q = _rng(N * K).integers(-1, 2, (N, K)).astype(np.int8)
+    p = orc.pack_b3(q)
+    Kp = -(-K // 320) * 320
+    assert p.size == N * Kp // 5 == orc.packed_bytes_b3(N, K)
+    assert p.max() <= 242
+    assert np.array_equal(orc.unpack_b3(p, N, K), q)
+    # the digits hold exactly the codes (a permutation), plus code 0 padding
+    digits = np.stack([(p.astype(np.int64) // 3 ** i) % 3 for i in range(5)], axis=1).ravel()
+    want = np.bincount((q + 1).ravel(), minlength=3)
+    got = np.bincount(digits, minlength=3)
+    assert got[1] == want[1] and got[2] == want[2] and got[0] == want[0] + N * (Kp - K)
+
+
+def test_pack_b3_footprint():
+    kv = _read_kv("model_2b_footprint.txt")
+    from w1_a8_matmul_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS["decode_step_2b"]
+    total = wl.layers * sum(l.N * (-(-l.K // 320) * 320) // 5 for l in wl.linears)
+    assert total == int(kv["packed_bytes_b3"][0])
+    assert abs(total / (wl.weights_per_step * np.log2(3) / 8) - 1) < 0.015
+
+
+def test_pack_b3_rejects_bad_input(orc):
+    with pytest.raises(ValueError):
+        orc.pack_b3(np.zeros((15, 320), np.int8))
+    with pytest.raises(ValueError):
+        orc.pack_b3(np.zeros((16, 100), np.int8))
+    with pytest.raises(ValueError):
+        orc.pack_b3(np.full((16, 320), 2, np.int8))
+    with pytest.raises(ValueError):
+        orc.unpack_b3(np.full(1024, 243, np.uint8), 16, 320)
