@@ -53,6 +53,9 @@ MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
 GEMV_SOURCES = ["gemv.hip", "gemv_tile.hpp", "common.hpp"]
 GEMM_SOURCES = ["gemm.hip", "group.hpp", "common.hpp"]
 GROUP_SOURCES = ["group.hip", "group.hpp", "gemv_tile.hpp", "quant_row.hpp", "common.hpp"]
+# Up to this many tokens the grouped decode quantizes inside its one launch;
+# above, a quantization launch precedes it.
+GROUP_INLINE_MAX_M = 3
 
 
 def log(*a):
@@ -583,7 +586,7 @@ def sub_records(args, torch, bl, wl, dev, main_runner):
         r = Runner(bl, torch, wl, dev, "decode_step_2b", M, grouped=True, share_weights=share)
         ev, wall = time_steps(torch, r, steps, warmup)
         rec = step_record(r, ev, wall, "hbm")
-        rec["launches_per_step"] = 1 if M <= 4 else 2
+        rec["launches_per_step"] = 1 if M <= GROUP_INLINE_MAX_M else 2
         subs[f"decode_step_2b_m{M}"] = rec
         del r
     torch.cuda.empty_cache()
@@ -666,9 +669,9 @@ def main():
         else:
             roof = hbm_roof(runner.bytes_step(), ev_ms * 1e3, key,
                             GEMM_SOURCES if M > 16 else GROUP_SOURCES)
-        roof["launches_per_step"] = 1 if M <= 4 else 2
+        roof["launches_per_step"] = 1 if M <= GROUP_INLINE_MAX_M else 2
         roof["timed_over"] = (f"the timed region: {args.steps} steps, HIP events on torch's "
-                              "stream" + ("" if M <= 4 else "; includes the quantization "
+                              "stream" + ("" if M <= GROUP_INLINE_MAX_M else "; includes the quantization "
                                           "launch"))
     else:
         roof = roofline_single(args, torch, bl, runner, metric_kind)

@@ -266,7 +266,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
  * Many independent BitLinear layers that share the token count M
  * (1..65536), run by persistent launches over the output tiles of all
  * layers.  Up to 16 tokens one launch streams the packed weights of all
- * layers back to back with v_dot4 / skinny MFMA contraction; up to 4 tokens
+ * layers back to back with skinny int8 MFMA contraction; up to 3 tokens
  * each workgroup quantizes the activations of the layers it works on itself,
  * above one more launch quantizes them first into the workspace.  Above 16
  * tokens the quantization launch is followed by one tiled int8 MFMA GEMM
@@ -309,7 +309,7 @@ size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops,
 bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops, int64_t M,
                                         void* ws, size_t ws_bytes, bitlinear_group** out);
 
-/* Runs every layer of the group on `stream` (one launch for M <= 4, two
+/* Runs every layer of the group on `stream` (one launch for M <= 3, two
  * above; capturable in a HIP graph).  Calls that overlap on one group
  * race. */
 bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream);

@@ -43,10 +43,14 @@ constexpr int kGroupStaticPercentPreq = 95;
 // Largest K of a grouped layer and largest token count.  Up to
 // kGroupInlineQuantMaxM tokens each workgroup quantizes the activations of
 // the layer it starts on itself (one launch); above, a separate launch
-// quantizes them once into the workspace.
+// quantizes them once into the workspace.  Measured on MI355X (2B step, one
+// box, alternating runs): inline 102.8 against 107.2 us at two tokens,
+// 107.6-110.5 against 110.3-111.3 at three, but 114.5-116.1 against
+// 112.0-112.1 at four, where a new layer's four rows cost about three
+// memory round trips inline and one copy after the quantization launch.
 constexpr int kGroupMaxK = 12288;
 constexpr int kGroupMaxM = 16;
-constexpr int kGroupInlineQuantMaxM = 4;
+constexpr int kGroupInlineQuantMaxM = 3;
 
 // Whether the group needs the quantization launch and workspace.
 bool bl_group_prequantizes(int M);
