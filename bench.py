@@ -2,7 +2,7 @@
 """Benchmark of the W1.58A8 BitLinear forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--tokens M] [--grouped | --per-linear] [--no-sub] [--no-cpu]
+                    [--tokens M] [--grouped | --per-linear] [--b3] [--no-sub] [--no-cpu]
 
 A step is one pass of the per-token hot path over one batch of synthetic
 input: per-token absmax int8 quantization, load + unpack of the packed
@@ -18,7 +18,8 @@ forward per step ("µs/token for all linears").  Two weight sets alternate, so
 no step finds its weights in the 256 MB Infinity Cache.  The same JSON line
 carries keyed sub-records (``sub``) for the decode GEMV pair (M = 1, up ->
 ReLU^2 -> down, 61 rotating weight copies), the 2B step at M = 4 and 16, and
-the prefill GEMMs at M = 2048 (int8 TOPS).
+the prefill GEMMs at M = 2048 (int8 TOPS), and the 2B step at M = 1 with its
+weights in the base-3 layout (five codes per byte).
 
 Timing: W warm-up steps, then exactly K steps, each as one HIP graph replay
 on torch's stream, bracketed by synchronizations; HIP events around the
@@ -85,6 +86,8 @@ def parse():
     p.add_argument("--glu", action="store_true",
                    help="gated FFN: pack each gate+up linear (N = 2 x the down projection's K) "
                         "for the gated squared-ReLU epilogue (output N/2)")
+    p.add_argument("--b3", action="store_true",
+                   help="weights in the base-3 layout (five codes per byte; grouped, M <= 16)")
     p.add_argument("--subln", action="store_true",
                    help="give every linear a subln gain (RMSNorm fused into its quantization)")
     p.add_argument("--probes", action="store_true",
@@ -111,16 +114,21 @@ class Linear:
     (the workload's distribution), its output and workspace."""
 
     def __init__(self, bl, torch, wl, dev, wk, layer, li, shape, M, copies, subln=False,
-                 glu=False):
+                 glu=False, fmt=None):
         self.N, self.K, self.M = shape.N, shape.K, M
         self.epi = "relu2_glu" if glu else None
+        self.packed_bytes = (bl.packed_bytes_b3(self.N, self.K) if fmt == "b3"
+                             else self.N * self.K // 4)
         self.packed, self.gamma = [], []
         t0 = time.perf_counter()
         for c in range(copies):
             # copy 0 uses the seed the parity tests use; the others differ
             seed = wl.weight_seed(wk.key, layer, li) + 100003 * c
             W = wl.gen_weight_device(seed, self.N, self.K, wk.weight_sparse_frac, dev)
-            p, g = bl.quantize_weights(W, glu=glu)
+            if fmt == "b3":
+                p, g = bl.quantize_weights_b3(W, glu=glu)
+            else:
+                p, g = bl.quantize_weights(W, glu=glu)
             self.packed.append(p)
             self.gamma.append(g)
             del W
@@ -137,9 +145,9 @@ class Linear:
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev) if ws > 0 else None
 
     def bytes(self):
-        """Algorithmic bytes of one forward: packed W + X in + Y out + gamma
-        (+ the subln gain)."""
-        return (self.N * self.K // 4 + self.X.numel() * self.X.element_size()
+        """Algorithmic bytes of one forward: packed W (in its layout) + X in +
+        Y out + gamma (+ the subln gain)."""
+        return (self.packed_bytes + self.X.numel() * self.X.element_size()
                 + self.Y.numel() * 4 + 4 + (self.K * 4 if self.gain is not None else 0))
 
     def ops(self):
@@ -157,9 +165,11 @@ class Runner:
     """A workload at M tokens: its linears and a step function."""
 
     def __init__(self, bl, torch, wl, dev, key, M, grouped, copies=None, subln=False,
-                 glu=False, share_weights=None):
+                 glu=False, share_weights=None, fmt=None):
         wk = wl.WORKLOADS[key]
-        self.wk, self.M = wk, M
+        self.wk, self.M, self.fmt = wk, M, fmt
+        if fmt == "b3" and (not grouped or M > 16):
+            raise SystemExit("base-3 weights run in the grouped decode forward (M <= 16)")
         self.copies = copies or weight_copies(wk.weights_per_step // 4)
         downs_k = {l.K for l in wk.linears}
         self.lins = []
@@ -170,6 +180,7 @@ class Runner:
                 lin = Linear.__new__(Linear)
                 src = share_weights.lins[idx]
                 lin.N, lin.K, lin.M, lin.epi = src.N, src.K, M, src.epi
+                lin.packed_bytes = src.packed_bytes
                 lin.packed, lin.gamma, lin.quant_s = src.packed, src.gamma, 0.0
                 lin.seed_x = src.seed_x + 100 * M
                 lin.X = make_acts(torch, wl, lin.seed_x, M, lin.K, wk.x_kind, dev)
@@ -181,7 +192,7 @@ class Runner:
                 lin.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev) if ws > 0 else None
             else:
                 lin = Linear(bl, torch, wl, dev, wk, layer, li, shape, M, self.copies,
-                             subln=subln, glu=g)
+                             subln=subln, glu=g, fmt=fmt)
             self.lins.append(lin)
         if share_weights is not None:
             self.copies = share_weights.copies
@@ -193,7 +204,7 @@ class Runner:
             if wk.chain_relu2:
                 raise SystemExit("a grouped forward needs independent linears")
             self.groups = [bl.Group([(l.X, l.packed[c], l.gamma[c], l.N, l.epi, l.Y, l.gain)
-                                     for l in self.lins])
+                                     for l in self.lins], fmt=fmt)
                            for c in range(self.copies)]
         self.bl = bl
         self.offset = 0  # first copy of the timed region
@@ -581,7 +592,8 @@ def sub_records(args, torch, bl, wl, dev, main_runner):
 
     # 2B step at M = 4 and 16, grouped
     share = main_runner if (main_runner.wk.key == "decode_step_2b" and
-                            main_runner.groups is not None) else None
+                            main_runner.groups is not None and
+                            main_runner.fmt is None) else None
     for M in (4, 16):
         r = Runner(bl, torch, wl, dev, "decode_step_2b", M, grouped=True, share_weights=share)
         ev, wall = time_steps(torch, r, steps, warmup)
@@ -590,6 +602,19 @@ def sub_records(args, torch, bl, wl, dev, main_runner):
         subs[f"decode_step_2b_m{M}"] = rec
         del r
     torch.cuda.empty_cache()
+
+    # 2B step at M = 1 with the weights in the base-3 layout (five codes per
+    # byte, 418.8 MB instead of 521.0 MB); GB/s counts the bytes it reads
+    if main_runner.fmt is None:
+        r = Runner(bl, torch, wl, dev, "decode_step_2b", 1, grouped=True, fmt="b3")
+        ev, wall = time_steps(torch, r, steps, warmup)
+        rec = step_record(r, ev, wall, "hbm")
+        rec["weight_format"] = "b3"
+        rec["launches_per_step"] = 1
+        subs["decode_step_2b_m1_b3"] = rec
+        log(f"2B step M=1, base-3 weights: {rec['us_per_step']} us, {rec['value']} GB/s")
+        del r
+        torch.cuda.empty_cache()
 
     # prefill, M = 2048: the whole step (two quantizations + two GEMMs) and each
     # GEMM launch alone
@@ -649,7 +674,7 @@ def main():
     if grouped is None:  # default: grouped for the multi-layer decode steps
         grouped = wk.layers > 1 and M <= 64 and not wk.chain_relu2
     runner = Runner(bl, torch, wl, dev, args.workload, M, grouped, subln=args.subln,
-                    glu=args.glu)
+                    glu=args.glu, fmt="b3" if args.b3 else None)
     log(f"workload {wk.key} M={M}: {len(runner.lins)} linears, {runner.copies} weight "
         f"copies, offline quantization {runner.quant_ms():.1f} ms per weight set")
     metric_kind = "tops" if M >= 128 else "hbm"
@@ -664,12 +689,16 @@ def main():
         # the step's only launch, so its average duration is the timed
         # region's event time per step.
         key = (f"group_gemm_{wk.key}_m{M}" if M > 16 else f"group_gemv_{wk.key}_m{M}")
+        key += "_b3" if args.b3 else ""
         if metric_kind == "tops":
             roof = mfma_roof(runner.ops_step(), ev_ms * 1e3, key, GEMM_SOURCES)
         else:
             roof = hbm_roof(runner.bytes_step(), ev_ms * 1e3, key,
                             GEMM_SOURCES if M > 16 else GROUP_SOURCES)
         roof["launches_per_step"] = 1 if M <= GROUP_INLINE_MAX_M else 2
+        if args.b3:
+            roof["note"] = ("base-3 weights: the digit extraction makes the kernel VALU-bound; "
+                            "the HBM fraction is kept for comparison with the 2-bit layout")
         roof["timed_over"] = (f"the timed region: {args.steps} steps, HIP events on torch's "
                               "stream" + ("" if M <= GROUP_INLINE_MAX_M else "; includes the quantization "
                                           "launch"))
@@ -712,6 +741,7 @@ def main():
             "offline_weight_quant_ms": round(runner.quant_ms(), 3),
             "subln": bool(args.subln),
             "glu": bool(args.glu),
+            "weight_format": "b3" if args.b3 else "2bit",
         },
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 3
+#define BITLINEAR_ABI_VERSION 4
 
 typedef enum {
   BITLINEAR_OK = 0,
@@ -99,6 +99,24 @@ typedef enum {
      then up rows.  Only valid with weights packed that way; dbg->acc_out
      then stays [M][N] in the unpermuted row order. */
 } bitlinear_epilogue;
+
+/* Layouts of packed weights.  BITLINEAR_FMT_2BIT is the layout described
+ * above (four codes per byte), used by every call.  BITLINEAR_FMT_B3 is the
+ * denser base-3 layout (five codes per byte, 1.6 bits per weight; a ternary
+ * weight carries log2(3) bits, wikiprompt.org "1.58-bit large language
+ * model", introduction; the technical-report card, Evidence, gives the 2B
+ * model's weights as 0.4 GB, which is that density): K is padded up to Kp, a
+ * multiple of 320, with code 0; the matrix is cut into tiles of 16 rows x
+ * 320 columns (1024 bytes) ordered row-tile major, then by column block;
+ * 16-byte chunk c of a tile holds row (c mod 16) and the columns
+ * 80*(c div 16) .. +79 of its block; byte b of little-endian 32-bit word j
+ * of a chunk holds the codes c_i of columns 20j + 4i + b (i = 0..4) as the
+ * number c_0 + 3 c_1 + 9 c_2 + 27 c_3 + 81 c_4 (0..242).  Only the grouped
+ * forward (up to 16 tokens) runs on it. */
+typedef enum {
+  BITLINEAR_FMT_2BIT = 0,
+  BITLINEAR_FMT_B3 = 1
+} bitlinear_weight_format;
 
 /* Optional extra outputs of bitlinear_forward, for checking the integer
  * intermediates.  Each pointer may be NULL.  xq_out: int8 [M][K];
@@ -166,6 +184,29 @@ bitlinear_status bitlinear_pack_ternary(const int8_t* Wq, int64_t N, int64_t K,
  * bitlinear_pack_ternary. */
 bitlinear_status bitlinear_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K,
                                           int8_t* Wq, void* stream);
+
+/* Bytes of an [N][K] matrix in the base-3 layout: N * Kp / 5 with Kp = K
+ * rounded up to a multiple of 320.  0 when N or K is below 1 or breaks
+ * N % 16 / K % 16. */
+size_t bitlinear_packed_bytes_b3(int64_t N, int64_t K);
+
+/* Absmean ternary quantization of float W [N][K], as
+ * bitlinear_quantize_weights (the same gamma and codes), packed in the
+ * base-3 layout: `packed` receives bitlinear_packed_bytes_b3(N, K) bytes.
+ * glu != 0 packs a fused gate+up matrix with its halves interleaved per
+ * 16-row tile, as bitlinear_quantize_weights_glu (then N % 32 == 0).  K needs
+ * only K % 16 == 0.  `ws` as bitlinear_quantize_weights. */
+bitlinear_status bitlinear_quantize_weights_b3(const float* W, int64_t N, int64_t K,
+                                               uint8_t* packed, float* gamma, void* ws,
+                                               size_t ws_bytes, int glu, void* stream);
+
+/* Packs int8 q_w [N][K] (values clamped into {-1, 0, 1}) in the base-3
+ * layout, and unpacks it (padding columns are skipped).  Shapes as
+ * bitlinear_packed_bytes_b3; errors as bitlinear_pack_ternary. */
+bitlinear_status bitlinear_pack_ternary_b3(const int8_t* Wq, int64_t N, int64_t K,
+                                           uint8_t* packed, void* stream);
+bitlinear_status bitlinear_unpack_ternary_b3(const uint8_t* packed, int64_t N, int64_t K,
+                                             int8_t* Wq, void* stream);
 
 /* Per-token absmax int8 quantization of X [M][K] (fishai digest, activation
  * quantization item; technical-report card, Method Adaptation).  Writes Xq
@@ -289,6 +330,10 @@ typedef struct {
                              the layer then quantizes as
                              bitlinear_quantize_acts_rmsnorm does */
   float norm_eps;         /* subln epsilon (finite, >= 0) when norm_gain is set */
+  bitlinear_weight_format format; /* layout of `packed`; 0 (2-bit) when zeroed.
+                             Every layer of a group uses the same one; the
+                             base-3 layout needs M <= 16 and K % 16 == 0
+                             (instead of K % 256), its padded K <= 12288 */
 } bitlinear_group_op;
 
 /* Opaque host-side handle of a planned group (host memory only). */

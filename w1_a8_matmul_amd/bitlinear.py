@@ -40,10 +40,13 @@ class Debug(ctypes.Structure):
     _fields_ = [("xq_out", _p), ("xscale_out", _p), ("acc_out", _p)]
 
 
+FMT = {"2bit": 0, None: 0, "b3": 1}
+
+
 class GroupOp(ctypes.Structure):
     _fields_ = [("X", _p), ("dtype", ctypes.c_int), ("epi", ctypes.c_int), ("K", _i64),
                 ("N", _i64), ("packed", _p), ("gamma", _p), ("Y", _p), ("norm_gain", _p),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("format", ctypes.c_int)]
 
 
 _lib = None
@@ -74,6 +77,12 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward_q_workspace_bytes.restype = _sz
     L.bitlinear_quantize_weights.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
     L.bitlinear_quantize_weights_glu.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, _p]
+    L.bitlinear_packed_bytes_b3.argtypes = [_i64, _i64]
+    L.bitlinear_packed_bytes_b3.restype = _sz
+    L.bitlinear_quantize_weights_b3.argtypes = [_p, _i64, _i64, _p, _p, _p, _sz, ctypes.c_int,
+                                                _p]
+    L.bitlinear_pack_ternary_b3.argtypes = [_p, _i64, _i64, _p, _p]
+    L.bitlinear_unpack_ternary_b3.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_pack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_unpack_ternary.argtypes = [_p, _i64, _i64, _p, _p]
     L.bitlinear_quantize_acts.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, _p]
@@ -90,7 +99,9 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_int, ctypes.POINTER(Debug), _p]
     for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
                  "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
-                 "bitlinear_forward_q", "bitlinear_forward_noalloc"):
+                 "bitlinear_forward_q", "bitlinear_forward_noalloc",
+                 "bitlinear_quantize_weights_b3", "bitlinear_pack_ternary_b3",
+                 "bitlinear_unpack_ternary_b3"):
         getattr(L, name).restype = ctypes.c_int
     L.bitlinear_group_workspace_bytes.argtypes = [ctypes.POINTER(GroupOp), ctypes.c_int, _i64]
     L.bitlinear_group_workspace_bytes.restype = _sz
@@ -181,6 +192,43 @@ def quantize_weights(W: torch.Tensor, packed: Optional[torch.Tensor] = None,
             _stream())
     check(st, "bitlinear_quantize_weights_glu" if glu else "bitlinear_quantize_weights")
     return packed, gamma
+
+
+def packed_bytes_b3(N: int, K: int) -> int:
+    return lib().bitlinear_packed_bytes_b3(N, K)
+
+
+def quantize_weights_b3(W: torch.Tensor, glu: bool = False,
+                        workspace: Optional[torch.Tensor] = None):
+    """quantize_weights into the base-3 layout (five codes per byte; K padded
+    to a multiple of 320).  Returns (packed uint8, gamma_c float32 [1])."""
+    N, K = W.shape
+    if W.dtype != torch.float32:
+        raise BitLinearError("W must be float32")
+    packed = torch.empty(max(packed_bytes_b3(N, K), 1), dtype=torch.uint8, device=W.device)
+    gamma = torch.empty(4, dtype=torch.float32, device=W.device)[:1]
+    if workspace is None:
+        workspace = _empty_bytes(max(N, 1) * 8 + 256, W.device)
+    check(lib().bitlinear_quantize_weights_b3(_ptr(W), N, K, _ptr(packed), _ptr(gamma),
+                                              _ptr(workspace), workspace.numel(), int(glu),
+                                              _stream()),
+          "bitlinear_quantize_weights_b3")
+    return packed, gamma
+
+
+def pack_ternary_b3(Wq: torch.Tensor) -> torch.Tensor:
+    N, K = Wq.shape
+    packed = torch.empty(max(packed_bytes_b3(N, K), 1), dtype=torch.uint8, device=Wq.device)
+    check(lib().bitlinear_pack_ternary_b3(_ptr(Wq), N, K, _ptr(packed), _stream()),
+          "bitlinear_pack_ternary_b3")
+    return packed
+
+
+def unpack_ternary_b3(packed: torch.Tensor, N: int, K: int) -> torch.Tensor:
+    Wq = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    check(lib().bitlinear_unpack_ternary_b3(_ptr(packed), N, K, _ptr(Wq), _stream()),
+          "bitlinear_unpack_ternary_b3")
+    return Wq
 
 
 def pack_ternary(Wq: torch.Tensor) -> torch.Tensor:
@@ -326,9 +374,10 @@ class Group:
     GPU and Y [M][N] float32 (allocated when None), optionally followed by a
     subln gain (float32 [K] or None) and its epsilon (default 1e-5).  The
     tensors must stay alive while the group is used; ``forward()`` enqueues
-    on torch's stream."""
+    on torch's stream.  ``fmt="b3"``: every layer's weights are in the
+    base-3 layout (quantize_weights_b3)."""
 
-    def __init__(self, layers):
+    def __init__(self, layers, fmt=None):
         L = lib()
         arr = (GroupOp * len(layers))()
         self.keep = []
@@ -346,7 +395,8 @@ class Group:
                 Y = torch.empty((M, _out_cols(N, epilogue)), dtype=torch.float32,
                                 device=X.device)
             arr[i] = GroupOp(_ptr(X), _dtype_code(X), EPI[epilogue], K, N, _ptr(packed),
-                             _ptr(gamma), _ptr(Y), _ptr(gain), eps if gain is not None else 0.0)
+                             _ptr(gamma), _ptr(Y), _ptr(gain), eps if gain is not None else 0.0,
+                             FMT[fmt])
             self.keep += [X, packed, gamma] + ([gain] if gain is not None else [])
             self.outputs.append(Y)
         self.M = M

@@ -56,7 +56,27 @@ bitlinear_status check_nk(int64_t N, int64_t K) {
   return BITLINEAR_OK;
 }
 
+// Shapes of the base-3 layout: N % 16 == 0, K % 16 == 0 (K is padded to a
+// multiple of 320 inside the layout).
+bitlinear_status check_nk_b3(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return fail(BITLINEAR_ERR_SHAPE, "N=%lld K=%lld must be >= 1", (long long)N, (long long)K);
+  if (N % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "N=%lld is not a multiple of 16", (long long)N);
+  if (K % 16 != 0) return fail(BITLINEAR_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (K > kMaxK) return fail(BITLINEAR_ERR_SHAPE, "K=%lld exceeds %lld", (long long)K, (long long)kMaxK);
+  if (N > kMaxN) return fail(BITLINEAR_ERR_SHAPE, "N=%lld exceeds %lld", (long long)N, (long long)kMaxN);
+  return BITLINEAR_OK;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool is_b3(const bitlinear_group_op& o) { return o.format == BITLINEAR_FMT_B3; }
+
+// 1 KiB weight blocks per 16-row tile of a layer (its cost unit), and the K
+// its kernel holds activations for (padded to 320 for the base-3 layout).
+int64_t op_kblocks(const bitlinear_group_op& o) {
+  return is_b3(o) ? bl_b3_padded_k(o.K) / 320 : o.K / 256;
+}
+int64_t op_lds_k(const bitlinear_group_op& o) { return is_b3(o) ? bl_b3_padded_k(o.K) : o.K; }
 
 // Workspace of the large-M path: int8 activations, scales, row sums.
 // Forward workspace above the fused small-M path: quantized activations,
@@ -88,10 +108,10 @@ void group_split(const bitlinear_group_op* ops, int n_ops, int64_t M, int64_t* s
   const int64_t pct = bl_group_prequantizes((int)M) ? kGroupStaticPercentPreq
                                                     : kGroupStaticPercentInline;
   int64_t total = 0;
-  for (int i = 0; i < n_ops; ++i) total += (ops[i].N / 16) * (ops[i].K / 256);
+  for (int i = 0; i < n_ops; ++i) total += (ops[i].N / 16) * op_kblocks(ops[i]);
   int64_t cost = 0, item = 0, s = -1, n = 0;
   for (int i = 0; i < n_ops; ++i) {
-    const int64_t tiles = ops[i].N / 16, kb = ops[i].K / 256;
+    const int64_t tiles = ops[i].N / 16, kb = op_kblocks(ops[i]);
     int64_t t = 0;
     if (s < 0) {
       // tiles of this layer still inside the static part
@@ -170,9 +190,17 @@ bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M
       return fail(BITLINEAR_ERR_DTYPE, "op %d: unknown dtype %d", i, (int)o.dtype);
     if (!valid_epi(o.epi))
       return fail(BITLINEAR_ERR_ARG, "op %d: unknown epilogue %d", i, (int)o.epi);
-    bitlinear_status st = check_nk(o.N, o.K);
+    if (o.format != BITLINEAR_FMT_2BIT && o.format != BITLINEAR_FMT_B3)
+      return fail(BITLINEAR_ERR_ARG, "op %d: unknown weight format %d", i, (int)o.format);
+    if (o.format != ops[0].format)
+      return fail(BITLINEAR_ERR_ARG, "op %d: every layer of a group needs the same weight format",
+                  i);
+    if (is_b3(o) && !skinny)
+      return fail(BITLINEAR_ERR_SHAPE, "op %d: base-3 weights need M <= %d, got %lld", i,
+                  kGroupMaxM, (long long)M);
+    bitlinear_status st = is_b3(o) ? check_nk_b3(o.N, o.K) : check_nk(o.N, o.K);
     if (st != BITLINEAR_OK) return st;
-    if (skinny && o.K > kGroupMaxK)
+    if (skinny && op_lds_k(o) > kGroupMaxK)
       return fail(BITLINEAR_ERR_SHAPE, "op %d: K=%lld exceeds %d (M <= %d)", i, (long long)o.K,
                   kGroupMaxK, kGroupMaxM);
     if (!o.X || !o.packed || !o.gamma || !o.Y) return fail(BITLINEAR_ERR_NULL, "op %d: X, packed, gamma and Y are required", i);
@@ -185,7 +213,7 @@ bitlinear_status check_group(const bitlinear_group_op* ops, int n_ops, int64_t M
   if (items > 0x7fffffff) return fail(BITLINEAR_ERR_SHAPE, "too many output tiles");
   if (!skinny) return BITLINEAR_OK;
   int64_t max_k = 0;
-  for (int i = 0; i < n_ops; ++i) max_k = ops[i].K > max_k ? ops[i].K : max_k;
+  for (int i = 0; i < n_ops; ++i) max_k = std::max(max_k, op_lds_k(ops[i]));
   if (bl_group_lds_bytes((int)M, (int)max_k) > kGroupMaxLds)
     return fail(BITLINEAR_ERR_SHAPE,
                 "M=%lld tokens of K=%lld activations do not fit in LDS (M * (K + 16) + M * 2048 "
@@ -238,6 +266,7 @@ struct bitlinear_group {
   int threads;
   bool norm;  // some layer has a subln gain
   bool glu;   // some layer has the gated epilogue
+  bool b3;    // the layers' weights use the base-3 layout
   bool gemm;
   int n_items;  // items over all layers (output tiles in the GEMM mode)
   int n_units;  // shared work units of the skinny kernel
@@ -332,6 +361,57 @@ bitlinear_status bitlinear_unpack_ternary(const uint8_t* packed, int64_t N, int6
     return fail(BITLINEAR_ERR_ALIGN, "Wq and packed must be 16-byte aligned");
   return from_hip(bl_launch_unpack(packed, N, K, Wq, static_cast<hipStream_t>(stream)),
                   "bitlinear_unpack_ternary");
+}
+
+size_t bitlinear_packed_bytes_b3(int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || N % 16 != 0 || K % 16 != 0) return 0;
+  return (size_t)N * (size_t)bl_b3_padded_k(K) / 5;
+}
+
+bitlinear_status bitlinear_quantize_weights_b3(const float* W, int64_t N, int64_t K,
+                                               uint8_t* packed, float* gamma, void* ws,
+                                               size_t ws_bytes, int glu, void* stream) {
+  if (!W || !packed || !gamma) return fail(BITLINEAR_ERR_NULL, "W, packed and gamma are required");
+  bitlinear_status st = check_nk_b3(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (glu && N % 32 != 0)
+    return fail(BITLINEAR_ERR_SHAPE, "a fused gate+up matrix needs N %% 32 == 0, got %lld",
+                (long long)N);
+  if (!aligned16(W) || !aligned16(packed) || !aligned16(gamma))
+    return fail(BITLINEAR_ERR_ALIGN, "W, packed and gamma must be 16-byte aligned");
+  const size_t need = align256((size_t)N * sizeof(double));
+  if (!ws || ws_bytes < need)
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* row_sum = static_cast<double*>(ws);
+  hipError_t e = bl_launch_absmean_rows(W, N, K, row_sum, s);
+  if (e == hipSuccess) e = bl_launch_absmean_final(row_sum, N, K, gamma, s);
+  if (e == hipSuccess) e = bl_launch_quant_pack_b3(W, N, K, gamma, packed, s, glu != 0);
+  return from_hip(e, "bitlinear_quantize_weights_b3");
+}
+
+bitlinear_status bitlinear_pack_ternary_b3(const int8_t* Wq, int64_t N, int64_t K,
+                                           uint8_t* packed, void* stream) {
+  if (!Wq || !packed) return fail(BITLINEAR_ERR_NULL, "Wq and packed are required");
+  bitlinear_status st = check_nk_b3(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (!aligned16(Wq) || !aligned16(packed))
+    return fail(BITLINEAR_ERR_ALIGN, "Wq and packed must be 16-byte aligned");
+  return from_hip(bl_launch_pack_b3(Wq, N, K, packed, static_cast<hipStream_t>(stream)),
+                  "bitlinear_pack_ternary_b3");
+}
+
+bitlinear_status bitlinear_unpack_ternary_b3(const uint8_t* packed, int64_t N, int64_t K,
+                                             int8_t* Wq, void* stream) {
+  if (!Wq || !packed) return fail(BITLINEAR_ERR_NULL, "packed and Wq are required");
+  bitlinear_status st = check_nk_b3(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (!aligned16(Wq) || !aligned16(packed))
+    return fail(BITLINEAR_ERR_ALIGN, "Wq and packed must be 16-byte aligned");
+  return from_hip(bl_launch_unpack_b3(packed, N, K, Wq, static_cast<hipStream_t>(stream)),
+                  "bitlinear_unpack_ternary_b3");
 }
 
 static bitlinear_status quantize_acts_impl(const void* X, bitlinear_dtype dtype, int64_t M,
@@ -551,6 +631,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     t.item_begin = (int32_t)item;
     t.norm_gain = o.norm_gain;
     t.norm_eps = o.norm_eps;
+    t.fmt = (int32_t)o.format;
     if (o.norm_gain) norm = true;
     t.xq_off = xq_off;
     xq_off += (int64_t)align256((size_t)M * (size_t)o.K);
@@ -558,14 +639,14 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
     // either way an item's cost is proportional to K.
     const int64_t items = skinny ? o.N / 16 : bl_group_gemm_tiles((int)M, (int)o.N);
     item += items;
-    if (o.K > max_k) max_k = (int)o.K;
+    if (op_lds_k(o) > max_k) max_k = (int)op_lds_k(o);
   }
   // As many workgroups as fit on the chip at once, at most four per compute
   // unit (skinny: each holds one layer's int8 activations in LDS and takes
   // work units from the queue; GEMM: output tiles strided).
   int threads = 256, per_cu = 1;
   if (skinny) {
-    e = bl_group_plan((int)M, max_k, norm, &threads, &per_cu);
+    e = bl_group_plan((int)M, max_k, norm, is_b3(ops[0]), &threads, &per_cu);
     if (e != hipSuccess) return from_hip(e, "bitlinear_group_create");
   } else {
     per_cu = bl_group_gemm_blocks_per_cu((int)M);
@@ -590,14 +671,14 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
       int64_t it = 0;
       for (int i = 0; i < n_ops && it < split; ++i) {
         const int64_t tiles = std::min<int64_t>(ops[i].N / 16, split - it);
-        static_cost += tiles * (ops[i].K / 256);
+        static_cost += tiles * op_kblocks(ops[i]);
         it += tiles;
       }
     }
     int g = 0;
     int64_t before = 0, it = 0;
     for (int i = 0; i < n_ops && it < split; ++i) {
-      const int64_t kb = ops[i].K / 256;
+      const int64_t kb = op_kblocks(ops[i]);
       const int64_t tiles = ops[i].N / 16;
       for (int64_t t = 0; t < tiles && it < split; ++t, ++it) {
         while (g <= G && before * G >= (int64_t)g * static_cost) wg_begin[(size_t)g++] = (int)it;
@@ -632,6 +713,7 @@ bitlinear_status bitlinear_group_create(const bitlinear_group_op* ops, int n_ops
   g->threads = threads;
   g->norm = norm;
   g->glu = glu;
+  g->b3 = is_b3(ops[0]);
   g->gemm = !skinny;
   g->n_items = (int)item;
   g->n_units = (int)L.n_units;
@@ -658,7 +740,7 @@ bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream)
     return from_hip(e, "bitlinear_group_forward");
   }
   return from_hip(bl_launch_group(g->ops, g->n_ops, g->M, g->wg_begin, g->units, g->n_units,
-                                  g->queue, g->G, g->max_k, g->threads, g->norm, g->xq, g->sx,
+                                  g->queue, g->G, g->max_k, g->threads, g->norm, g->b3, g->xq, g->sx,
                                   g->rs,
                                   static_cast<hipStream_t>(stream)),
                   "bitlinear_group_forward");

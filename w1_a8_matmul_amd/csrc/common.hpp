@@ -16,6 +16,9 @@ constexpr uint32_t kCodeMask = 0x03030303u;
 constexpr int kTileRows = 16;
 constexpr int kTileCols = 256;
 constexpr int kTileBytes = 1024;
+// The base-3 layout (five codes per byte): tiles of 16 rows x 320 columns,
+// also 1 KiB; K padded up to a multiple of 320 with code 0.
+constexpr int kB3TileCols = 320;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -177,6 +180,14 @@ hipError_t bl_launch_quant_pack(const float* W, int64_t N, int64_t K, const floa
                                 bool glu = false);
 hipError_t bl_launch_pack(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packed,
                           hipStream_t s);
+// The base-3 layout: K padded to a multiple of 320 (bl_b3_padded_k).
+inline int64_t bl_b3_padded_k(int64_t K) { return (K + bl::kB3TileCols - 1) / bl::kB3TileCols * bl::kB3TileCols; }
+hipError_t bl_launch_quant_pack_b3(const float* W, int64_t N, int64_t K, const float* gamma,
+                                   uint8_t* packed, hipStream_t s, bool glu);
+hipError_t bl_launch_pack_b3(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packed,
+                             hipStream_t s);
+hipError_t bl_launch_unpack_b3(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
+                               hipStream_t s);
 hipError_t bl_launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
                             hipStream_t s);
 // Per-token activation quantization; also zeroes n_zero ints at `zero`

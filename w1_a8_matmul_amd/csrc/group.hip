@@ -54,6 +54,59 @@ __device__ __forceinline__ void mfma_block(const uint4 w, const int8_t* xa, v4i&
   }
 }
 
+// The base-3 layout (five codes per byte): the lane's 16 bytes (row l % 16,
+// columns 80q .. 80q + 79 of a 320-column block) decode into 20 dwords of
+// four int8 codes, dword t holding columns 4t .. 4t + 3 (byte b of packed
+// word j carries columns 20j + 4i + b as its base-3 digits i).  MFMA m
+// contracts dwords 4m .. 4m + 3, columns 16m .. 16m + 15, with the same 16
+// activation bytes.  Digits come two bytes at a time in 16-bit lanes:
+// v / 3 = (v * 171) >> 9 exactly for v <= 255, digit = v - 3 (v / 3).
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t us2_bits(us2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// The five digit dwords of one packed word: d_i holds digit i of its four
+// bytes (codes of four consecutive columns).
+struct B3Digits {
+  uint32_t d0, d1, d2, d3, d4;
+};
+
+__device__ __forceinline__ B3Digits b3_word_digits(uint32_t w) {
+  us2 lo = __builtin_bit_cast(us2, w & 0x00ff00ffu);         // bytes 0 and 2
+  us2 hi = __builtin_bit_cast(us2, (w >> 8) & 0x00ff00ffu);  // bytes 1 and 3
+  uint32_t d[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const us2 ql = (lo * (unsigned short)171) >> (unsigned short)9;
+    const us2 qh = (hi * (unsigned short)171) >> (unsigned short)9;
+    const us2 dl = lo - ql * (unsigned short)3, dh = hi - qh * (unsigned short)3;
+    d[i] = us2_bits(dl) | (us2_bits(dh) << 8);
+    lo = ql;
+    hi = qh;
+  }
+  return B3Digits{d[0], d[1], d[2], d[3], us2_bits(lo) | (us2_bits(hi) << 8)};
+}
+
+// Five MFMAs per block, each fed as soon as its 16 codes are decoded: the
+// 20 digit dwords run through the four words in order, four per MFMA.
+__device__ __forceinline__ void mfma_block_b3(const uint4 w, const int8_t* xa, v4i& acc0,
+                                              v4i& acc1) {
+  auto mma = [&](int m, uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, v4i& acc) {
+    const v4i a = *reinterpret_cast<const v4i*>(xa + 16 * m);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, v4i{(int)c0, (int)c1, (int)c2, (int)c3},
+                                                acc, 0, 0, 0);
+  };
+  const B3Digits x = b3_word_digits(w.x);
+  mma(0, x.d0, x.d1, x.d2, x.d3, acc0);
+  const B3Digits y = b3_word_digits(w.y);
+  mma(1, x.d4, y.d0, y.d1, y.d2, acc1);
+  const B3Digits z = b3_word_digits(w.z);
+  mma(2, y.d3, y.d4, z.d0, z.d1, acc0);
+  const B3Digits t = b3_word_digits(w.w);
+  mma(3, z.d2, z.d3, z.d4, t.d0, acc1);
+  mma(4, t.d1, t.d2, t.d3, t.d4, acc0);
+}
+
 template <int NT>
 struct Smem {
   float red_f[NT / kWave];
@@ -69,8 +122,9 @@ struct Smem {
 // segment copies its layer's int8 rows, scales and row sums into LDS instead.
 // NORM (inline quantization only): layers with a subln gain get it applied
 // before their quantization.  MR (inline quantization, M > 1): the next
-// token row is loaded while the current one is quantized.
-template <int NT, int KCH, int DT, bool PREQ, bool NORM, bool MR>
+// token row is loaded while the current one is quantized.  B3: the weights
+// use the base-3 layout (blocks of 16 rows x 320 columns, K padded to 320).
+template <int NT, int KCH, int DT, bool PREQ, bool NORM, bool MR, bool B3>
 __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, int last,
                                             bool quantize, int8_t* xs, int xstride,
                                             float* s_sx, int* s_rs, float* s_y, Smem<NT>& sm,
@@ -81,14 +135,15 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   constexpr int kThreads = NT;
   constexpr int kWaves = NT / kWave;
   constexpr int C = kChunk;
+  constexpr int kBlockCols = B3 ? kB3TileCols : kTileCols;  // columns per 1 KiB block
   const int K = o.K;
-  const int kblocks = K / kTileCols;
+  const int kblocks = B3 ? (K + kB3TileCols - 1) / kB3TileCols : K / kTileCols;
   const int nc = (kblocks + C - 1) / C;
   const int stride = kWaves;
   const int mine = first + wave;
   const int n_mine = mine < last ? (last - mine + stride - 1) / stride : 0;
   const int total = n_mine * nc;
-  const int q16 = lane >> 4;                     // 64-column quarter held by this lane
+  const int q16 = lane >> 4;                     // quarter of the block held by this lane
   const int arow = min(lane & 15, M - 1);        // token row of this lane's A operand
 
   // Chunk cursors (tile, chunk within the tile) advance with selects only:
@@ -196,7 +251,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   __syncthreads();
 
   const float gamma = *o.gamma;
-  const int8_t* xrow = xs + arow * xstride + q16 * 64;
+  const int8_t* xrow = xs + arow * xstride + q16 * (kBlockCols / 4);
   v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
 
   // D layout: lane l holds tile row l%16 and tokens 4*(l/16) + r, r = 0..3.
@@ -204,7 +259,10 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
 #pragma unroll
     for (int i = 0; i < C; ++i) {
       const int b = min(q.c * C + i, kblocks - 1);  // past the end: zero codes, any x
-      mfma_block(buf[i], xrow + b * kTileCols, acc0, acc1);
+      if constexpr (B3)
+        mfma_block_b3(buf[i], xrow + b * kBlockCols, acc0, acc1);
+      else
+        mfma_block(buf[i], xrow + b * kBlockCols, acc0, acc1);
     }
     if (q.c == nc - 1) {
       const v4i d = acc0 + acc1;
@@ -283,7 +341,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
 // counts the workgroups that found the queue empty; the last of them puts
 // both back to zero for the next launch.  A layer's int8 activations are
 // quantized (or copied) whenever a workgroup moves to a new layer.
-template <int NT, int KCH, bool PREQ, bool NORM, bool MR>
+template <int NT, int KCH, bool PREQ, bool NORM, bool MR, bool B3>
 __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ ops, int n_ops,
                                                    int M, int max_k,
                                                    const int* __restrict__ wg_begin,
@@ -307,18 +365,19 @@ __global__ __launch_bounds__(NT) void group_kernel(const GroupOp* __restrict__ o
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int quantized_op = -1;
   // Tiles first .. end-1 of layer op (end - first <= kSegTiles).
-  auto segment = [&](int op, int first, int end) {
+  auto segment = [&](int op, int first, int end) __attribute__((always_inline)) {
     const GroupOp o = ops[op];
     const bool quantize = quantized_op != op;
     if (PREQ)
-      run_segment<NT, KCH, 0, true, false, false>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
-                                    sm, xq, sx, rs, op, wave, lane);
+      run_segment<NT, KCH, 0, true, false, false, B3>(o, M, first, end, quantize, xs, xstride,
+                                                      s_sx, s_rs, s_y, sm, xq, sx, rs, op, wave,
+                                                      lane);
     else if (o.dtype == 1)
-      run_segment<NT, KCH, 1, false, NORM, MR>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
-                                     sm, xq, sx, rs, op, wave, lane);
+      run_segment<NT, KCH, 1, false, NORM, MR, B3>(o, M, first, end, quantize, xs, xstride, s_sx,
+                                                   s_rs, s_y, sm, xq, sx, rs, op, wave, lane);
     else
-      run_segment<NT, KCH, 0, false, NORM, MR>(o, M, first, end, quantize, xs, xstride, s_sx, s_rs, s_y,
-                                     sm, xq, sx, rs, op, wave, lane);
+      run_segment<NT, KCH, 0, false, NORM, MR, B3>(o, M, first, end, quantize, xs, xstride, s_sx,
+                                                   s_rs, s_y, sm, xq, sx, rs, op, wave, lane);
     __syncthreads();  // before the next segment overwrites xs, the scales, s_y or s_unit
     quantized_op = op;
   };
@@ -433,54 +492,62 @@ __global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restr
 
 // Activation chunks per thread: each covers NT * 8 elements of a row.
 // Kernel modes: pre-quantized (the quantization launch applies any subln);
-// inline quantization without or with subln gains, of one row or of several.
-template <int NT, bool PREQ, bool NORM, bool MR>
+// inline quantization without or with subln gains, of one row or of
+// several; each for the 2-bit and the base-3 weight layout.
+template <int NT, bool PREQ, bool NORM, bool MR, bool B3>
 const void* kernel_for(int max_k) {
   if (max_k <= NT * 8 * 2)
-    return reinterpret_cast<const void*>(&group_kernel<NT, 2, PREQ, NORM, MR>);
+    return reinterpret_cast<const void*>(&group_kernel<NT, 2, PREQ, NORM, MR, B3>);
   if (max_k <= NT * 8 * 4)
-    return reinterpret_cast<const void*>(&group_kernel<NT, 4, PREQ, NORM, MR>);
-  return reinterpret_cast<const void*>(&group_kernel<NT, 6, PREQ, NORM, MR>);
+    return reinterpret_cast<const void*>(&group_kernel<NT, 4, PREQ, NORM, MR, B3>);
+  return reinterpret_cast<const void*>(&group_kernel<NT, 6, PREQ, NORM, MR, B3>);
 }
 
-template <int NT, bool NORM>
+template <int NT, bool NORM, bool B3>
 const void* kernel_for(bool mr, int max_k) {
-  return mr ? kernel_for<NT, false, NORM, true>(max_k) : kernel_for<NT, false, NORM, false>(max_k);
+  return mr ? kernel_for<NT, false, NORM, true, B3>(max_k)
+            : kernel_for<NT, false, NORM, false, B3>(max_k);
 }
 
-// The kernel a launch for M tokens uses.
+template <bool B3>
 const void* kernel_for(int threads, int M, bool norm, int max_k) {
   const bool preq = bl_group_prequantizes(M), mr = M > 1;
   if (threads == 512) {
-    if (preq) return kernel_for<512, true, false, false>(max_k);
-    return norm ? kernel_for<512, true>(mr, max_k) : kernel_for<512, false>(mr, max_k);
+    if (preq) return kernel_for<512, true, false, false, B3>(max_k);
+    return norm ? kernel_for<512, true, B3>(mr, max_k) : kernel_for<512, false, B3>(mr, max_k);
   }
-  if (preq) return kernel_for<256, true, false, false>(max_k);
-  return norm ? kernel_for<256, true>(mr, max_k) : kernel_for<256, false>(mr, max_k);
+  if (preq) return kernel_for<256, true, false, false, B3>(max_k);
+  return norm ? kernel_for<256, true, B3>(mr, max_k) : kernel_for<256, false, B3>(mr, max_k);
 }
 
-template <int NT, bool PREQ, bool NORM, bool MR>
+// The kernel a launch for M tokens uses.
+const void* kernel_for(int threads, int M, bool norm, bool b3, int max_k) {
+  return b3 ? kernel_for<true>(threads, M, norm, max_k)
+            : kernel_for<false>(threads, M, norm, max_k);
+}
+
+template <int NT, bool PREQ, bool NORM, bool MR, bool B3>
 void launch(const GroupOp* ops, int n_ops, int M, const int* wg_begin, const GroupUnit* units,
             int n_units, int* queue, int G, int max_k, size_t lds, const int8_t* xq,
             const float* sx, const int* rs, hipStream_t s) {
   if (max_k <= NT * 8 * 2)
-    hipLaunchKernelGGL((group_kernel<NT, 2, PREQ, NORM, MR>), dim3(G), dim3(NT), lds, s, ops,
-                       n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
+    hipLaunchKernelGGL((group_kernel<NT, 2, PREQ, NORM, MR, B3>), dim3(G), dim3(NT), lds, s,
+                       ops, n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else if (max_k <= NT * 8 * 4)
-    hipLaunchKernelGGL((group_kernel<NT, 4, PREQ, NORM, MR>), dim3(G), dim3(NT), lds, s, ops,
-                       n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
+    hipLaunchKernelGGL((group_kernel<NT, 4, PREQ, NORM, MR, B3>), dim3(G), dim3(NT), lds, s,
+                       ops, n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
   else
-    hipLaunchKernelGGL((group_kernel<NT, 6, PREQ, NORM, MR>), dim3(G), dim3(NT), lds, s, ops,
-                       n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
+    hipLaunchKernelGGL((group_kernel<NT, 6, PREQ, NORM, MR, B3>), dim3(G), dim3(NT), lds, s,
+                       ops, n_ops, M, max_k, wg_begin, units, n_units, queue, xq, sx, rs);
 }
 
-template <int NT>
+template <int NT, bool B3>
 void launch(bool norm, const GroupOp* ops, int n_ops, int M, const int* wg_begin,
             const GroupUnit* units, int n_units, int* queue, int G, int max_k, size_t lds,
             const int8_t* xq, const float* sx, const int* rs, hipStream_t s) {
-#define BL_GROUP_LAUNCH(P, NM, MRV)                                                      \
-  launch<NT, P, NM, MRV>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq, \
-                         sx, rs, s)
+#define BL_GROUP_LAUNCH(P, NM, MRV)                                                         \
+  launch<NT, P, NM, MRV, B3>(ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, \
+                             xq, sx, rs, s)
   if (bl_group_prequantizes(M))
     BL_GROUP_LAUNCH(true, false, false);
   else if (norm)
@@ -490,10 +557,10 @@ void launch(bool norm, const GroupOp* ops, int n_ops, int M, const int* wg_begin
 #undef BL_GROUP_LAUNCH
 }
 
-int blocks_per_cu(int threads, int M, bool norm, size_t lds, int max_k) {
+int blocks_per_cu(int threads, int M, bool norm, bool b3, size_t lds, int max_k) {
   int blocks = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &blocks, kernel_for(threads, M, norm, max_k), threads, lds);
+      &blocks, kernel_for(threads, M, norm, b3, max_k), threads, lds);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
@@ -521,12 +588,12 @@ size_t bl_group_lds_bytes(int M, int max_k) {
   return (size_t)M * (size_t)(max_k + 16) + (size_t)M * kSegTiles * kTileRows * sizeof(float);
 }
 
-hipError_t bl_group_plan(int M, int max_k, bool norm, int* threads, int* per_cu) {
+hipError_t bl_group_plan(int M, int max_k, bool norm, bool b3, int* threads, int* per_cu) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
   for (int nt : {256, 512}) {
     if (lds > 64 * 1024) {
       const hipError_t e =
-          hipFuncSetAttribute(kernel_for(nt, M, norm, max_k),
+          hipFuncSetAttribute(kernel_for(nt, M, norm, b3, max_k),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
@@ -534,20 +601,20 @@ hipError_t bl_group_plan(int M, int max_k, bool norm, int* threads, int* per_cu)
   // Four-wave workgroups while at least two fit on a compute unit (more,
   // shorter weight streams); eight-wave ones when the activations take so
   // much LDS that only one does.
-  const int b256 = blocks_per_cu(256, M, norm, lds, max_k);
+  const int b256 = blocks_per_cu(256, M, norm, b3, lds, max_k);
   if (b256 >= 2) {
     *threads = 256;
     *per_cu = b256;
   } else {
     *threads = 512;
-    *per_cu = blocks_per_cu(512, M, norm, lds, max_k);
+    *per_cu = blocks_per_cu(512, M, norm, b3, lds, max_k);
   }
   return hipSuccess;
 }
 
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin,
                            const GroupUnit* units, int n_units, int* queue, int G, int max_k,
-                           int threads, bool norm, int8_t* xq, float* sx, int* rs,
+                           int threads, bool norm, bool b3, int8_t* xq, float* sx, int* rs,
                            hipStream_t s) {
   const size_t lds = bl_group_lds_bytes(M, max_k);
   const bool preq = bl_group_prequantizes(M);
@@ -555,11 +622,17 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
     const hipError_t e = bl_launch_group_quant(ops, n_ops, M, max_k, xq, sx, rs, s);
     if (e != hipSuccess) return e;
   }
-  if (threads == 512)
-    launch<512>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq, sx, rs,
-                s);
+  if (threads == 512 && b3)
+    launch<512, true>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                      sx, rs, s);
+  else if (threads == 512)
+    launch<512, false>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                       sx, rs, s);
+  else if (b3)
+    launch<256, true>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                      sx, rs, s);
   else
-    launch<256>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq, sx, rs,
-                s);
+    launch<256, false>(norm, ops, n_ops, M, wg_begin, units, n_units, queue, G, max_k, lds, xq,
+                       sx, rs, s);
   return hipGetLastError();
 }

@@ -16,7 +16,8 @@ struct GroupOp {
   int32_t dtype, epi;      // epi: kEpiNone, kEpiRelu2 or kEpiGlu (Y then [M][N/2])
   int32_t item_begin;      // index of this layer's first 16-row tile in the flat list
   float norm_eps;          // subln epsilon
-  int32_t pad[2];
+  int32_t fmt;             // weight layout: 0 two-bit codes, 1 base-3 (kernels take it as a template)
+  int32_t pad;
 };
 static_assert(sizeof(GroupOp) == 80, "GroupOp must stay 80 bytes");
 
@@ -64,16 +65,17 @@ size_t bl_group_lds_bytes(int M, int max_k);
 // Chooses the workgroup size (256 or 512 threads) and reports how many
 // workgroups fit on one compute unit; also allows the kernel the dynamic
 // LDS it needs.  norm: some layer has a subln gain.
-hipError_t bl_group_plan(int M, int max_k, bool norm, int* threads, int* per_cu);
+hipError_t bl_group_plan(int M, int max_k, bool norm, bool b3, int* threads, int* per_cu);
 
-// Grouped forward: G workgroups of `threads` threads; workgroup g first runs
+// Grouped forward (b3: every layer's weights in the base-3 layout, and max_k
+// the largest padded K): G workgroups of `threads` threads; workgroup g first runs
 // tiles wg_begin[g] .. wg_begin[g+1]-1, then takes the n_units units from the
 // queue (two ints, zero on entry and left zero); max_k the largest K.  xq,
 // sx, rs: the quantized activations, scales and row sums (used when
 // bl_group_prequantizes(M)); norm as for bl_group_plan.
 hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin,
                            const GroupUnit* units, int n_units, int* queue, int G, int max_k,
-                           int threads, bool norm, int8_t* xq, float* sx, int* rs,
+                           int threads, bool norm, bool b3, int8_t* xq, float* sx, int* rs,
                            hipStream_t s);
 
 // Above kGroupMaxM tokens a group runs as one persistent tiled int8 GEMM over
