@@ -2,7 +2,8 @@
 """Benchmark of the W1.58A8 BitLinear forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--tokens M] [--grouped | --per-linear] [--b3] [--no-sub] [--no-cpu]
+                    [--tokens M] [--grouped | --per-linear] [--b3] [--lut] [--no-sub]
+                    [--no-cpu]
 
 A step is one pass of the per-token hot path over one batch of synthetic
 input: per-token absmax int8 quantization, load + unpack of the packed
@@ -18,8 +19,9 @@ forward per step ("µs/token for all linears").  Two weight sets alternate, so
 no step finds its weights in the 256 MB Infinity Cache.  The same JSON line
 carries keyed sub-records (``sub``) for the decode GEMV pair (M = 1, up ->
 ReLU^2 -> down, 61 rotating weight copies), the 2B step at M = 4 and 16, and
-the prefill GEMMs at M = 2048 (int8 TOPS), and the 2B step at M = 1 with its
-weights in the base-3 layout (five codes per byte).
+the prefill GEMMs at M = 2048 (int8 TOPS), the 2B step at M = 1 with its
+weights in the base-3 layout (five codes per byte), and the decode pair by
+table lookup instead of multiplies.
 
 Timing: W warm-up steps, then exactly K steps, each as one HIP graph replay
 on torch's stream, bracketed by synchronizations; HIP events around the
@@ -53,6 +55,7 @@ MALL_BYTES = 256 * 1024 * 1024  # Infinity Cache
 # to the kernel version it was taken on (matched by their hash).
 GEMV_SOURCES = ["gemv.hip", "gemv_tile.hpp", "common.hpp"]
 GEMM_SOURCES = ["gemm.hip", "group.hpp", "common.hpp"]
+LUT_SOURCES = ["lut.hip", "gemv_tile.hpp", "common.hpp"]
 GROUP_SOURCES = ["group.hip", "group.hpp", "gemv_tile.hpp", "quant_row.hpp", "common.hpp"]
 # Up to this many tokens the grouped decode quantizes inside its one launch;
 # above, a quantization launch precedes it.
@@ -86,6 +89,8 @@ def parse():
     p.add_argument("--glu", action="store_true",
                    help="gated FFN: pack each gate+up linear (N = 2 x the down projection's K) "
                         "for the gated squared-ReLU epilogue (output N/2)")
+    p.add_argument("--lut", action="store_true",
+                   help="one-token linears by table lookup (bitlinear_forward_lut; per linear)")
     p.add_argument("--b3", action="store_true",
                    help="weights in the base-3 layout (five codes per byte; grouped, M <= 16)")
     p.add_argument("--subln", action="store_true",
@@ -165,9 +170,11 @@ class Runner:
     """A workload at M tokens: its linears and a step function."""
 
     def __init__(self, bl, torch, wl, dev, key, M, grouped, copies=None, subln=False,
-                 glu=False, share_weights=None, fmt=None):
+                 glu=False, share_weights=None, fmt=None, lut=False):
         wk = wl.WORKLOADS[key]
-        self.wk, self.M, self.fmt = wk, M, fmt
+        self.wk, self.M, self.fmt, self.lut = wk, M, fmt, lut
+        if lut and (grouped or M != 1 or subln):
+            raise SystemExit("the lookup-table GEMV runs one linear per launch at M = 1")
         if fmt == "b3" and (not grouped or M > 16):
             raise SystemExit("base-3 weights run in the grouped decode forward (M <= 16)")
         self.copies = copies or weight_copies(wk.weights_per_step // 4)
@@ -214,6 +221,11 @@ class Runner:
         c = (i + self.offset) % self.copies
         if self.groups is not None:
             self.groups[c].forward()
+        elif self.lut:
+            for lin in self.lins:  # in order, so the chain's down reads up's output
+                epi = "relu2" if (self.wk.chain_relu2 and lin is self.lins[0]) else lin.epi
+                bl.forward_lut(lin.X, lin.packed[c], lin.gamma[c], lin.N, epilogue=epi,
+                               out=lin.Y)
         elif self.wk.chain_relu2:
             up, down = self.lins
             bl.forward(up.X, up.packed[c], up.gamma[c], up.N, epilogue="relu2", out=up.Y,
@@ -322,6 +334,8 @@ def roofline_single(args, torch, bl, runner, metric_kind):
         if gemm:
             bl.forward_q(Xq, sx, rs, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi,
                          out=dom.Y, workspace=qws)
+        elif runner.lut:
+            bl.forward_lut(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y)
         else:
             bl.forward(dom.X, dom.packed[c], dom.gamma[c], dom.N, epilogue=epi, out=dom.Y,
                        workspace=dom.ws, norm_gain=dom.gain)
@@ -330,6 +344,9 @@ def roofline_single(args, torch, bl, runner, metric_kind):
     if metric_kind == "tops":
         roof = mfma_roof(dom.ops(), us, f"gemm_q_{dom.K}x{dom.N}_m{M}", GEMM_SOURCES)
         roof["launches_timed"] = "gemm only (forward_q)"
+    elif runner.lut:
+        roof = hbm_roof(dom.bytes(), us, f"lut_gemv_{dom.K}x{dom.N}_m{M}", LUT_SOURCES)
+        roof["launches_timed"] = "one fused launch (lookup tables)"
     else:
         roof = hbm_roof(dom.bytes(), us, f"gemv_{dom.K}x{dom.N}_m{M}", GEMV_SOURCES)
         roof["launches_timed"] = "one fused launch" if dom.ws is None else \
@@ -590,6 +607,16 @@ def sub_records(args, torch, bl, wl, dev, main_runner):
     subs["decode_gemv_pair_m1"] = rec
     del r
 
+    # the same pair by table lookup (bitlinear_forward_lut)
+    r = Runner(bl, torch, wl, dev, "decode_gemv_pair_m1", 1, grouped=False, copies=61, lut=True)
+    ev, wall = time_steps(torch, r, max(steps, 61), warmup)
+    rec = step_record(r, ev, wall, "hbm")
+    rec["roofline"] = roofline_single(args, torch, bl, r, "hbm")
+    rec["launches_per_step"] = 2
+    subs["decode_gemv_pair_m1_lut"] = rec
+    log(f"decode pair by table lookup: {rec['us_per_step']} us")
+    del r
+
     # 2B step at M = 4 and 16, grouped
     share = main_runner if (main_runner.wk.key == "decode_step_2b" and
                             main_runner.groups is not None and
@@ -673,8 +700,10 @@ def main():
     grouped = args.grouped
     if grouped is None:  # default: grouped for the multi-layer decode steps
         grouped = wk.layers > 1 and M <= 64 and not wk.chain_relu2
+    if args.lut:
+        grouped = False
     runner = Runner(bl, torch, wl, dev, args.workload, M, grouped, subln=args.subln,
-                    glu=args.glu, fmt="b3" if args.b3 else None)
+                    glu=args.glu, fmt="b3" if args.b3 else None, lut=args.lut)
     log(f"workload {wk.key} M={M}: {len(runner.lins)} linears, {runner.copies} weight "
         f"copies, offline quantization {runner.quant_ms():.1f} ms per weight set")
     metric_kind = "tops" if M >= 128 else "hbm"
@@ -742,6 +771,7 @@ def main():
             "subln": bool(args.subln),
             "glu": bool(args.glu),
             "weight_format": "b3" if args.b3 else "2bit",
+            "lookup_tables": bool(args.lut),
         },
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 4
+#define BITLINEAR_ABI_VERSION 5
 
 typedef enum {
   BITLINEAR_OK = 0,
@@ -250,6 +250,20 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
                                    const float* gamma, float* Y, bitlinear_epilogue epi,
                                    const bitlinear_debug* dbg, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* The forward of one token (M = 1) by table lookup instead of multiplies,
+ * the method bitnet.cpp's ternary kernels take from T-MAC (dignews.cc
+ * article on BitNet b1.58 2B4T, section 3).  X [1][K] is quantized as in
+ * bitlinear_forward; then, for every pair of columns, a table of the 16 sums
+ * its two 2-bit codes can select is built in LDS, and each 4-bit field of
+ * the packed weights reads one entry.  The int32 sums, and so Y, are the same
+ * bits as bitlinear_forward's; `dbg` as there.  Needs K % 256 == 0 and
+ * K <= 8192 (16.5 bytes of table per column must fit in LDS); N as
+ * bitlinear_forward; no workspace.  Errors as bitlinear_forward. */
+bitlinear_status bitlinear_forward_lut(const void* X, bitlinear_dtype dtype, int64_t K,
+                                       int64_t N, const uint8_t* packed, const float* gamma,
+                                       float* Y, bitlinear_epilogue epi,
+                                       const bitlinear_debug* dbg, void* stream);
 
 /* bitlinear_forward with subln first, fused into the quantization (as in
  * bitlinear_quantize_acts_rmsnorm): norm_gain float [K] (device, 16-byte

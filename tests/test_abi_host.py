@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert L.bitlinear_abi_version() == 4
+    assert L.bitlinear_abi_version() == 5
     for s in range(8):
         assert L.bitlinear_status_string(s).decode()
     assert L.bitlinear_status_string(99).decode() == "unknown status"

@@ -97,9 +97,11 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_int, _p, _sz, _p]
     L.bitlinear_forward_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p,
                                             ctypes.c_int, ctypes.POINTER(Debug), _p]
+    L.bitlinear_forward_lut.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, ctypes.c_int,
+                                        ctypes.POINTER(Debug), _p]
     for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
                  "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
-                 "bitlinear_forward_q", "bitlinear_forward_noalloc",
+                 "bitlinear_forward_q", "bitlinear_forward_noalloc", "bitlinear_forward_lut",
                  "bitlinear_quantize_weights_b3", "bitlinear_pack_ternary_b3",
                  "bitlinear_unpack_ternary_b3"):
         getattr(L, name).restype = ctypes.c_int
@@ -333,6 +335,30 @@ def forward_noalloc(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, 
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # BITLINEAR_NOALLOC_SCRATCH_BYTES
+
+
+def forward_lut(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
+                epilogue: Optional[str] = None, out: Optional[torch.Tensor] = None,
+                debug: bool = False):
+    """The one-token forward by table lookup (X [1][K], K <= 8192): same
+    outputs as forward(); no workspace."""
+    M, K = X.shape
+    if M != 1:
+        raise BitLinearError(f"forward_lut takes one token, got M={M}")
+    if out is None:
+        out = torch.empty((1, _out_cols(N, epilogue)), dtype=torch.float32, device=X.device)
+    dbg = None
+    dbg_struct = None
+    if debug:
+        dbg = {"xq": torch.empty((1, K), dtype=torch.int8, device=X.device),
+               "x_scale": torch.empty(4, dtype=torch.float32, device=X.device)[:1],
+               "acc": torch.empty((1, N), dtype=torch.int32, device=X.device)}
+        dbg_struct = Debug(_ptr(dbg["xq"]), _ptr(dbg["x_scale"]), _ptr(dbg["acc"]))
+    dbg_arg = ctypes.byref(dbg_struct) if dbg_struct is not None else None
+    check(lib().bitlinear_forward_lut(_ptr(X), _dtype_code(X), K, N, _ptr(packed), _ptr(gamma),
+                                      _ptr(out), EPI[epilogue], dbg_arg, _stream()),
+          "bitlinear_forward_lut")
+    return (out, dbg) if debug else out
 
 
 def forward_q_workspace(M: int, K: int, N: int, device) -> torch.Tensor:

@@ -20,7 +20,8 @@ LIBRARY = os.path.join(PKG, "libbitlinear.so")
 PROBES_LIBRARY = os.path.join(PKG, "libbitlinear_probes.so")
 PROBES_SOURCES = ["probes.hip"]
 
-SOURCES = ["abi.cpp", "weights.hip", "acts.hip", "gemv.hip", "gemm.hip", "group.hip"]
+SOURCES = ["abi.cpp", "weights.hip", "acts.hip", "gemv.hip", "gemm.hip", "group.hip",
+           "lut.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

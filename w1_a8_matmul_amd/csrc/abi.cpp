@@ -532,6 +532,32 @@ bitlinear_status bitlinear_forward_rmsnorm(const void* X, bitlinear_dtype dtype,
 }
 
 
+bitlinear_status bitlinear_forward_lut(const void* X, bitlinear_dtype dtype, int64_t K,
+                                       int64_t N, const uint8_t* packed, const float* gamma,
+                                       float* Y, bitlinear_epilogue epi,
+                                       const bitlinear_debug* dbg, void* stream) {
+  if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
+    return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (!valid_epi(epi)) return fail(BITLINEAR_ERR_ARG, "unknown epilogue %d", (int)epi);
+  bitlinear_status st = check_nk(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (K > kLutMaxK)
+    return fail(BITLINEAR_ERR_SHAPE, "K=%lld exceeds %lld (the tables must fit in LDS)",
+                (long long)K, (long long)kLutMaxK);
+  if (!X || !packed || !gamma || !Y)
+    return fail(BITLINEAR_ERR_NULL, "X, packed, gamma and Y are required");
+  int8_t* xq_out = dbg ? dbg->xq_out : nullptr;
+  float* xs_out = dbg ? dbg->xscale_out : nullptr;
+  int32_t* acc_out = dbg ? dbg->acc_out : nullptr;
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(gamma) || !aligned16(Y) ||
+      (xq_out && !aligned16(xq_out)) || (xs_out && !aligned16(xs_out)) ||
+      (acc_out && !aligned16(acc_out)))
+    return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  return from_hip(bl_launch_lut_gemv(X, (int)dtype, K, N, packed, gamma, Y, (int)epi, xq_out,
+                                     xs_out, acc_out, static_cast<hipStream_t>(stream)),
+                  "bitlinear_forward_lut");
+}
+
 bitlinear_status bitlinear_forward_noalloc(const void* X, bitlinear_dtype dtype, int64_t M,
                                            int64_t K, int64_t N, const uint8_t* packed,
                                            const float* gamma, float* Y,

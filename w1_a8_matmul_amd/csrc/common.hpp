@@ -204,6 +204,16 @@ hipError_t bl_launch_gemv(const void* X, int dtype, int64_t M, int64_t K, int64_
                           int8_t* xq_out, float* xscale_out, int32_t* acc_out,
                           hipStream_t s, const float* norm_gain = nullptr,
                           float norm_eps = 0.0f);
+// Lookup-table GEMV for one token (K % 256 == 0, K <= kLutMaxK): int16
+// tables of column-pair sums in LDS indexed by 4-bit fields of the packed
+// codes; same outputs as bl_launch_gemv at M = 1.
+constexpr int64_t kLutMaxK = 8192;
+size_t bl_lut_lds_bytes(int64_t K);
+size_t bl_lut_max_lds_bytes();
+hipError_t bl_launch_lut_gemv(const void* X, int dtype, int64_t K, int64_t N,
+                              const uint8_t* packed, const float* gamma, float* Y, int epi,
+                              int8_t* xq_out, float* xscale_out, int32_t* acc_out,
+                              hipStream_t s);
 // Forward from quantized activations on the int8 MFMA units.  gemm_ws
 // (bl_gemm_workspace_bytes, its first bl_gemm_counter_bytes zero on entry
 // and left zero) lets the last, partial round of tiles be shared along K;
