@@ -575,6 +575,44 @@ def context_probes(torch):
 # ---------------------------------------------------------------------------
 # Records
 # ---------------------------------------------------------------------------
+def ffn_record(torch, bl, wl, dev, launches):
+    """The 2B model's gated FFN for one token (layer 0's gate+up and down
+    weights of the 2B step): gate+up 2560 -> 13824 (fused,
+    gated ReLU^2) then down 6912 -> 2560, two ways -- two plain forwards (the
+    down launch quantizes h itself), and forward_glu_quant (h quantized by the
+    gate+up launch's last workgroup) then forward_q from the codes.  Weight
+    sets rotate past the Infinity Cache; graph-timed, HIP events."""
+    K, N, Kd, Nd = 2560, 13824, 6912, 2560
+    copies = weight_copies(N * K // 4 + Nd * Kd // 4)
+    gu, dn = [], []
+    for c in range(copies):
+        W = wl.gen_weight_device(wl.weight_seed("decode_step_2b", 0, 2) + 100003 * c, N, K, 0.0, dev)
+        gu.append(bl.quantize_weights(W, glu=True))
+        W = wl.gen_weight_device(wl.weight_seed("decode_step_2b", 0, 3) + 100003 * c, Nd, Kd, 0.0, dev)
+        dn.append(bl.quantize_weights(W))
+        del W
+    X = make_acts(torch, wl, wl.act_seed("decode_step_2b", 0, 2), 1, K, "normal_bf16", dev)
+    H = torch.empty((1, N // 2), dtype=torch.float32, device=dev)
+    Y = torch.empty((1, Nd), dtype=torch.float32, device=dev)
+    ws = bl.forward_glu_quant_workspace(dev)
+
+    def plain(i):
+        c = i % copies
+        bl.forward(X, gu[c][0], gu[c][1], N, epilogue="relu2_glu", out=H)
+        bl.forward(H, dn[c][0], dn[c][1], Nd, out=Y)
+
+    def fused(i):
+        c = i % copies
+        _, hq, hs, hr = bl.forward_glu_quant(X, gu[c][0], gu[c][1], N, workspace=ws, out=H)
+        bl.forward_q(hq, hs, hr, dn[c][0], dn[c][1], Nd, out=Y, split_remainder=False)
+
+    t_plain = time_graph(torch, plain, max(launches, copies))
+    t_fused = time_graph(torch, fused, max(launches, copies))
+    return {"us_two_forwards": round(t_plain, 3), "us_glu_quant_then_forward_q": round(t_fused, 3),
+            "weight_copies_rotated": copies, "tokens": 1,
+            "note": "gate+up 2560->13824 with the gated ReLU^2, down 6912->2560"}
+
+
 def step_record(runner, ev_ms, wall_ms, metric_kind):
     """Throughput of one workload line from its per-step event time."""
     bytes_step, ops_step = runner.bytes_step(), runner.ops_step()
@@ -616,6 +654,11 @@ def sub_records(args, torch, bl, wl, dev, main_runner):
     subs["decode_gemv_pair_m1_lut"] = rec
     log(f"decode pair by table lookup: {rec['us_per_step']} us")
     del r
+
+    # the 2B gated FFN at one token, with and without the fused quantization of h
+    subs["decode_ffn_2b_m1"] = ffn_record(torch, bl, wl, dev, max(steps, 61))
+    log(f"gated FFN, one token: {subs['decode_ffn_2b_m1']}")
+    torch.cuda.empty_cache()
 
     # 2B step at M = 4 and 16, grouped
     share = main_runner if (main_runner.wk.key == "decode_step_2b" and

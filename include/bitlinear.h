@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 5
+#define BITLINEAR_ABI_VERSION 6
 
 typedef enum {
   BITLINEAR_OK = 0,
@@ -306,9 +306,11 @@ bitlinear_status bitlinear_forward_noalloc(const void* X, bitlinear_dtype dtype,
  * required).  The output tiles (128 x 128) are spread over the compute
  * units one workgroup each; when they do not divide evenly, each tile of the
  * last, partial round is instead cut along K into pieces, one workgroup
- * each, whose exact int32 partial sums meet in `ws` (same bits either way).  `ws` (device, 16-byte aligned, at least
- * bitlinear_forward_q_workspace_bytes) enables that; NULL runs one workgroup
- * per tile.  Its first 4 KiB (counters) must be zero the first time a
+ * each, whose exact int32 partial sums meet in `ws` (same bits either way).
+ * `ws` (device, 16-byte aligned, at least bitlinear_forward_q_workspace_bytes)
+ * enables that; NULL runs one workgroup per tile.  Up to four tokens (K <=
+ * 12288) the one-launch decode kernel runs instead, with the rows copied
+ * rather than quantized, and `ws` is not used.  Its first 4 KiB (counters) must be zero the first time a
  * workspace is used, and every call leaves them zero again; the rest needs
  * no initial contents.  Calls that share a workspace must not overlap. */
 bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
@@ -316,6 +318,26 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                                      int64_t N, const uint8_t* packed, const float* gamma,
                                      float* Y, bitlinear_epilogue epi, void* ws,
                                      size_t ws_bytes, void* stream);
+
+/* The front half of the gated FFN (the technical-report card, Method
+ * Adaptation: squared ReLU as the FFN activation) with the down projection's input
+ * quantization fused in: from a fused gate+up matrix packed with
+ * bitlinear_quantize_weights_glu, h = max(gate, 0)^2 * up as the
+ * BITLINEAR_EPI_RELU2_GLU forward computes it, written to H [M][N/2]
+ * (float) and, in the same launch, quantized per token exactly as
+ * bitlinear_quantize_acts would quantize H: Hq [M][N/2] int8, h_scale [M],
+ * h_rowsum [M], ready for bitlinear_forward_q of the down projection.  The
+ * last workgroup to finish quantizes (no workgroup waits for another).
+ * 1 <= M <= 4, K % 256 == 0 and K <= 12288, N % 32 == 0.  `ws`: at least
+ * bitlinear_forward_glu_quant_workspace_bytes() bytes, 16-byte aligned,
+ * zero before its first use and left zero by every call (a counter); calls
+ * sharing it must not overlap.  Errors as bitlinear_forward. */
+size_t bitlinear_forward_glu_quant_workspace_bytes(void);
+bitlinear_status bitlinear_forward_glu_quant(const void* X, bitlinear_dtype dtype, int64_t M,
+                                             int64_t K, int64_t N, const uint8_t* packed,
+                                             const float* gamma, float* H, int8_t* Hq,
+                                             float* h_scale, int32_t* h_rowsum, void* ws,
+                                             size_t ws_bytes, void* stream);
 
 /* ---- Grouped decode forward ------------------------------------------------
  * Many independent BitLinear layers that share the token count M

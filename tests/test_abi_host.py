@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert L.bitlinear_abi_version() == 5
+    assert L.bitlinear_abi_version() == 6
     for s in range(8):
         assert L.bitlinear_status_string(s).decode()
     assert L.bitlinear_status_string(99).decode() == "unknown status"
@@ -149,6 +149,34 @@ def test_forward_q_validation(L):
     assert f(A, A, A, 4, 256, 16, A, A, A, 0, A, 1024, None) == ERR_WS
     assert f(A, A, A, 4, 256, 16, A, A, A, 0, U, 1 << 30, None) == ERR_ALIGN
     assert f(None, None, None, 0, 256, 16, None, None, None, 0, None, 0, None) == OK
+
+
+def test_forward_glu_quant_validation(L):
+    f = L.bitlinear_forward_glu_quant
+    n = L.bitlinear_forward_glu_quant_workspace_bytes()
+    assert n >= 4
+    #          X  dt M  K    N   packed g  H  Hq hs hr ws  bytes stream
+    assert f(A, 7, 1, 256, 32, A, A, A, A, A, A, A, n, None) == ERR_DTYPE
+    assert f(A, 0, 1, 256, 48, A, A, A, A, A, A, A, n, None) == ERR_SHAPE   # N % 32
+    assert f(A, 0, 5, 256, 32, A, A, A, A, A, A, A, n, None) == ERR_SHAPE   # M > 4
+    assert f(A, 0, 0, 256, 32, A, A, A, A, A, A, A, n, None) == ERR_SHAPE   # M < 1
+    assert f(A, 0, 1, 12544, 32, A, A, A, A, A, A, A, n, None) == ERR_SHAPE  # K > 12288
+    assert f(A, 0, 1, 256, 32, A, A, A, None, A, A, A, n, None) == ERR_NULL
+    assert f(A, 0, 1, 256, 32, A, A, A, A, U, A, A, n, None) == ERR_ALIGN
+    assert f(A, 0, 1, 256, 32, A, A, A, A, A, A, None, 0, None) == ERR_WS
+    assert f(A, 0, 1, 256, 32, A, A, A, A, A, A, A, n - 1, None) == ERR_WS
+    assert f(A, 0, 1, 256, 32, A, A, A, A, A, A, U, n, None) == ERR_ALIGN
+
+
+def test_forward_lut_validation(L):
+    f = L.bitlinear_forward_lut
+    #          X  dt K     N   packed g  Y  epi dbg stream
+    assert f(A, 7, 256, 16, A, A, A, 0, None, None) == ERR_DTYPE
+    assert f(A, 0, 256, 16, A, A, A, 9, None, None) == ERR_ARG
+    assert f(A, 0, 320, 16, A, A, A, 0, None, None) == ERR_SHAPE
+    assert f(A, 0, 8448, 16, A, A, A, 0, None, None) == ERR_SHAPE
+    assert f(None, 0, 256, 16, A, A, A, 0, None, None) == ERR_NULL
+    assert f(A, 0, 256, 16, U, A, A, 0, None, None) == ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

@@ -97,11 +97,16 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_int, _p, _sz, _p]
     L.bitlinear_forward_noalloc.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p,
                                             ctypes.c_int, ctypes.POINTER(Debug), _p]
+    L.bitlinear_forward_glu_quant_workspace_bytes.argtypes = []
+    L.bitlinear_forward_glu_quant_workspace_bytes.restype = _sz
+    L.bitlinear_forward_glu_quant.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p, _p,
+                                              _p, _p, _p, _sz, _p]
     L.bitlinear_forward_lut.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, ctypes.c_int,
                                         ctypes.POINTER(Debug), _p]
     for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
                  "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
                  "bitlinear_forward_q", "bitlinear_forward_noalloc", "bitlinear_forward_lut",
+                 "bitlinear_forward_glu_quant",
                  "bitlinear_quantize_weights_b3", "bitlinear_pack_ternary_b3",
                  "bitlinear_unpack_ternary_b3"):
         getattr(L, name).restype = ctypes.c_int
@@ -335,6 +340,33 @@ def forward_noalloc(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, 
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # BITLINEAR_NOALLOC_SCRATCH_BYTES
+
+
+def forward_glu_quant_workspace(device) -> torch.Tensor:
+    """The counter workspace of forward_glu_quant, zeroed (reusable)."""
+    n = lib().bitlinear_forward_glu_quant_workspace_bytes()
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def forward_glu_quant(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,
+                      workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None):
+    """Gated FFN front half (fused gate+up weights, M <= 4): returns
+    (H float [M][N/2], Hq int8 [M][N/2], h_scale [M], h_rowsum [M]), the last
+    three as quantize_acts(H) would give them, from one launch."""
+    M, K = X.shape
+    F = N // 2
+    if workspace is None:
+        workspace = forward_glu_quant_workspace(X.device)
+    H = out if out is not None else torch.empty((M, F), dtype=torch.float32, device=X.device)
+    Hq = torch.empty((M, F), dtype=torch.int8, device=X.device)
+    hs = torch.empty(max(M, 4), dtype=torch.float32, device=X.device)[:M]
+    hr = torch.empty(max(M, 4), dtype=torch.int32, device=X.device)[:M]
+    check(lib().bitlinear_forward_glu_quant(_ptr(X), _dtype_code(X), M, K, N, _ptr(packed),
+                                            _ptr(gamma), _ptr(H), _ptr(Hq), _ptr(hs), _ptr(hr),
+                                            _ptr(workspace), workspace.numel(), _stream()),
+          "bitlinear_forward_glu_quant")
+    return H, Hq, hs, hr
 
 
 def forward_lut(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,

@@ -14,6 +14,7 @@
 #include "../../include/bitlinear.h"
 #include "common.hpp"
 #include "group.hpp"
+#include "launch.hpp"
 
 namespace {
 
@@ -602,6 +603,7 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
   if (!aligned16(Xq) || !aligned16(x_scale) || !aligned16(x_rowsum) || !aligned16(packed) ||
       !aligned16(gamma) || !aligned16(Y))
     return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
   if (ws) {
     const size_t need = bl_gemm_workspace_bytes(M, K, N);
     if (ws_bytes < need)
@@ -609,10 +611,46 @@ bitlinear_status bitlinear_forward_q(const int8_t* Xq, const float* x_scale,
                   ws_bytes);
     if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
+  if (bl_gemv_supports(M, K))  // up to four tokens: the rows are copied, not re-quantized
+    return from_hip(bl_launch_gemv_q(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, (int)epi,
+                                     nullptr, s),
+                    "bitlinear_forward_q");
   return from_hip(bl_launch_gemm_q(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y,
-                                   (int)epi, nullptr, ws,
-                                   static_cast<hipStream_t>(stream)),
+                                   (int)epi, nullptr, ws, s),
                   "bitlinear_forward_q");
+}
+
+size_t bitlinear_forward_glu_quant_workspace_bytes(void) { return 256; }
+
+bitlinear_status bitlinear_forward_glu_quant(const void* X, bitlinear_dtype dtype, int64_t M,
+                                             int64_t K, int64_t N, const uint8_t* packed,
+                                             const float* gamma, float* H, int8_t* Hq,
+                                             float* h_scale, int32_t* h_rowsum, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
+    return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  bitlinear_status st = check_nk(N, K);
+  if (st != BITLINEAR_OK) return st;
+  if (N % 32 != 0)
+    return fail(BITLINEAR_ERR_SHAPE, "a fused gate+up matrix needs N %% 32 == 0, got %lld",
+                (long long)N);
+  if (M < 1 || !bl_gemv_supports(M, K))
+    return fail(BITLINEAR_ERR_SHAPE,
+                "M=%lld K=%lld: the quantized gated output needs 1 <= M <= 4 and K <= 12288",
+                (long long)M, (long long)K);
+  if (!X || !packed || !gamma || !H || !Hq || !h_scale || !h_rowsum)
+    return fail(BITLINEAR_ERR_NULL, "X, packed, gamma, H, Hq, h_scale and h_rowsum are required");
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(gamma) || !aligned16(H) ||
+      !aligned16(Hq) || !aligned16(h_scale) || !aligned16(h_rowsum))
+    return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!ws || ws_bytes < bitlinear_forward_glu_quant_workspace_bytes())
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                bitlinear_forward_glu_quant_workspace_bytes(), ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return from_hip(bl_launch_gemv_glu_quant(X, (int)dtype, M, K, N, packed, gamma, H, Hq, h_scale,
+                                           h_rowsum, static_cast<int*>(ws),
+                                           static_cast<hipStream_t>(stream)),
+                  "bitlinear_forward_glu_quant");
 }
 
 size_t bitlinear_group_workspace_bytes(const bitlinear_group_op* ops, int n_ops, int64_t M) {

@@ -6,6 +6,7 @@
 #include "common.hpp"
 #include "gemv_tile.hpp"
 #include "quant_row.hpp"
+#include "launch.hpp"
 
 namespace {
 

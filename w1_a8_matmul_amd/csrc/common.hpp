@@ -168,59 +168,3 @@ __device__ __forceinline__ uint32_t codes(uint32_t w, int f) {
 }
 
 }  // namespace bl
-
-// Host-side launchers (defined in the .hip files).  All return hipError_t of
-// the launch; shapes were validated by the ABI layer.
-hipError_t bl_launch_absmean_rows(const float* W, int64_t N, int64_t K, double* row_sum,
-                                  hipStream_t s);
-hipError_t bl_launch_absmean_final(const double* row_sum, int64_t N, int64_t K,
-                                   float* gamma, hipStream_t s);
-hipError_t bl_launch_quant_pack(const float* W, int64_t N, int64_t K, const float* gamma,
-                                uint8_t* packed, hipStream_t s,
-                                bool glu = false);
-hipError_t bl_launch_pack(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packed,
-                          hipStream_t s);
-// The base-3 layout: K padded to a multiple of 320 (bl_b3_padded_k).
-inline int64_t bl_b3_padded_k(int64_t K) { return (K + bl::kB3TileCols - 1) / bl::kB3TileCols * bl::kB3TileCols; }
-hipError_t bl_launch_quant_pack_b3(const float* W, int64_t N, int64_t K, const float* gamma,
-                                   uint8_t* packed, hipStream_t s, bool glu);
-hipError_t bl_launch_pack_b3(const int8_t* Wq, int64_t N, int64_t K, uint8_t* packed,
-                             hipStream_t s);
-hipError_t bl_launch_unpack_b3(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
-                               hipStream_t s);
-hipError_t bl_launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int8_t* Wq,
-                            hipStream_t s);
-// Per-token activation quantization; also zeroes n_zero ints at `zero`
-// (may be null) for the launch that follows.  norm_gain (float [K], 16-byte
-// aligned) selects subln first (RMSNorm with that gain and norm_eps).
-hipError_t bl_launch_quant_acts(const void* X, int dtype, int64_t M, int64_t K, int8_t* Xq,
-                                float* x_scale, int32_t* x_rowsum, int* zero, int n_zero,
-                                hipStream_t s, const float* norm_gain = nullptr,
-                                float norm_eps = 0.0f);
-// Small-M fused forward (activation quantization inside the kernel).
-bool bl_gemv_supports(int64_t M, int64_t K);
-hipError_t bl_launch_gemv(const void* X, int dtype, int64_t M, int64_t K, int64_t N,
-                          const uint8_t* packed, const float* gamma, float* Y, int epi,
-                          int8_t* xq_out, float* xscale_out, int32_t* acc_out,
-                          hipStream_t s, const float* norm_gain = nullptr,
-                          float norm_eps = 0.0f);
-// Lookup-table GEMV for one token (K % 256 == 0, K <= kLutMaxK): int16
-// tables of column-pair sums in LDS indexed by 4-bit fields of the packed
-// codes; same outputs as bl_launch_gemv at M = 1.
-constexpr int64_t kLutMaxK = 8192;
-size_t bl_lut_lds_bytes(int64_t K);
-size_t bl_lut_max_lds_bytes();
-hipError_t bl_launch_lut_gemv(const void* X, int dtype, int64_t K, int64_t N,
-                              const uint8_t* packed, const float* gamma, float* Y, int epi,
-                              int8_t* xq_out, float* xscale_out, int32_t* acc_out,
-                              hipStream_t s);
-// Forward from quantized activations on the int8 MFMA units.  gemm_ws
-// (bl_gemm_workspace_bytes, its first bl_gemm_counter_bytes zero on entry
-// and left zero) lets the last, partial round of tiles be shared along K;
-// null runs one workgroup per tile.
-size_t bl_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
-size_t bl_gemm_counter_bytes();
-hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_t* x_rowsum,
-                            int64_t M, int64_t K, int64_t N, const uint8_t* packed,
-                            const float* gamma, float* Y, int epi, int32_t* acc_out,
-                            void* gemm_ws, hipStream_t s);

@@ -32,6 +32,7 @@
 
 #include "common.hpp"
 #include "group.hpp"
+#include "launch.hpp"
 
 namespace {
 

@@ -24,6 +24,7 @@
 #include "gemv_tile.hpp"
 #include "group.hpp"
 #include "quant_row.hpp"
+#include "launch.hpp"
 
 namespace {
 

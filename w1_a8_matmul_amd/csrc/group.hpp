@@ -53,41 +53,5 @@ constexpr int kGroupMaxK = 12288;
 constexpr int kGroupMaxM = 16;
 constexpr int kGroupInlineQuantMaxM = 3;
 
-// Whether the group needs the quantization launch and workspace.
-bool bl_group_prequantizes(int M);
-
 // LDS available to one workgroup.
 constexpr size_t kGroupMaxLds = 160 * 1024;
-
-// Dynamic LDS bytes of the grouped kernel for M tokens and largest K.
-size_t bl_group_lds_bytes(int M, int max_k);
-
-// Chooses the workgroup size (256 or 512 threads) and reports how many
-// workgroups fit on one compute unit; also allows the kernel the dynamic
-// LDS it needs.  norm: some layer has a subln gain.
-hipError_t bl_group_plan(int M, int max_k, bool norm, bool b3, int* threads, int* per_cu);
-
-// Grouped forward (b3: every layer's weights in the base-3 layout, and max_k
-// the largest padded K): G workgroups of `threads` threads; workgroup g first runs
-// tiles wg_begin[g] .. wg_begin[g+1]-1, then takes the n_units units from the
-// queue (two ints, zero on entry and left zero); max_k the largest K.  xq,
-// sx, rs: the quantized activations, scales and row sums (used when
-// bl_group_prequantizes(M)); norm as for bl_group_plan.
-hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_begin,
-                           const GroupUnit* units, int n_units, int* queue, int G, int max_k,
-                           int threads, bool norm, bool b3, int8_t* xq, float* sx, int* rs,
-                           hipStream_t s);
-
-// Above kGroupMaxM tokens a group runs as one persistent tiled int8 GEMM over
-// the output tiles of all its layers (activations quantized beforehand).
-// Output tiles of one layer at M tokens; workgroups per compute unit.
-int bl_group_gemm_tiles(int M, int N);
-int bl_group_gemm_blocks_per_cu(int M);
-// n_items: output tiles over all layers; G workgroups take them strided.
-hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
-                                const int8_t* xq, const float* sx, const int* rs, bool glu,
-                                hipStream_t s);
-// The quantization launch of the grouped forward (one workgroup per layer
-// and token) into xq / sx / rs at each layer's xq_off; max_k the largest K.
-hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int max_k, int8_t* xq,
-                                 float* sx, int* rs, hipStream_t s);

@@ -18,6 +18,7 @@
 // pair (b + 8, b + 12).
 #include "common.hpp"
 #include "gemv_tile.hpp"
+#include "launch.hpp"
 
 #include <atomic>
 

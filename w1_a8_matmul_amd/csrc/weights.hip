@@ -4,6 +4,7 @@
 // Absmean to {-1, 0, +1} and four ternary weights per byte follow the
 // "BitNet b1.58 2B4T Technical Report" card, section "Method Adaptation".
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace {
 
