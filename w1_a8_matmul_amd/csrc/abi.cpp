@@ -106,8 +106,9 @@ struct GroupLayout {
 template <typename F>
 void group_split(const bitlinear_group_op* ops, int n_ops, int64_t M, int64_t* split,
                  int64_t* n_units, F f) {
-  const int64_t pct = bl_group_prequantizes((int)M) ? kGroupStaticPercentPreq
-                                                    : kGroupStaticPercentInline;
+  const int64_t pct = !bl_group_prequantizes((int)M) ? kGroupStaticPercentInline
+                      : M >= kGroupPreqWideM            ? kGroupStaticPercentPreqWide
+                                                        : kGroupStaticPercentPreq;
   int64_t total = 0;
   for (int i = 0; i < n_ops; ++i) total += (ops[i].N / 16) * op_kblocks(ops[i]);
   int64_t cost = 0, item = 0, s = -1, n = 0;

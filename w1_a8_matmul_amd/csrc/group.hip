@@ -312,19 +312,28 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   __syncthreads();
   const int rows = (last - first) * kTileRows;
   const int64_t n0 = (int64_t)(first - o.item_begin) * kTileRows;
+  // Four consecutive outputs per thread and store (16 bytes): at 16 tokens
+  // this took the 2B step from 139-140 to 133-136 us against one float per
+  // store.
   if (o.epi == kEpiGlu) {
     // interleaved gate+up tiles: rows 0..7 gates, 8..15 their up rows;
     // output row r of the segment is gate row r (tile r/8) of N/2
-    const int half = rows / 2;
-    for (int i = threadIdx.x; i < M * half; i += kThreads) {
-      const int m = i / half, r = i - m * half;
+    const int q4 = rows / 8;
+    for (int i = threadIdx.x; i < M * q4; i += kThreads) {
+      const int m = i / q4, r = (i - m * q4) * 4;
       const float* ty = s_y + m * kSegTiles * kTileRows + (r / 8) * kTileRows + (r % 8);
-      o.Y[m * (int64_t)(o.N / 2) + n0 / 2 + r] = glu_relu2(ty[0], ty[8]);
+      const float4 g = *reinterpret_cast<const float4*>(ty);
+      const float4 u = *reinterpret_cast<const float4*>(ty + 8);
+      *reinterpret_cast<float4*>(o.Y + m * (int64_t)(o.N / 2) + n0 / 2 + r) =
+          make_float4(glu_relu2(g.x, u.x), glu_relu2(g.y, u.y), glu_relu2(g.z, u.z),
+                      glu_relu2(g.w, u.w));
     }
   } else {
-    for (int i = threadIdx.x; i < M * rows; i += kThreads) {
-      const int m = i / rows, r = i - m * rows;
-      o.Y[m * (int64_t)o.N + n0 + r] = s_y[m * kSegTiles * kTileRows + r];
+    const int q4 = rows / 4;
+    for (int i = threadIdx.x; i < M * q4; i += kThreads) {
+      const int m = i / q4, r = (i - m * q4) * 4;
+      *reinterpret_cast<float4*>(o.Y + m * (int64_t)o.N + n0 + r) =
+          *reinterpret_cast<const float4*>(s_y + m * kSegTiles * kTileRows + r);
     }
   }
 }
@@ -601,7 +610,9 @@ hipError_t bl_group_plan(int M, int max_k, bool norm, bool b3, int* threads, int
   }
   // Four-wave workgroups while at least two fit on a compute unit (more,
   // shorter weight streams); eight-wave ones when the activations take so
-  // much LDS that only one does.
+  // much LDS that only one does.  (Sixteen waves on pre-quantized rows, four
+  // per SIMD instead of two, measured no faster at 16 tokens: 138.7 against
+  // 140.4 us, within the spread of runs.)
   const int b256 = blocks_per_cu(256, M, norm, b3, lds, max_k);
   if (b256 >= 2) {
     *threads = 256;

@@ -26,20 +26,8 @@ static_assert(sizeof(GroupOp) == 80, "GroupOp must stay 80 bytes");
 struct GroupUnit {
   int32_t first, end, op, pad;
 };
-// A unit holds about kGroupUnitBlocks 1 KiB weight blocks (16 rows x 256
-// columns each), at most one segment: 32 tiles at K = 2560, 12 at K = 6912,
-// 20 at K = 4096.  Measured on MI355X over 80..640: smaller units cost more
-// set-ups (a new layer's quantization, a pipeline restart), larger ones a
-// longer tail (2B step at M = 1: 93 us at 320, 98 at 160, 100 at 80).
-constexpr int kGroupUnitBlocks = 320;
 // Tiles whose outputs a workgroup holds in LDS at once (one segment).
 constexpr int kGroupSegTiles = 32;
-// Share of the work (by bytes) in the static ranges, in percent, when the
-// workgroups quantize activations themselves (a new layer costs a
-// quantization) and when they copy pre-quantized rows (a new layer costs a
-// copy of M rows); measured on MI355X over 2B and 7B decode steps.
-constexpr int kGroupStaticPercentInline = 75;
-constexpr int kGroupStaticPercentPreq = 95;
 
 // Largest K of a grouped layer and largest token count.  Up to
 // kGroupInlineQuantMaxM tokens each workgroup quantizes the activations of

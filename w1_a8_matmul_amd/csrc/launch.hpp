@@ -80,7 +80,27 @@ hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_
                             const float* gamma, float* Y, int epi, int32_t* acc_out,
                             void* gemm_ws, hipStream_t s);
 
-// Grouped forward.
+// Grouped forward: the host's split of the work (constants the kernel does
+// not see).
+// A unit holds about kGroupUnitBlocks 1 KiB weight blocks (16 rows x 256
+// columns each), at most one segment: 32 tiles at K = 2560, 12 at K = 6912,
+// 20 at K = 4096.  Measured on MI355X over 80..640: smaller units cost more
+// set-ups (a new layer's quantization, a pipeline restart), larger ones a
+// longer tail (2B step at M = 1: 93 us at 320, 98 at 160, 100 at 80).
+constexpr int kGroupUnitBlocks = 320;
+// Share of the work (by bytes) in the static ranges, in percent, when the
+// workgroups quantize activations themselves (a new layer costs a
+// quantization) and when they copy pre-quantized rows (a new layer costs a
+// copy of M rows); measured on MI355X over 2B and 7B decode steps.  From
+// kGroupPreqWideM tokens on, the copies and output stores of a unit are long
+// enough that a larger shared part balances better: 2B step at 8 tokens,
+// 116.8-117.4 us at 85% against 121.8-123.4 at 95% (two runs each on one
+// box; at 4 and 16 tokens the two were within the spread of runs).
+constexpr int kGroupStaticPercentInline = 75;
+constexpr int kGroupStaticPercentPreq = 95;
+constexpr int kGroupStaticPercentPreqWide = 85;
+constexpr int kGroupPreqWideM = 8;
+
 // Whether the group needs the quantization launch and workspace.
 bool bl_group_prequantizes(int M);
 
