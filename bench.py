@@ -578,9 +578,10 @@ def context_probes(torch):
 def ffn_record(torch, bl, wl, dev, launches):
     """The 2B model's gated FFN for one token (layer 0's gate+up and down
     weights of the 2B step): gate+up 2560 -> 13824 (fused,
-    gated ReLU^2) then down 6912 -> 2560, two ways -- two plain forwards (the
-    down launch quantizes h itself), and forward_glu_quant (h quantized by the
-    gate+up launch's last workgroup) then forward_q from the codes.  Weight
+    gated ReLU^2) then down 6912 -> 2560, three ways -- two plain forwards (the
+    down launch quantizes h itself); forward_glu_quant (h quantized by the
+    gate+up launch's last workgroup) then forward_q from the codes; and
+    ffn_chain (both projections in one launch).  Weight
     sets rotate past the Infinity Cache; graph-timed, HIP events."""
     K, N, Kd, Nd = 2560, 13824, 6912, 2560
     copies = weight_copies(N * K // 4 + Nd * Kd // 4)
@@ -595,6 +596,7 @@ def ffn_record(torch, bl, wl, dev, launches):
     H = torch.empty((1, N // 2), dtype=torch.float32, device=dev)
     Y = torch.empty((1, Nd), dtype=torch.float32, device=dev)
     ws = bl.forward_glu_quant_workspace(dev)
+    wc = bl.ffn_chain_workspace(N, dev)
 
     def plain(i):
         c = i % copies
@@ -606,9 +608,16 @@ def ffn_record(torch, bl, wl, dev, launches):
         _, hq, hs, hr = bl.forward_glu_quant(X, gu[c][0], gu[c][1], N, workspace=ws, out=H)
         bl.forward_q(hq, hs, hr, dn[c][0], dn[c][1], Nd, out=Y, split_remainder=False)
 
+    def chain(i):
+        c = i % copies
+        bl.ffn_chain(X, gu[c][0], gu[c][1], N, dn[c][0], dn[c][1], Nd, glu=True, workspace=wc,
+                     H=H, out=Y)
+
     t_plain = time_graph(torch, plain, max(launches, copies))
     t_fused = time_graph(torch, fused, max(launches, copies))
+    t_chain = time_graph(torch, chain, max(launches, copies))
     return {"us_two_forwards": round(t_plain, 3), "us_glu_quant_then_forward_q": round(t_fused, 3),
+            "us_one_launch_chain": round(t_chain, 3),
             "weight_copies_rotated": copies, "tokens": 1,
             "note": "gate+up 2560->13824 with the gated ReLU^2, down 6912->2560"}
 
@@ -643,6 +652,24 @@ def sub_records(args, torch, bl, wl, dev, main_runner):
     rec["roofline"] = roofline_single(args, torch, bl, r, "hbm")
     rec["launches_per_step"] = 2
     subs["decode_gemv_pair_m1"] = rec
+    del r
+
+    # the same pair in one launch (bitlinear_ffn_chain)
+    r = Runner(bl, torch, wl, dev, "decode_gemv_pair_m1", 1, grouped=False, copies=61)
+    up, down = r.lins
+    wc = bl.ffn_chain_workspace(up.N, dev)
+
+    def chain_step(i):
+        c = i % r.copies
+        bl.ffn_chain(up.X, up.packed[c], up.gamma[c], up.N, down.packed[c], down.gamma[c],
+                     down.N, workspace=wc, H=up.Y, out=down.Y)
+
+    us = time_graph(torch, chain_step, max(steps, 61))
+    subs["decode_gemv_pair_m1_chain"] = {"us_per_step": round(us, 3),
+                                         "value": round(r.bytes_step() / (us * 1e-6) / 1e9, 3),
+                                         "unit": "GB/s", "launches_per_step": 1,
+                                         "weight_copies_rotated": r.copies}
+    log(f"decode pair in one launch: {us:.3f} us")
     del r
 
     # the same pair by table lookup (bitlinear_forward_lut)

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define BITLINEAR_ABI_VERSION 6
+#define BITLINEAR_ABI_VERSION 7
 
 typedef enum {
   BITLINEAR_OK = 0,
@@ -250,6 +250,31 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
                                    const float* gamma, float* Y, bitlinear_epilogue epi,
                                    const bitlinear_debug* dbg, void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* The decode FFN ("BitNet b1.58 2B4T Technical Report" card, Method
+ * Adaptation: squared ReLU as the FFN activation) in one persistent launch:
+ * h = relu(X W_up^T)^2 -- or, with epi_up BITLINEAR_EPI_RELU2_GLU and W_up a
+ * fused gate+up matrix from bitlinear_quantize_weights_glu, the gated
+ * max(gate, 0)^2 * up -- written to H [M][F] (F = N_up, or N_up / 2 gated),
+ * then Y [M][N_down] = the BitLinear forward of h with W_down [N_down][F].
+ * H and Y are the same bits as two bitlinear_forward calls.  The up tiles'
+ * workgroups come first in the grid; a down tile's workgroup waits until
+ * every up tile is done (a bounded wait: workgroups start in index order, so
+ * the up tiles are running).  1 <= M <= 4; K % 256 == 0 and F %
+ * 256 == 0, both <= 12288; dtype as bitlinear_forward.  `ws`: at least
+ * bitlinear_ffn_chain_workspace_bytes(N_up) bytes (0 for a bad N_up),
+ * 16-byte aligned, zero before its first use; it holds a counter, a
+ * generation count and one flag per up tile, which every call leaves ready
+ * for the next (its third int is set to 1 and stays set if a wait ever gave
+ * up, which only a failing device can cause).  Calls sharing it must not
+ * overlap.  Errors as bitlinear_forward. */
+size_t bitlinear_ffn_chain_workspace_bytes(int64_t N_up);
+bitlinear_status bitlinear_ffn_chain(const void* X, bitlinear_dtype dtype, int64_t M, int64_t K,
+                                     int64_t N_up, const uint8_t* packed_up,
+                                     const float* gamma_up, bitlinear_epilogue epi_up,
+                                     int64_t N_down, const uint8_t* packed_down,
+                                     const float* gamma_down, float* H, float* Y, void* ws,
+                                     size_t ws_bytes, void* stream);
 
 /* The forward of one token (M = 1) by table lookup instead of multiplies,
  * the method bitnet.cpp's ternary kernels take from T-MAC (dignews.cc

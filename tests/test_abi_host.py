@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_strings(L):
-    assert L.bitlinear_abi_version() == 6
+    assert L.bitlinear_abi_version() == 7
     for s in range(8):
         assert L.bitlinear_status_string(s).decode()
     assert L.bitlinear_status_string(99).decode() == "unknown status"
@@ -166,6 +166,24 @@ def test_forward_glu_quant_validation(L):
     assert f(A, 0, 1, 256, 32, A, A, A, A, A, A, None, 0, None) == ERR_WS
     assert f(A, 0, 1, 256, 32, A, A, A, A, A, A, A, n - 1, None) == ERR_WS
     assert f(A, 0, 1, 256, 32, A, A, A, A, A, A, U, n, None) == ERR_ALIGN
+
+
+def test_ffn_chain_validation(L):
+    f = L.bitlinear_ffn_chain
+    n = L.bitlinear_ffn_chain_workspace_bytes(256)
+    assert n >= 16 + 4 * 16
+    assert L.bitlinear_ffn_chain_workspace_bytes(24) == 0
+    #        X  dt M  K     Nup  pu g  epi Nd  pd gd H  Y  ws bytes stream
+    assert f(A, 7, 1, 256, 256, A, A, 1, 16, A, A, A, A, A, n, None) == ERR_DTYPE
+    assert f(A, 0, 1, 256, 256, A, A, 0, 16, A, A, A, A, A, n, None) == ERR_ARG   # no ReLU^2
+    assert f(A, 0, 5, 256, 256, A, A, 1, 16, A, A, A, A, A, n, None) == ERR_SHAPE
+    assert f(A, 0, 1, 256, 272, A, A, 1, 16, A, A, A, A, A, n, None) == ERR_SHAPE  # F % 256
+    assert f(A, 0, 1, 256, 528, A, A, 2, 16, A, A, A, A, A, n, None) == ERR_SHAPE  # glu N % 32
+    assert f(A, 0, 1, 12544, 256, A, A, 1, 16, A, A, A, A, A, n, None) == ERR_SHAPE
+    assert f(A, 0, 1, 256, 256, A, A, 1, 16, A, None, A, A, A, n, None) == ERR_NULL
+    assert f(A, 0, 1, 256, 256, A, A, 1, 16, A, A, U, A, A, n, None) == ERR_ALIGN
+    assert f(A, 0, 1, 256, 256, A, A, 1, 16, A, A, A, A, None, 0, None) == ERR_WS
+    assert f(A, 0, 1, 256, 256, A, A, 1, 16, A, A, A, A, U, n, None) == ERR_ALIGN
 
 
 def test_forward_lut_validation(L):

@@ -4,7 +4,7 @@
   gate+up 2560->13824, down 6912->2560) = 120 linears, 2.08 G weights, as
   one grouped forward at M = 1, 4 and 16 (the persistent kernel with its
   static ranges and shared queue, in the launch configuration the bench
-  times).
+  times), and at M = 1 with every linear in the base-3 layout.
 - The whole 7B-like step: 32 layers x (QKV 4096->12288, O 4096->4096,
   gate+up 4096->22016, down 11008->4096) = 128 linears, 6.5 G weights with
   30% near-zero entries, Student-t(3) activations, at M = 1 (skinny kernel)
@@ -91,16 +91,21 @@ class Step:
             self.linears.append((layer, li, shape, packed, gamma, q, gc))
         torch.cuda.synchronize()
 
-    def check_grouped(self, dev, bl, orc, M):
+    def check_grouped(self, dev, bl, orc, M, fmt=None):
         layers, refs = [], []
         for layer, li, shape, packed, gamma, q, gc in self.linears:
             X, is_bf16 = wl.gen_acts(wl.act_seed(self.key, layer, li) + 100 * M, M, shape.K,
                                      self.wk.x_kind)
             assert is_bf16
             Xt = torch.from_numpy(X).to(dev).view(torch.bfloat16)
+            if fmt == "b3":
+                # the same codes in the base-3 layout, packed on the GPU and
+                # checked byte for byte against the oracle's packing
+                packed = bl.pack_ternary_b3(torch.from_numpy(q).to(dev))
+                assert np.array_equal(packed.cpu().numpy(), orc.pack_b3(q)), (layer, li)
             layers.append((Xt, packed, gamma, shape.N, None, None))
             refs.append((X, q, gc))
-        g = bl.Group(layers)
+        g = bl.Group(layers, fmt=fmt)
         first = [y.clone() for y in g.forward()]
         torch.cuda.synchronize()
         worst = 0.0
@@ -129,6 +134,13 @@ def step_2b(dev, bl, orc):
 def test_decode_step_2b_grouped_full(dev, bl, orc, step_2b, M):
     assert len(step_2b.linears) == 120
     step_2b.check_grouped(dev, bl, orc, M)
+
+
+@pytest.mark.timeout(900)
+def test_decode_step_2b_grouped_full_b3(dev, bl, orc, step_2b):
+    # the whole 2B step with every linear in the base-3 layout (418.8 MB)
+    step_2b.check_grouped(dev, bl, orc, 1, fmt="b3")
+    torch.cuda.empty_cache()
 
 
 @pytest.fixture(scope="module")

@@ -101,12 +101,16 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward_glu_quant_workspace_bytes.restype = _sz
     L.bitlinear_forward_glu_quant.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p, _p,
                                               _p, _p, _p, _sz, _p]
+    L.bitlinear_ffn_chain_workspace_bytes.argtypes = [_i64]
+    L.bitlinear_ffn_chain_workspace_bytes.restype = _sz
+    L.bitlinear_ffn_chain.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, ctypes.c_int,
+                                      _i64, _p, _p, _p, _p, _p, _sz, _p]
     L.bitlinear_forward_lut.argtypes = [_p, ctypes.c_int, _i64, _i64, _p, _p, _p, ctypes.c_int,
                                         ctypes.POINTER(Debug), _p]
     for name in ("bitlinear_quantize_weights", "bitlinear_pack_ternary",
                  "bitlinear_unpack_ternary", "bitlinear_quantize_acts", "bitlinear_forward",
                  "bitlinear_forward_q", "bitlinear_forward_noalloc", "bitlinear_forward_lut",
-                 "bitlinear_forward_glu_quant",
+                 "bitlinear_forward_glu_quant", "bitlinear_ffn_chain",
                  "bitlinear_quantize_weights_b3", "bitlinear_pack_ternary_b3",
                  "bitlinear_unpack_ternary_b3"):
         getattr(L, name).restype = ctypes.c_int
@@ -367,6 +371,37 @@ def forward_glu_quant(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor
                                             _ptr(workspace), workspace.numel(), _stream()),
           "bitlinear_forward_glu_quant")
     return H, Hq, hs, hr
+
+
+def ffn_chain_workspace(N_up: int, device) -> torch.Tensor:
+    """The workspace of ffn_chain for an up projection of N_up rows, zeroed
+    (reusable; its third int is the error flag)."""
+    n = lib().bitlinear_ffn_chain_workspace_bytes(N_up)
+    if n == 0:
+        raise BitLinearError(f"bad N_up={N_up}")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def ffn_chain(X: torch.Tensor, packed_up: torch.Tensor, gamma_up: torch.Tensor, N_up: int,
+              packed_down: torch.Tensor, gamma_down: torch.Tensor, N_down: int,
+              glu: bool = False, workspace: Optional[torch.Tensor] = None,
+              H: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """The decode FFN (M <= 4) in one launch: returns (H, Y), h = the squared
+    ReLU (gated when ``glu``) of the up projection and Y its down projection."""
+    M, K = X.shape
+    F = N_up // 2 if glu else N_up
+    if workspace is None:
+        workspace = ffn_chain_workspace(N_up, X.device)
+    if H is None:
+        H = torch.empty((M, F), dtype=torch.float32, device=X.device)
+    if out is None:
+        out = torch.empty((M, N_down), dtype=torch.float32, device=X.device)
+    check(lib().bitlinear_ffn_chain(_ptr(X), _dtype_code(X), M, K, N_up, _ptr(packed_up),
+                                    _ptr(gamma_up), EPI["relu2_glu" if glu else "relu2"],
+                                    N_down, _ptr(packed_down), _ptr(gamma_down), _ptr(H),
+                                    _ptr(out), _ptr(workspace), workspace.numel(), _stream()),
+          "bitlinear_ffn_chain")
+    return H, out
 
 
 def forward_lut(X: torch.Tensor, packed: torch.Tensor, gamma: torch.Tensor, N: int,

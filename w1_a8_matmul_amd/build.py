@@ -21,7 +21,7 @@ PROBES_LIBRARY = os.path.join(PKG, "libbitlinear_probes.so")
 PROBES_SOURCES = ["probes.hip"]
 
 SOURCES = ["abi.cpp", "weights.hip", "acts.hip", "gemv.hip", "gemm.hip", "group.hip",
-           "lut.hip"]
+           "lut.hip", "chain.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -560,6 +560,50 @@ bitlinear_status bitlinear_forward_lut(const void* X, bitlinear_dtype dtype, int
                   "bitlinear_forward_lut");
 }
 
+size_t bitlinear_ffn_chain_workspace_bytes(int64_t N_up) {
+  if (N_up < 16 || N_up % 16 != 0 || N_up > kMaxN) return 0;
+  return align256(bl_chain_workspace_bytes(N_up));
+}
+
+bitlinear_status bitlinear_ffn_chain(const void* X, bitlinear_dtype dtype, int64_t M, int64_t K,
+                                     int64_t N_up, const uint8_t* packed_up,
+                                     const float* gamma_up, bitlinear_epilogue epi_up,
+                                     int64_t N_down, const uint8_t* packed_down,
+                                     const float* gamma_down, float* H, float* Y, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (dtype != BITLINEAR_F32 && dtype != BITLINEAR_BF16)
+    return fail(BITLINEAR_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (epi_up != BITLINEAR_EPI_RELU2 && epi_up != BITLINEAR_EPI_RELU2_GLU)
+    return fail(BITLINEAR_ERR_ARG, "epi_up must be BITLINEAR_EPI_RELU2 or _RELU2_GLU, got %d",
+                (int)epi_up);
+  const bool glu = epi_up == BITLINEAR_EPI_RELU2_GLU;
+  bitlinear_status st = check_nk(N_up, K);
+  if (st != BITLINEAR_OK) return st;
+  if (glu && N_up % 32 != 0)
+    return fail(BITLINEAR_ERR_SHAPE, "a fused gate+up matrix needs N %% 32 == 0, got %lld",
+                (long long)N_up);
+  const int64_t F = glu ? N_up / 2 : N_up;
+  st = check_nk(N_down, F);
+  if (st != BITLINEAR_OK) return st;
+  if (M < 1 || M > 4 || K > 12288 || F > 12288)
+    return fail(BITLINEAR_ERR_SHAPE,
+                "M=%lld K=%lld F=%lld: the chained FFN needs 1 <= M <= 4 and K, F <= 12288",
+                (long long)M, (long long)K, (long long)F);
+  if (!X || !packed_up || !gamma_up || !packed_down || !gamma_down || !H || !Y)
+    return fail(BITLINEAR_ERR_NULL, "X, both weights and gammas, H and Y are required");
+  if (!aligned16(X) || !aligned16(packed_up) || !aligned16(gamma_up) ||
+      !aligned16(packed_down) || !aligned16(gamma_down) || !aligned16(H) || !aligned16(Y))
+    return fail(BITLINEAR_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+  if (!ws || ws_bytes < bitlinear_ffn_chain_workspace_bytes(N_up))
+    return fail(BITLINEAR_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                bitlinear_ffn_chain_workspace_bytes(N_up), ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(BITLINEAR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return from_hip(bl_launch_ffn_chain(X, (int)dtype, M, K, N_up, packed_up, gamma_up, glu, H,
+                                      N_down, packed_down, gamma_down, Y, ws,
+                                      static_cast<hipStream_t>(stream)),
+                  "bitlinear_ffn_chain");
+}
+
 bitlinear_status bitlinear_forward_noalloc(const void* X, bitlinear_dtype dtype, int64_t M,
                                            int64_t K, int64_t N, const uint8_t* packed,
                                            const float* gamma, float* Y,

@@ -80,6 +80,18 @@ hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_
                             const float* gamma, float* Y, int epi, int32_t* acc_out,
                             void* gemm_ws, hipStream_t s);
 
+// The decode FFN (M <= 4) in one persistent launch: up projection with the
+// squared ReLU (glu: the gated one of a fused gate+up matrix), h [M][F]
+// (F = n_up, or n_up / 2 with glu), down projection [n_down][F] into Y.  ws
+// holds bl_chain_workspace_bytes(n_up) bytes (counters and one flag per up
+// tile), zero before its first use; its third int is an error flag, set if a
+// wait gave up.  K and F are multiples of 256 up to 12288.
+size_t bl_chain_workspace_bytes(int64_t n_up);
+hipError_t bl_launch_ffn_chain(const void* X, int dtype, int64_t M, int64_t K, int64_t n_up,
+                               const uint8_t* packed_up, const float* gamma_up, bool glu,
+                               float* H, int64_t n_down, const uint8_t* packed_down,
+                               const float* gamma_down, float* Y, void* ws, hipStream_t s);
+
 // Grouped forward: the host's split of the work (constants the kernel does
 // not see).
 // A unit holds about kGroupUnitBlocks 1 KiB weight blocks (16 rows x 256
