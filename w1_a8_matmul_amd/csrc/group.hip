@@ -6,7 +6,9 @@
 // layer, the workgroup quantizes that layer's activation rows per token
 // (absmax, int8) into LDS itself -- a few kilobytes read from L2, cheaper
 // than a separate quantization launch -- while its waves' first weight
-// loads are already in flight.  Its waves then stream their tiles' packed
+// loads are already in flight (above kGroupInlineQuantMaxM tokens a
+// quantization launch does this once per layer and token, and workgroups
+// copy the int8 rows instead).  Its waves then stream their tiles' packed
 // weights in chunks of 16-byte lane loads (one 1 KiB block per wave load,
 // chunks through two register buffers), unpack the 2-bit codes in registers
 // and contract them on the int8 matrix cores (v_mfma_i32_16x16x64_i8, the
@@ -19,7 +21,8 @@
 // The per-layer arithmetic is that of the single-layer forward: absmean
 // ternary weights and per-token absmax int8 activations ("BitNet b1.58 2B4T
 // Technical Report" card, section "Method Adaptation"), exact int32 sums,
-// ((float)acc * s_x) * gamma.
+// ((float)acc * s_x) * gamma.  The same loop also runs on weights in the
+// base-3 layout (five codes per byte, B3 instantiations).
 #include "common.hpp"
 #include "gemv_tile.hpp"
 #include "group.hpp"
