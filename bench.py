@@ -40,6 +40,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -477,10 +478,16 @@ def traffic_from_profile(kernel_src_hash, kernel_key):
 
 
 def source_hash(names):
+    """Hash of a kernel's sources with comments and blank space removed, so
+    that a counter record stays valid across edits that leave the code as
+    it was."""
     h = hashlib.sha1()
     for n in names:
-        with open(os.path.join(ROOT, "w1_a8_matmul_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "w1_a8_matmul_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
