@@ -251,45 +251,6 @@ bitlinear_status bitlinear_forward(const void* X, bitlinear_dtype dtype, int64_t
                                    const bitlinear_debug* dbg, void* ws, size_t ws_bytes,
                                    void* stream);
 
-/* The decode FFN ("BitNet b1.58 2B4T Technical Report" card, Method
- * Adaptation: squared ReLU as the FFN activation) in one persistent launch:
- * h = relu(X W_up^T)^2 -- or, with epi_up BITLINEAR_EPI_RELU2_GLU and W_up a
- * fused gate+up matrix from bitlinear_quantize_weights_glu, the gated
- * max(gate, 0)^2 * up -- written to H [M][F] (F = N_up, or N_up / 2 gated),
- * then Y [M][N_down] = the BitLinear forward of h with W_down [N_down][F].
- * H and Y are the same bits as two bitlinear_forward calls.  The up tiles'
- * workgroups come first in the grid; a down tile's workgroup waits until
- * every up tile is done (a bounded wait: workgroups start in index order, so
- * the up tiles are running).  1 <= M <= 4; K % 256 == 0 and F %
- * 256 == 0, both <= 12288; dtype as bitlinear_forward.  `ws`: at least
- * bitlinear_ffn_chain_workspace_bytes(N_up) bytes (0 for a bad N_up),
- * 16-byte aligned, zero before its first use; it holds a counter, a
- * generation count and one flag per up tile, which every call leaves ready
- * for the next (its third int is set to 1 and stays set if a wait ever gave
- * up, which only a failing device can cause).  Calls sharing it must not
- * overlap.  Errors as bitlinear_forward. */
-size_t bitlinear_ffn_chain_workspace_bytes(int64_t N_up);
-bitlinear_status bitlinear_ffn_chain(const void* X, bitlinear_dtype dtype, int64_t M, int64_t K,
-                                     int64_t N_up, const uint8_t* packed_up,
-                                     const float* gamma_up, bitlinear_epilogue epi_up,
-                                     int64_t N_down, const uint8_t* packed_down,
-                                     const float* gamma_down, float* H, float* Y, void* ws,
-                                     size_t ws_bytes, void* stream);
-
-/* The forward of one token (M = 1) by table lookup instead of multiplies,
- * the method bitnet.cpp's ternary kernels take from T-MAC (dignews.cc
- * article on BitNet b1.58 2B4T, section 3).  X [1][K] is quantized as in
- * bitlinear_forward; then, for every pair of columns, a table of the 16 sums
- * its two 2-bit codes can select is built in LDS, and each 4-bit field of
- * the packed weights reads one entry.  The int32 sums, and so Y, are the same
- * bits as bitlinear_forward's; `dbg` as there.  Needs K % 256 == 0 and
- * K <= 8192 (16.5 bytes of table per column must fit in LDS); N as
- * bitlinear_forward; no workspace.  Errors as bitlinear_forward. */
-bitlinear_status bitlinear_forward_lut(const void* X, bitlinear_dtype dtype, int64_t K,
-                                       int64_t N, const uint8_t* packed, const float* gamma,
-                                       float* Y, bitlinear_epilogue epi,
-                                       const bitlinear_debug* dbg, void* stream);
-
 /* bitlinear_forward with subln first, fused into the quantization (as in
  * bitlinear_quantize_acts_rmsnorm): norm_gain float [K] (device, 16-byte
  * aligned, required), norm_eps finite and >= 0.  Same kernels, workspace and
@@ -363,6 +324,46 @@ bitlinear_status bitlinear_forward_glu_quant(const void* X, bitlinear_dtype dtyp
                                              const float* gamma, float* H, int8_t* Hq,
                                              float* h_scale, int32_t* h_rowsum, void* ws,
                                              size_t ws_bytes, void* stream);
+
+/* The decode FFN ("BitNet b1.58 2B4T Technical Report" card, Method
+ * Adaptation: squared ReLU as the FFN activation) in one persistent launch:
+ * h = relu(X W_up^T)^2 -- or, with epi_up BITLINEAR_EPI_RELU2_GLU and W_up a
+ * fused gate+up matrix from bitlinear_quantize_weights_glu, the gated
+ * max(gate, 0)^2 * up -- written to H [M][F] (F = N_up, or N_up / 2 gated),
+ * then Y [M][N_down] = the BitLinear forward of h with W_down [N_down][F].
+ * H and Y are the same bits as two bitlinear_forward calls.  The up tiles'
+ * workgroups come first in the grid; a down tile's workgroup waits until
+ * every up tile is done (a bounded wait: workgroups start in index order, so
+ * the up tiles are running).  1 <= M <= 4; K % 256 == 0 and F %
+ * 256 == 0, both <= 12288; dtype as bitlinear_forward.  `ws`: at least
+ * bitlinear_ffn_chain_workspace_bytes(N_up) bytes (0 for a bad N_up),
+ * 16-byte aligned, zero before its first use; it holds a counter, a
+ * generation count and one flag per up tile, which every call leaves ready
+ * for the next (its third int is set to 1 and stays set if a wait ever gave
+ * up, which only a failing device can cause).  Calls sharing it must not
+ * overlap.  Errors as bitlinear_forward. */
+size_t bitlinear_ffn_chain_workspace_bytes(int64_t N_up);
+bitlinear_status bitlinear_ffn_chain(const void* X, bitlinear_dtype dtype, int64_t M, int64_t K,
+                                     int64_t N_up, const uint8_t* packed_up,
+                                     const float* gamma_up, bitlinear_epilogue epi_up,
+                                     int64_t N_down, const uint8_t* packed_down,
+                                     const float* gamma_down, float* H, float* Y, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* The forward of one token (M = 1) by table lookup instead of multiplies,
+ * the method bitnet.cpp's ternary kernels take from T-MAC (dignews.cc
+ * article on BitNet b1.58 2B4T, section 3).  X [1][K] is quantized as in
+ * bitlinear_forward; then, for every pair of columns, a table of the 16 sums
+ * its two 2-bit codes can select is built in LDS, and each 4-bit field of
+ * the packed weights reads one entry.  The int32 sums, and so Y, are the same
+ * bits as bitlinear_forward's; `dbg` as there.  Needs K % 256 == 0 and
+ * K <= 8192 (16.5 bytes of table per column must fit in LDS); N as
+ * bitlinear_forward; no workspace.  Errors as bitlinear_forward. */
+bitlinear_status bitlinear_forward_lut(const void* X, bitlinear_dtype dtype, int64_t K,
+                                       int64_t N, const uint8_t* packed, const float* gamma,
+                                       float* Y, bitlinear_epilogue epi,
+                                       const bitlinear_debug* dbg, void* stream);
+
 
 /* ---- Grouped decode forward ------------------------------------------------
  * Many independent BitLinear layers that share the token count M
