@@ -519,11 +519,18 @@ __device__ __forceinline__ bool sk_contribute(int8_t* ring, v16i (&acc)[TM][TN],
   return true;
 }
 
+// Waves per SIMD a configuration is built for: four for 64x64 wave tiles
+// (at most 128 registers), two for wider ones (their accumulators alone take
+// 128).
+template <int TM, int TN>
+constexpr int kWavesPerSimd = TM * TN > 4 ? 2 : 4;
+
 // One layer.  Workgroups below plan.tiles_dp take one output tile each
 // (whole K); the tiles_sk * pieces workgroups after them take one piece of
-// a remaining tile each (sk_ws: counters, then one slot per piece).
+// a remaining tile each (sk_ws: counters, then one slot per piece).  Tiles
+// larger than a slot are never cut (the host plans no pieces for them).
 template <int WM, int WN, int TM, int TN, int S, bool DEBUG, bool LEVEL, bool GLU>
-__global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
+__global__ __launch_bounds__(64 * WM * WN, (kWavesPerSimd<TM, TN>)) void gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
@@ -557,7 +564,10 @@ __global__ __launch_bounds__(64 * WM * WN, 4) void gemm_kernel(
   if constexpr (LEVEL) if (split) __builtin_amdgcn_s_setprio(3);
   tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, k0, k1, !split, acc);
   if constexpr (LEVEL) __builtin_amdgcn_s_setprio(0);
-  if (!split || sk_contribute<WM, WN, TM, TN, S>(ring, acc, plan, sk_ws, t, g))
+  bool whole = !split;
+  if constexpr (T::BM * T::BN <= kSkSlotInts)
+    if (split) whole = sk_contribute<WM, WN, TM, TN, S>(ring, acc, plan, sk_ws, t, g);
+  if (whole)
     tile_epilogue<WM, WN, TM, TN, S, DEBUG, GLU>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
                                             tn);
 }
@@ -638,7 +648,7 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
   const int tiles_n = (int)((N + T::BN - 1) / T::BN);
   const int total = tiles_m * tiles_n;
   SkPlan plan{total, 0, (int)(K / kStepCols), 0};
-  if (sk_ws) {
+  if (sk_ws && T::BM * T::BN <= kSkSlotInts) {
     const int P = std::min(device_cus(), kSkMaxGroups);
     const int R = total % P;
     // Pieces per remaining tile: fill the compute units, at least two
@@ -691,7 +701,23 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 // 64x256 (4 waves of 32x128) for many layers, whose persistent grid has
 // work for every slot: the wider tile halves the activation bytes copied
 // per multiply (7B step at M = 64: 547 against 611 us).
+//
+// One exception for one layer above 64 tokens: when the 128x256 tiles (4
+// waves of 64x128, two workgroups per CU) make one round that every CU
+// joins (more tiles than CUs, no more than the resident slots), they are
+// used instead.  A 64x128 wave tile reads half the activation bytes from
+// LDS per multiply, and the workgroup copies 24 KiB per step for 128
+// multiplies against 20 KiB for 64.  Measured (graph-timed launches, three
+// runs each): 2048 x 2560 -> 6912 (432 tiles) 34.5-34.8 us against
+// 37.5-38.9 us; 512 x 4096 -> 22016 (344 tiles) 44.6-47.0 against
+// 43.2-49.9 us.  Elsewhere the wide tiles lost or tied: fewer tiles than
+// CUs (2048 x 6912 -> 2560: 160 tiles) 46 against 38 us; 1.7 rounds
+// (4096 x 2560 -> 6912) 69.6 against 67.1 us; 2048 x 2560 -> 13824 70.5
+// against 68.5 us.  (At four whole rounds, 8192 x 4096 -> 8192, they won,
+// 209 against 223 us; one shape, not taken.)  Those tiles are never cut
+// along K (a slot holds one 128x128 tile).
 using BigCfg = Tile<2, 2, 2, 2, 2>;
+using WideCfg = Tile<2, 2, 2, 4, 2>;
 using GroupSmallCfg = Tile<2, 2, 1, 4, 2>;
 constexpr int kSmallM = 64;
 
@@ -740,6 +766,12 @@ hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_
                             void* gemm_ws, hipStream_t s) {
   if (M <= kSmallM)
     return launch_cfg<2, 2, 1, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
+                                     acc_out, static_cast<int*>(gemm_ws), s);
+  const int64_t wide_tiles = ((M + WideCfg::BM - 1) / WideCfg::BM) *
+                             ((N + WideCfg::BN - 1) / WideCfg::BN);
+  const int cus = device_cus();
+  if (wide_tiles > cus && wide_tiles <= (int64_t)cus * resident_per_cu<2, 2, 2, 4, 2>())
+    return launch_cfg<2, 2, 2, 4, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
                                      acc_out, static_cast<int*>(gemm_ws), s);
   return launch_cfg<2, 2, 2, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
                                    acc_out, static_cast<int*>(gemm_ws), s);
