@@ -582,7 +582,7 @@ __global__ __launch_bounds__(64 * WM * WN, (kWavesPerSimd<TM, TN>)) void gemm_ke
 // to different XCDs), so what they share stays in one L2.  Every layer's
 // items spread evenly over the workgroups, which balances the cost.
 template <int WM, int WN, int TM, int TN, int S, bool GLU>
-__global__ __launch_bounds__(64 * WM * WN, 3) void group_gemm_kernel(
+__global__ __launch_bounds__(64 * WM * WN, (TM * TN > 4 ? 2 : 3)) void group_gemm_kernel(
     const GroupOp* __restrict__ ops, int n_ops, int M, int n_items,
     const int8_t* __restrict__ xq, const float* __restrict__ sx, const int* __restrict__ rs) {
   using T = Tile<WM, WN, TM, TN, S>;
@@ -692,46 +692,47 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 
 }  // namespace
 
-// Tile choice, measured on MI355X over the prefill shapes (M = 512, 2048;
-// K = 2560..6912; N = 2560..22016): 128x128 workgroup tiles (4 waves of
-// 64x64) with a two-stage ring and four waves per SIMD beat 128x256 tiles
-// (fewer workgroups than slots at N = 2560), 64x128 and 64x256 tiles, and
-// deeper rings with shorter steps.  Up to 64 tokens, 64-row tiles avoid
-// multiplying 64 empty rows: 64x128 (4 waves of 32x64) for one layer, and
-// 64x256 (4 waves of 32x128) for many layers, whose persistent grid has
-// work for every slot: the wider tile halves the activation bytes copied
-// per multiply (7B step at M = 64: 547 against 611 us).
+// Tile choice, measured on MI355X (graph-timed launches, several runs each).
 //
-// One exception for one layer above 64 tokens: when the 128x256 tiles (4
-// waves of 64x128, two workgroups per CU) make one round that every CU
-// joins (more tiles than CUs, no more than the resident slots), they are
-// used instead.  A 64x128 wave tile reads half the activation bytes from
-// LDS per multiply, and the workgroup copies 24 KiB per step for 128
-// multiplies against 20 KiB for 64.  Measured (graph-timed launches, three
-// runs each): 2048 x 2560 -> 6912 (432 tiles) 34.5-34.8 us against
-// 37.5-38.9 us; 512 x 4096 -> 22016 (344 tiles) 44.6-47.0 against
-// 43.2-49.9 us.  Elsewhere the wide tiles lost or tied: fewer tiles than
-// CUs (2048 x 6912 -> 2560: 160 tiles) 46 against 38 us; 1.7 rounds
-// (4096 x 2560 -> 6912) 69.6 against 67.1 us; 2048 x 2560 -> 13824 70.5
-// against 68.5 us.  (At four whole rounds, 8192 x 4096 -> 8192, they won,
-// 209 against 223 us; one shape, not taken.)  Those tiles are never cut
-// along K (a slot holds one 128x128 tile).
-using BigCfg = Tile<2, 2, 2, 2, 2>;
+// One layer above 64 tokens: 128x128 tiles (4 waves of 64x64, four
+// workgroups per CU), with the last partial round cut along K.  These beat
+// 64x128 and 64x256 tiles, deeper rings with shorter steps, and two-wave
+// workgroups.  The exception: when 128x256 tiles (4 waves of 64x128, two
+// workgroups per CU) make one round that every CU joins (more tiles than
+// CUs, no more than the resident slots), they are used instead.  A 64x128
+// wave tile reads half the activation bytes from LDS per multiply, and the
+// workgroup copies 24 KiB per step for 128 multiplies against 20 KiB for 64:
+// 2048 x 2560 -> 6912 (432 tiles) 34.5-34.8 us against 37.5-38.9 us.
+// Elsewhere they lost or tied: fewer tiles than CUs (2048 x 6912 -> 2560)
+// 46 against 38 us; 1.7 rounds (4096 x 2560 -> 6912) 69.6 against 67.1 us.
+// They are never cut along K (a slot holds one 128x128 tile).
+//
+// One layer up to 64 tokens: 64-row tiles avoid multiplying 64 empty rows,
+// 64x128 (4 waves of 32x64).
+//
+// Many layers (a persistent grid that has work for every slot): up to 64
+// tokens, 64x256 tiles, which halve the activation bytes copied per multiply
+// against 64x128 (7B step at M = 64: 547 against 611 us).  Their four waves
+// sit side by side, 64x64 each, so every unpacked weight operand feeds two
+// MFMAs (as 32x128 waves, one): 508-513 against 557-563 us, and the 2B step
+// at M = 64 248 against 250 us.  (4 waves of 64x128 in 64x512 tiles: 538
+// and 230 us.)  Above 64 tokens, the 128x256 tiles: 7B step at M = 512
+// 3157-3195 against 3382 us with 128x128 tiles.
 using WideCfg = Tile<2, 2, 2, 4, 2>;
-using GroupSmallCfg = Tile<2, 2, 1, 4, 2>;
+using GroupSmallCfg = Tile<1, 4, 2, 2, 2>;
 constexpr int kSmallM = 64;
 
 int bl_group_gemm_tiles(int M, int N) {
-  const int bm = M <= kSmallM ? GroupSmallCfg::BM : BigCfg::BM;
-  const int bn = M <= kSmallM ? GroupSmallCfg::BN : BigCfg::BN;
+  const int bm = M <= kSmallM ? GroupSmallCfg::BM : WideCfg::BM;
+  const int bn = M <= kSmallM ? GroupSmallCfg::BN : WideCfg::BN;
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
 int bl_group_gemm_blocks_per_cu(int M) {
   int blocks = 0;
   const void* k = M <= kSmallM
-                      ? reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 1, 4, 2, false>)
-                      : reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 2, 2, false>);
+                      ? reinterpret_cast<const void*>(&group_gemm_kernel<1, 4, 2, 2, 2, false>)
+                      : reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 4, 2, false>);
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 256, 0);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
@@ -739,15 +740,15 @@ int bl_group_gemm_blocks_per_cu(int M) {
 hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
                                 const int8_t* xq, const float* sx, const int* rs, bool glu,
                                 hipStream_t s) {
-#define BL_GROUP_GEMM(CFG, TN, GL)                                                            \
-  hipLaunchKernelGGL((group_gemm_kernel<2, 2, CFG::BM / 64, TN, 2, GL>), dim3(G),              \
-                     dim3(CFG::kThreads), 0, s, ops, n_ops, M, n_items, xq, sx, rs)
+#define BL_GROUP_GEMM(WM, WN, TM, TN, GL)                                                     \
+  hipLaunchKernelGGL((group_gemm_kernel<WM, WN, TM, TN, 2, GL>), dim3(G), dim3(64 * WM * WN), \
+                     0, s, ops, n_ops, M, n_items, xq, sx, rs)
   if (M <= kSmallM) {
-    if (glu) BL_GROUP_GEMM(GroupSmallCfg, 4, true);
-    else BL_GROUP_GEMM(GroupSmallCfg, 4, false);
+    if (glu) BL_GROUP_GEMM(1, 4, 2, 2, true);
+    else BL_GROUP_GEMM(1, 4, 2, 2, false);
   } else {
-    if (glu) BL_GROUP_GEMM(BigCfg, 2, true);
-    else BL_GROUP_GEMM(BigCfg, 2, false);
+    if (glu) BL_GROUP_GEMM(2, 2, 2, 4, true);
+    else BL_GROUP_GEMM(2, 2, 2, 4, false);
   }
 #undef BL_GROUP_GEMM
   return hipGetLastError();
