@@ -716,10 +716,11 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 // sit side by side, 64x64 each, so every unpacked weight operand feeds two
 // MFMAs (as 32x128 waves, one): 508-513 against 557-563 us, and the 2B step
 // at M = 64 248 against 250 us.  (4 waves of 64x128 in 64x512 tiles: 538
-// and 230 us.)  Above 64 tokens, the 128x256 tiles: 7B step at M = 512
+// and 230 us.)  A 3-stage ring (48 KiB, three workgroups per CU) then
+// gains: 519-524 against 534-550 us, 2B step 225 against 251 us.  Above 64 tokens, the 128x256 tiles: 7B step at M = 512
 // 3157-3195 against 3382 us with 128x128 tiles.
 using WideCfg = Tile<2, 2, 2, 4, 2>;
-using GroupSmallCfg = Tile<1, 4, 2, 2, 2>;
+using GroupSmallCfg = Tile<1, 4, 2, 2, 3>;
 constexpr int kSmallM = 64;
 
 int bl_group_gemm_tiles(int M, int N) {
@@ -731,7 +732,7 @@ int bl_group_gemm_tiles(int M, int N) {
 int bl_group_gemm_blocks_per_cu(int M) {
   int blocks = 0;
   const void* k = M <= kSmallM
-                      ? reinterpret_cast<const void*>(&group_gemm_kernel<1, 4, 2, 2, 2, false>)
+                      ? reinterpret_cast<const void*>(&group_gemm_kernel<1, 4, 2, 2, 3, false>)
                       : reinterpret_cast<const void*>(&group_gemm_kernel<2, 2, 2, 4, 2, false>);
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 256, 0);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
@@ -740,15 +741,15 @@ int bl_group_gemm_blocks_per_cu(int M) {
 hipError_t bl_launch_group_gemm(const GroupOp* ops, int n_ops, int M, int n_items, int G,
                                 const int8_t* xq, const float* sx, const int* rs, bool glu,
                                 hipStream_t s) {
-#define BL_GROUP_GEMM(WM, WN, TM, TN, GL)                                                     \
-  hipLaunchKernelGGL((group_gemm_kernel<WM, WN, TM, TN, 2, GL>), dim3(G), dim3(64 * WM * WN), \
+#define BL_GROUP_GEMM(WM, WN, TM, TN, S, GL)                                                  \
+  hipLaunchKernelGGL((group_gemm_kernel<WM, WN, TM, TN, S, GL>), dim3(G), dim3(64 * WM * WN), \
                      0, s, ops, n_ops, M, n_items, xq, sx, rs)
   if (M <= kSmallM) {
-    if (glu) BL_GROUP_GEMM(1, 4, 2, 2, true);
-    else BL_GROUP_GEMM(1, 4, 2, 2, false);
+    if (glu) BL_GROUP_GEMM(1, 4, 2, 2, 3, true);
+    else BL_GROUP_GEMM(1, 4, 2, 2, 3, false);
   } else {
-    if (glu) BL_GROUP_GEMM(2, 2, 2, 4, true);
-    else BL_GROUP_GEMM(2, 2, 2, 4, false);
+    if (glu) BL_GROUP_GEMM(2, 2, 2, 4, 2, true);
+    else BL_GROUP_GEMM(2, 2, 2, 4, 2, false);
   }
 #undef BL_GROUP_GEMM
   return hipGetLastError();
