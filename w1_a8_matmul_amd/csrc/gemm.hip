@@ -520,17 +520,18 @@ __device__ __forceinline__ bool sk_contribute(int8_t* ring, v16i (&acc)[TM][TN],
 }
 
 // Waves per SIMD a configuration is built for: four for 64x64 wave tiles
-// (at most 128 registers), two for wider ones (their accumulators alone take
-// 128).
-template <int TM, int TN>
-constexpr int kWavesPerSimd = TM * TN > 4 ? 2 : 4;
+// in a 2-stage ring (at most 128 registers), two for wider ones (their
+// accumulators alone take 128) and for 3-stage rings (60 KiB of LDS: two
+// workgroups per CU).
+template <int TM, int TN, int S>
+constexpr int kWavesPerSimd = TM * TN > 4 || S > 2 ? 2 : 4;
 
 // One layer.  Workgroups below plan.tiles_dp take one output tile each
 // (whole K); the tiles_sk * pieces workgroups after them take one piece of
 // a remaining tile each (sk_ws: counters, then one slot per piece).  Tiles
 // larger than a slot are never cut (the host plans no pieces for them).
 template <int WM, int WN, int TM, int TN, int S, bool DEBUG, bool LEVEL, bool GLU>
-__global__ __launch_bounds__(64 * WM * WN, (kWavesPerSimd<TM, TN>)) void gemm_kernel(
+__global__ __launch_bounds__(64 * WM * WN, (kWavesPerSimd<TM, TN, S>)) void gemm_kernel(
     const int8_t* __restrict__ Xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_rowsum, int M, int K, int N,
     const uint8_t* __restrict__ packed, const float* __restrict__ gamma_p,
@@ -639,16 +640,15 @@ int resident_per_cu() {
   return v;
 }
 
-template <int WM, int WN, int TM, int TN, int S>
-hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M,
-                      int64_t K, int64_t N, const uint8_t* packed, const float* gamma, float* Y,
-                      int epi, int32_t* acc_out, int* sk_ws, hipStream_t s) {
-  using T = Tile<WM, WN, TM, TN, S>;
-  const int tiles_m = (int)((M + T::BM - 1) / T::BM);
-  const int tiles_n = (int)((N + T::BN - 1) / T::BN);
+// Output tiles of BM x BN for one layer, and which of them are cut along K
+// (split: a workspace was given and a slot holds such a tile).
+template <int BM, int BN>
+SkPlan plan_tiles(int64_t M, int64_t K, int64_t N, bool split) {
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int tiles_n = (int)((N + BN - 1) / BN);
   const int total = tiles_m * tiles_n;
   SkPlan plan{total, 0, (int)(K / kStepCols), 0};
-  if (sk_ws && T::BM * T::BN <= kSkSlotInts) {
+  if (split && BM * BN <= kSkSlotInts) {
     const int P = std::min(device_cus(), kSkMaxGroups);
     const int R = total % P;
     // Pieces per remaining tile: fill the compute units, at least two
@@ -660,7 +660,19 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
       plan.pieces = f;
     }
   }
-  const int grid = plan.tiles_dp + plan.tiles_sk * plan.pieces;
+  return plan;
+}
+
+int plan_grid(const SkPlan& p) { return p.tiles_dp + p.tiles_sk * p.pieces; }
+
+template <int WM, int WN, int TM, int TN, int S>
+hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int64_t M,
+                      int64_t K, int64_t N, const uint8_t* packed, const float* gamma, float* Y,
+                      int epi, int32_t* acc_out, int* sk_ws, hipStream_t s) {
+  using T = Tile<WM, WN, TM, TN, S>;
+  const int tiles_n = (int)((N + T::BN - 1) / T::BN);
+  const SkPlan plan = plan_tiles<T::BM, T::BN>(M, K, N, sk_ws != nullptr);
+  const int grid = plan_grid(plan);
   // Level the whole-tile workgroups (priority steps) when the whole grid is
   // resident at once: with rounds queued behind them, staggered finishes
   // overlap one workgroup's epilogue with the next one's start.  With split
@@ -705,7 +717,13 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 // 2048 x 2560 -> 6912 (432 tiles) 34.5-34.8 us against 37.5-38.9 us.
 // Elsewhere they lost or tied: fewer tiles than CUs (2048 x 6912 -> 2560)
 // 46 against 38 us; 1.7 rounds (4096 x 2560 -> 6912) 69.6 against 67.1 us.
-// They are never cut along K (a slot holds one 128x128 tile).
+// They are never cut along K (a slot holds one 128x128 tile).  When the
+// 128x128 grid (pieces included) needs no more than two workgroups per CU,
+// a 3-stage ring (60 KiB, two steps of copies in flight) costs no
+// residency and gains: 2048 x 6912 -> 2560 (256 tiles and 64 tiles in 4
+// pieces) 36.9-37.2 against 38.0-38.4 us, 512 x 11008 -> 4096 28.9-29.3
+// against 30.4-31.2 us; with rounds queued it loses (4096 x 2560 -> 6912:
+// 73.6 against 66.3 us).
 //
 // One layer up to 64 tokens: 64-row tiles avoid multiplying 64 empty rows,
 // 64x128 (4 waves of 32x64).
@@ -774,6 +792,9 @@ hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_
   const int cus = device_cus();
   if (wide_tiles > cus && wide_tiles <= (int64_t)cus * resident_per_cu<2, 2, 2, 4, 2>())
     return launch_cfg<2, 2, 2, 4, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
+                                     acc_out, static_cast<int*>(gemm_ws), s);
+  if (plan_grid(plan_tiles<128, 128>(M, K, N, gemm_ws != nullptr)) <= 2 * cus)
+    return launch_cfg<2, 2, 2, 2, 3>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
                                      acc_out, static_cast<int*>(gemm_ws), s);
   return launch_cfg<2, 2, 2, 2, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
                                    acc_out, static_cast<int*>(gemm_ws), s);
