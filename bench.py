@@ -20,8 +20,9 @@ no step finds its weights in the 256 MB Infinity Cache.  The same JSON line
 carries keyed sub-records (``sub``) for the decode GEMV pair (M = 1, up ->
 ReLU^2 -> down, 61 rotating weight copies), the 2B step at M = 4 and 16, and
 the prefill GEMMs at M = 2048 (int8 TOPS), the 2B step at M = 1 with its
-weights in the base-3 layout (five codes per byte), and the decode pair by
-table lookup instead of multiplies.
+weights in the base-3 layout (five codes per byte), the 7B-like step (32
+layers, 128 linears) at M = 1, 64 and 512 (int8 TOPS at 512), and the decode
+pair by table lookup instead of multiplies.
 
 Timing: W warm-up steps, then exactly K steps, each as one HIP graph replay
 on torch's stream, bracketed by synchronizations; HIP events around the
@@ -648,7 +649,8 @@ def step_record(runner, ev_ms, wall_ms, metric_kind):
 
 def sub_records(args, torch, bl, wl, dev, main_runner):
     """Keyed sub-records: decode GEMV pair; the 2B step at M = 4 and 16 (on the
-    main line's weights when it is the 2B step); prefill GEMMs at M = 2048."""
+    main line's weights when it is the 2B step); the 7B-like step at M = 1, 64
+    and 512; prefill GEMMs at M = 2048."""
     subs = {}
     steps, warmup = max(20, args.steps // 2), max(5, args.warmup // 2)
 
@@ -719,6 +721,23 @@ def sub_records(args, torch, bl, wl, dev, main_runner):
         log(f"2B step M=1, base-3 weights: {rec['us_per_step']} us, {rec['value']} GB/s")
         del r
         torch.cuda.empty_cache()
+
+    # the 7B-like step (32 layers, 128 linears, 1.62 GB packed) at M = 1, 64
+    # and 512 on one weight set pair, grouped; M = 512 in int8 TOPS
+    r7 = Runner(bl, torch, wl, dev, "decode_prefill_7b", 1, grouped=True)
+    for M in (1, 64, 512):
+        r = r7 if M == 1 else Runner(bl, torch, wl, dev, "decode_prefill_7b", M, grouped=True,
+                                     share_weights=r7)
+        kind = "tops" if M >= 128 else "hbm"
+        ev, wall = time_steps(torch, r, steps, warmup)
+        rec = step_record(r, ev, wall, kind)
+        rec["launches_per_step"] = 1 if M <= GROUP_INLINE_MAX_M else 2
+        subs[f"decode_prefill_7b_m{M}"] = rec
+        log(f"7B step M={M}: {rec['us_per_step']} us, {rec['value']} {rec['unit']}")
+        if r is not r7:
+            del r
+    del r7
+    torch.cuda.empty_cache()
 
     # prefill, M = 2048: the whole step (two quantizations + two GEMMs) and each
     # GEMM launch alone
