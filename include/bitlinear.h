@@ -289,12 +289,15 @@ bitlinear_status bitlinear_forward_noalloc(const void* X, bitlinear_dtype dtype,
 /* The same forward from activations already quantized by
  * bitlinear_quantize_acts (the int8 matmul and rescale of the same card,
  * Method Adaptation): Xq [M][K], x_scale [M], x_rowsum [M] (all three
- * required).  The output tiles (128 x 128) are spread over the compute
- * units one workgroup each; when they do not divide evenly, each tile of the
- * last, partial round is instead cut along K into pieces, one workgroup
- * each, whose exact int32 partial sums meet in `ws` (same bits either way).
- * `ws` (device, 16-byte aligned, at least bitlinear_forward_q_workspace_bytes)
- * enables that; NULL runs one workgroup per tile.  Up to four tokens (K <=
+ * required).  The output tiles (128 x 128; 64 x 128 up to 64 tokens) are
+ * spread over the compute units one workgroup each; when they do not divide
+ * evenly, each tile of the last, partial round is instead cut along K into
+ * pieces, one workgroup each, whose exact int32 partial sums meet in `ws`
+ * (same bits either way).  `ws` (device, 16-byte aligned, at least
+ * bitlinear_forward_q_workspace_bytes) enables that; NULL runs one workgroup
+ * per tile.  Above 64 tokens, when 128 x 256 tiles outnumber the compute
+ * units but fit on them at once (two per unit), those run instead, never cut
+ * along K.  Every choice gives the same bits.  Up to four tokens (K <=
  * 12288) the one-launch decode kernel runs instead, with the rows copied
  * rather than quantized, and `ws` is not used.  Its first 4 KiB (counters) must be zero the first time a
  * workspace is used, and every call leaves them zero again; the rest needs
