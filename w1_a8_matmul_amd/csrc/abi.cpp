@@ -842,7 +842,7 @@ bitlinear_status bitlinear_group_forward(const bitlinear_group* g, void* stream)
   if (g->gemm) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e =
-        bl_launch_group_quant(g->ops, g->n_ops, g->M, g->max_k, g->xq, g->sx, g->rs, s);
+        bl_launch_group_quant(g->ops, g->n_ops, g->M, g->max_k, g->norm, g->xq, g->sx, g->rs, s);
     if (e == hipSuccess)
       e = bl_launch_group_gemm(g->ops, g->n_ops, g->M, g->n_items, g->G, g->xq, g->sx, g->rs,
                                g->glu, s);

@@ -465,22 +465,29 @@ __global__ __launch_bounds__(256) void group_quant_loop_kernel(const GroupOp* __
 // One pass for layers of at most KCH * 2048 columns: the row's chunks (and
 // any subln gains) are loaded at entry and stay in registers through the
 // max reduction; same arithmetic, in the same order, as the two-pass form.
-template <int DT, int KCH>
+// NORM: some layer of the group has a subln gain (a layer without one then
+// reads an empty range of zeros and skips it).  Without it the kernel holds
+// no gain registers: at 6 chunks 64 registers instead of 154 (8 waves per
+// SIMD instead of 3), at 4 chunks 48 instead of 106.
+template <int DT, int KCH, bool NORM>
 __device__ __forceinline__ void group_quant_row(const GroupOp& o, int m, int8_t* dst,
                                                 float* red_f, int* red_i, double* red_d,
                                                 float* s_scale, int* s_rowsum) {
   Chunk<DT> ch[KCH];
   load_row<DT, 256, KCH>(o.X, m, o.K, ch);
-  Gains<256, KCH> gn;
-  load_gains<256, KCH>(o.norm_gain, o.K, gn);  // no gain: an empty range, zeros
-  if (o.norm_gain)
-    quantize_row<DT, 256, KCH, true>(ch, o.K, dst, red_f, red_i, s_scale, s_rowsum, &gn, true,
-                                     o.norm_eps, red_d);
-  else
-    quantize_row<DT, 256, KCH, false>(ch, o.K, dst, red_f, red_i, s_scale, s_rowsum);
+  if constexpr (NORM) {
+    Gains<256, KCH> gn;
+    load_gains<256, KCH>(o.norm_gain, o.K, gn);  // no gain: an empty range, zeros
+    if (o.norm_gain) {
+      quantize_row<DT, 256, KCH, true>(ch, o.K, dst, red_f, red_i, s_scale, s_rowsum, &gn, true,
+                                       o.norm_eps, red_d);
+      return;
+    }
+  }
+  quantize_row<DT, 256, KCH, false>(ch, o.K, dst, red_f, red_i, s_scale, s_rowsum);
 }
 
-template <int KCH>
+template <int KCH, bool NORM>
 __global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restrict__ ops, int M,
                                                           int8_t* __restrict__ xq,
                                                           float* __restrict__ sx,
@@ -494,9 +501,9 @@ __global__ __launch_bounds__(256) void group_quant_kernel(const GroupOp* __restr
   const GroupOp o = ops[op];
   int8_t* dst = xq + o.xq_off + (int64_t)m * o.K;
   if (o.dtype == 1)
-    group_quant_row<1, KCH>(o, m, dst, red_f, red_i, red_d, &s_scale, &s_rowsum);
+    group_quant_row<1, KCH, NORM>(o, m, dst, red_f, red_i, red_d, &s_scale, &s_rowsum);
   else
-    group_quant_row<0, KCH>(o, m, dst, red_f, red_i, red_d, &s_scale, &s_rowsum);
+    group_quant_row<0, KCH, NORM>(o, m, dst, red_f, red_i, red_d, &s_scale, &s_rowsum);
   if (threadIdx.x == 0) {  // thread 0 wrote both
     sx[op * M + m] = s_scale;
     rs[op * M + m] = s_rowsum;
@@ -581,19 +588,25 @@ int blocks_per_cu(int threads, int M, bool norm, bool b3, size_t lds, int max_k)
 
 bool bl_group_prequantizes(int M) { return M > kGroupInlineQuantMaxM; }
 
-hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int max_k, int8_t* xq,
-                                 float* sx, int* rs, hipStream_t s) {
+hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int max_k, bool norm,
+                                 int8_t* xq, float* sx, int* rs, hipStream_t s) {
   const dim3 grid((unsigned)(n_ops * M)), block(256);
-  if (max_k <= 2048)
-    hipLaunchKernelGGL(group_quant_kernel<1>, grid, block, 0, s, ops, M, xq, sx, rs);
-  else if (max_k <= 4096)
-    hipLaunchKernelGGL(group_quant_kernel<2>, grid, block, 0, s, ops, M, xq, sx, rs);
-  else if (max_k <= 8192)
-    hipLaunchKernelGGL(group_quant_kernel<4>, grid, block, 0, s, ops, M, xq, sx, rs);
-  else if (max_k <= 12288)
-    hipLaunchKernelGGL(group_quant_kernel<6>, grid, block, 0, s, ops, M, xq, sx, rs);
-  else
+#define BL_GROUP_QUANT(KCH)                                                                  \
+  if (norm)                                                                                  \
+    hipLaunchKernelGGL((group_quant_kernel<KCH, true>), grid, block, 0, s, ops, M, xq, sx, rs); \
+  else                                                                                       \
+    hipLaunchKernelGGL((group_quant_kernel<KCH, false>), grid, block, 0, s, ops, M, xq, sx, rs)
+  if (max_k <= 2048) {
+    BL_GROUP_QUANT(1);
+  } else if (max_k <= 4096) {
+    BL_GROUP_QUANT(2);
+  } else if (max_k <= 8192) {
+    BL_GROUP_QUANT(4);
+  } else if (max_k <= 12288) {
+    BL_GROUP_QUANT(6);
+  } else
     hipLaunchKernelGGL(group_quant_loop_kernel, grid, block, 0, s, ops, M, xq, sx, rs);
+#undef BL_GROUP_QUANT
   return hipGetLastError();
 }
 
@@ -634,7 +647,7 @@ hipError_t bl_launch_group(const GroupOp* ops, int n_ops, int M, const int* wg_b
   const size_t lds = bl_group_lds_bytes(M, max_k);
   const bool preq = bl_group_prequantizes(M);
   if (preq) {
-    const hipError_t e = bl_launch_group_quant(ops, n_ops, M, max_k, xq, sx, rs, s);
+    const hipError_t e = bl_launch_group_quant(ops, n_ops, M, max_k, norm, xq, sx, rs, s);
     if (e != hipSuccess) return e;
   }
   if (threads == 512 && b3)

@@ -117,9 +117,10 @@ constexpr int kGroupPreqWideM = 8;
 bool bl_group_prequantizes(int M);
 
 // The quantization launch of the grouped forward (one workgroup per layer
-// and token) into xq / sx / rs at each layer's xq_off; max_k the largest K.
-hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int max_k, int8_t* xq,
-                                 float* sx, int* rs, hipStream_t s);
+// and token) into xq / sx / rs at each layer's xq_off; max_k the largest K,
+// norm whether some layer has a subln gain.
+hipError_t bl_launch_group_quant(const GroupOp* ops, int n_ops, int M, int max_k, bool norm,
+                                 int8_t* xq, float* sx, int* rs, hipStream_t s);
 
 // Dynamic LDS bytes of the grouped kernel for M tokens and largest K.
 size_t bl_group_lds_bytes(int M, int max_k);
