@@ -63,6 +63,14 @@ __device__ __forceinline__ void copy16(v4i rs, uint32_t voff, void* lds) {
                :: "v"(voff), "s"(la), "s"(rs) : "memory", "m0");
 }
 
+// The same copy with the non-temporal (streaming) policy: for weight tiles
+// that no other workgroup will read.
+__device__ __forceinline__ void copy16_nt(v4i rs, uint32_t voff, void* lds) {
+  const uint32_t la = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen nt lds"
+               :: "v"(voff), "s"(la), "s"(rs) : "memory", "m0");
+}
+
 // The same copy with the sc1 cache policy (device-coherent: it does not
 // hit data that another XCD's L2 may hold stale).
 __device__ __forceinline__ void copy16_coherent(v4i rs, uint32_t voff, void* lds) {
@@ -118,7 +126,8 @@ __device__ __forceinline__ void lds_barrier() {
 // [k0, k1) (128 columns each) into acc.  `ring` is the workgroup's LDS ring
 // (S stages of kStageBytes).  Every wave leaves with its copies landed and
 // its LDS reads returned; other waves may still be reading the ring.
-template <int WM, int WN, int TM, int TN, int S, bool LEVEL>
+// STREAM_B: copy the weight tiles with the non-temporal policy.
+template <int WM, int WN, int TM, int TN, int S, bool LEVEL, bool STREAM_B = false>
 __device__ __forceinline__ void tile_mainloop(int8_t* ring, const int8_t* __restrict__ Xq,
                                               int M, int K, int N,
                                               const uint8_t* __restrict__ packed, int tm,
@@ -172,7 +181,10 @@ __device__ __forceinline__ void tile_mainloop(int8_t* ring, const int8_t* __rest
       const uint32_t voff = (uint32_t)((t * kblocks + (kh >> 1)) * kTileBytes +
                                        (kh & 1) * (kTileBytes / 2) + (lane & 31) * 16) |
                             past;
-      copy16(b_rsrc, voff, base + T::kABytes + q * 1024);
+      if constexpr (STREAM_B)
+        copy16_nt(b_rsrc, voff, base + T::kABytes + q * 1024);
+      else
+        copy16(b_rsrc, voff, base + T::kABytes + q * 1024);
     }
   };
   // Copies this wave issues per step.
@@ -406,8 +418,16 @@ __device__ __forceinline__ void gemm_tile(
   const RowScale own = load_row_scale<WM, WN, TM, TN, S>(x_scale, x_rowsum, M, tm);
   const float gamma = *gamma_p;
   v16i acc[TM][TN];
-  tile_mainloop<WM, WN, TM, TN, S, LEVEL>(ring, Xq, M, K, N, packed, tm, tn, 0, K / kStepCols,
-                                          true, acc);
+  // Many layers up to 64 tokens (64-row tiles): one tile row per layer, so
+  // each weight byte is read once and streams past the caches (7B step at
+  // M = 64: 455-464 against 462-479 us, 2B step at M = 64 208-210 against
+  // 216-219).  Taller tiles share weight tiles through L2 and keep the
+  // default policy (non-temporal: 7B step at M = 512 +4.5%, prefill GEMMs
+  // +20%), and so does the one-layer kernel (64 x 4096 -> 22016: 20.2
+  // against 16.7 us).
+  constexpr bool kStreamB = 32 * TM * WM <= 64;
+  tile_mainloop<WM, WN, TM, TN, S, LEVEL, kStreamB>(ring, Xq, M, K, N, packed, tm, tn, 0,
+                                                    K / kStepCols, true, acc);
   tile_epilogue<WM, WN, TM, TN, S, DEBUG, GLU>(ring, acc, own, gamma, M, N, Y, epi, acc_out, tm,
                                           tn);
 }
