@@ -520,8 +520,9 @@ def context_probes(torch):
     from w1_a8_matmul_amd.build import PROBES_LIBRARY
 
     L = ctypes.CDLL(PROBES_LIBRARY)
-    L.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
-                                    ctypes.c_int, ctypes.c_void_p]
+    for fn_name in ("probe_stream_read", "probe_stream_read_nt"):
+        getattr(L, fn_name).argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_void_p]
     L.probe_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                 ctypes.c_int, ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -530,9 +531,15 @@ def context_probes(torch):
     out = {"probe": "context", "compute_units": cus}
 
     # streaming read: sizes x buffer copies (copies rotate so that the small
-    # sizes stream from HBM rather than the 256 MB Infinity Cache)
-    for label, nbytes, copies in (("1GiB", 1 << 30, 1), ("2b_step_521MB", 521011200, 1),
-                                  ("gemv_4.4MB", 4423680, 61)):
+    # sizes stream from HBM rather than the 256 MB Infinity Cache, and the
+    # 521 MB read alternates two buffers as the decode bench does), with the
+    # default and the non-temporal load policy
+    for label, nbytes, copies, read in (
+            ("1GiB", 1 << 30, 1, L.probe_stream_read),
+            ("2b_step_521MB", 521011200, 1, L.probe_stream_read),
+            ("2b_step_521MB_2buf_nt", 521011200, 2, L.probe_stream_read_nt),
+            ("gemv_4.4MB", 4423680, 61, L.probe_stream_read),
+            ("gemv_4.4MB_nt", 4423680, 61, L.probe_stream_read_nt)):
         bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
         best = None
         for wg_per_cu in (2, 3, 4, 8):
@@ -540,10 +547,10 @@ def context_probes(torch):
 
             def fn(i):
                 b = bufs[i % copies]
-                rc = L.probe_stream_read(b.data_ptr(), nbytes, sink.data_ptr(), grid, st())
+                rc = read(b.data_ptr(), nbytes, sink.data_ptr(), grid, st())
                 assert rc == 0, rc
 
-            us = time_graph(torch, fn, 4 if copies == 1 else 200)
+            us = time_graph(torch, fn, 4 if copies == 1 else (40 if copies == 2 else 200))
             gbs = nbytes / (us * 1e-6) / 1e9
             if best is None or gbs > best[0]:
                 best = (round(gbs, 1), round(us, 3), wg_per_cu)

@@ -14,7 +14,10 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // Streaming read: workgroup g reads the 16-byte chunks g*256 + t, advancing
 // by the whole grid, ten loads in flight per lane.  Each workgroup writes
-// one word so that the loads stay live.  `bytes` is a multiple of 16.
+// one word so that the loads stay live.  `bytes` is a multiple of 16.  NT:
+// the loads carry the non-temporal (streaming) policy, as the decode
+// kernels' weight loads do.
+template <bool NT>
 __global__ __launch_bounds__(256) void read_kernel(const v4u* __restrict__ src, uint64_t n16,
                                                    uint32_t* __restrict__ sink) {
   const uint64_t stride = (uint64_t)gridDim.x * 256;
@@ -23,7 +26,8 @@ __global__ __launch_bounds__(256) void read_kernel(const v4u* __restrict__ src, 
   for (; i + 9 * stride < n16; i += 10 * stride) {
     v4u v[10];
 #pragma unroll
-    for (int u = 0; u < 10; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < 10; ++u)
+      v[u] = NT ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
 #pragma unroll
     for (int u = 0; u < 10; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
@@ -80,7 +84,15 @@ extern "C" {
 // workgroups of 256 threads; `sink` holds `grid` words.  0 or a hipError_t.
 int probe_stream_read(const void* src, uint64_t bytes, void* sink, int grid, void* stream) {
   if (!src || !sink || grid < 1 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(read_kernel<false>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const v4u*>(src), bytes / 16, static_cast<uint32_t*>(sink));
+  return (int)hipGetLastError();
+}
+
+// The same read with non-temporal loads.
+int probe_stream_read_nt(const void* src, uint64_t bytes, void* sink, int grid, void* stream) {
+  if (!src || !sink || grid < 1 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(read_kernel<true>, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                      static_cast<const v4u*>(src), bytes / 16, static_cast<uint32_t*>(sink));
   return (int)hipGetLastError();
 }
