@@ -296,8 +296,8 @@ bitlinear_status bitlinear_forward_noalloc(const void* X, bitlinear_dtype dtype,
  * (same bits either way).  `ws` (device, 16-byte aligned, at least
  * bitlinear_forward_q_workspace_bytes) enables that; NULL runs one workgroup
  * per tile.  Above 64 tokens, when 128 x 256 tiles outnumber the compute
- * units but fit on them at once (two per unit), those run instead, never cut
- * along K.  Every choice gives the same bits.  Up to four tokens (K <=
+ * units, fit on them at once (two per unit) and fill at least three
+ * quarters of those places, those run instead, never cut along K.  Every choice gives the same bits.  Up to four tokens (K <=
  * 12288) the one-launch decode kernel runs instead, with the rows copied
  * rather than quantized, and `ws` is not used.  Its first 4 KiB (counters) must be zero the first time a
  * workspace is used, and every call leaves them zero again; the rest needs

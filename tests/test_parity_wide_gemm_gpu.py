@@ -2,10 +2,11 @@
 workgroups per CU) with the CPU oracle, through the C ABI.
 
 The library takes these tiles for one layer above 64 tokens when they make
-one round that every CU joins: more 128x256 tiles than CUs, and no more than
-the CUs' resident slots (two per CU).  On a 256-CU MI355X the shapes below do:
-1024 x 8448 (264 tiles), 1000 x 8464 (272, ragged rows and a last column tile
-of 16 columns), 2048 x 6912 (432, the 2B prefill up projection).  Every output
+one round that every CU joins and that fills at least three quarters of the
+CUs' resident slots (two per CU).  On a 256-CU MI355X (512 slots) the shapes
+below do: 2048 x 6400 (400 tiles), 2000 x 6160 (400, ragged rows and a last
+column tile of 16 columns), 2048 x 6144 (384, the least that qualifies),
+2048 x 6912 (432, the 2B prefill up projection).  Every output
 element is compared on the smaller shapes, through the debug kernel (int32
 accumulators too) and the plain one (forward_q), with the plain, squared-ReLU
 and gated epilogues.  Expected values come only from the oracle.
@@ -77,9 +78,9 @@ def _weights(bl, orc, seed, N, K, dev, glu=False):
     return packed, gamma, qw, gc
 
 
-@pytest.mark.parametrize("M,K,N,kind,epi", [(1024, 256, 8448, "normal_bf16", None),
-                                            (1000, 512, 8464, "outlier_bf16", "relu2"),
-                                            (1024, 768, 8448, "student_t3_bf16", None)])
+@pytest.mark.parametrize("M,K,N,kind,epi", [(2048, 256, 6400, "normal_bf16", None),
+                                            (2000, 512, 6160, "outlier_bf16", "relu2"),
+                                            (2048, 768, 6144, "student_t3_bf16", None)])
 def test_wide_tiles_every_element(dev, bl, orc, M, K, N, kind, epi):
     packed, gamma, qw, gc = _weights(bl, orc, 20100 + N + K, N, K, dev)
     X, is_bf16 = wl.gen_acts(20200 + M + K, M, K, kind)
@@ -102,7 +103,7 @@ def test_wide_tiles_every_element(dev, bl, orc, M, K, N, kind, epi):
 
 
 def test_wide_tiles_gated_epilogue(dev, bl, orc):
-    M, K, N = 1024, 512, 8448
+    M, K, N = 2048, 512, 6400
     packed, gamma, qw, gc = _weights(bl, orc, 20300, N, K, dev, glu=True)
     X, _ = wl.gen_acts(20301, M, K, "normal_bf16")
     Xt = _acts_gpu(X, True, dev)
@@ -124,6 +125,22 @@ def test_wide_tiles_prefill_up_projection_every_tile(dev, bl, orc):
     M, K, N = 2048, 2560, 6912
     packed, gamma, qw, gc = _weights(bl, orc, 20400, N, K, dev)
     X, _ = wl.gen_acts(20401, M, K, "outlier_bf16")
+    Xq, sx, rs = bl.quantize_acts(_acts_gpu(X, True, dev))
+    Y = bl.forward_q(Xq, sx, rs, packed, gamma, N)
+    rows = np.unique(np.concatenate([np.arange(0, M, 128), np.arange(127, M, 128)]))
+    y_ref, *_ = orc.forward(X[rows], qw, gc, bf16=True)
+    y = Y.cpu().numpy()[rows]
+    assert _rel(y, y_ref) <= REL_TOL
+    assert np.array_equal(y, y_ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(512, 4096, 22016), (1536, 2560, 6912)])
+def test_fewer_wide_tiles_take_square_tiles(dev, bl, orc, M, K, N):
+    # 344 and 324 128x256 tiles fill under three quarters of the 512 slots,
+    # so these run on 128x128 tiles (688 and 648 of them, one round, no
+    # pieces): two rows of every 128-row tile, every column.
+    packed, gamma, qw, gc = _weights(bl, orc, 20500 + M, N, K, dev)
+    X, _ = wl.gen_acts(20501 + M, M, K, "student_t3_bf16")
     Xq, sx, rs = bl.quantize_acts(_acts_gpu(X, True, dev))
     Y = bl.forward_q(Xq, sx, rs, packed, gamma, N)
     rows = np.unique(np.concatenate([np.arange(0, M, 128), np.arange(127, M, 128)]))

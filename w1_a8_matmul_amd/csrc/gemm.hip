@@ -737,13 +737,18 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 // workgroups per CU), with the last partial round cut along K.  These beat
 // 64x128 and 64x256 tiles, deeper rings with shorter steps, and two-wave
 // workgroups.  The exception: when 128x256 tiles (4 waves of 64x128, two
-// workgroups per CU) make one round that every CU joins (more tiles than
-// CUs, no more than the resident slots), they are used instead.  A 64x128
-// wave tile reads half the activation bytes from LDS per multiply, and the
-// workgroup copies 24 KiB per step for 128 multiplies against 20 KiB for 64:
-// 2048 x 2560 -> 6912 (432 tiles) 34.5-34.8 us against 37.5-38.9 us.
-// Elsewhere they lost or tied: fewer tiles than CUs (2048 x 6912 -> 2560)
-// 46 against 38 us; 1.7 rounds (4096 x 2560 -> 6912) 69.6 against 67.1 us.
+// workgroups per CU) make one round that fills at least three quarters of
+// the resident slots (so every CU joins and few finish early with one tile),
+// they are used instead.  A 64x128 wave tile reads half the activation
+// bytes from LDS per multiply, and the workgroup copies 24 KiB per step for
+// 128 multiplies against 20 KiB for 64: 2048 x 2560 -> 6912 (432 tiles of
+// 512 slots) 33.9-35.1 us against 36.9-38.9 us.  With fewer tiles the CUs
+// left with one tile idle half the launch, and the 128x128 grid's finer
+// balance wins: 324 tiles (1536 x 2560 -> 6912) 29.0-30.2 against
+// 31.7-37.5 us, 344 (512 x 4096 -> 22016, 1024 x 4096 -> 11008) 42.5-46.6
+// against 45.2-50.7 us; 264 (1024 x 2560 -> 8448) tied.  Fewer tiles than
+// CUs (2048 x 6912 -> 2560): 46 against 38 us; 1.7 rounds
+// (4096 x 2560 -> 6912): 69.6 against 67.1 us.
 // They are never cut along K (a slot holds one 128x128 tile).  When the
 // 128x128 grid (pieces included) needs no more than two workgroups per CU,
 // a 3-stage ring (60 KiB, two steps of copies in flight) costs no
@@ -817,7 +822,8 @@ hipError_t bl_launch_gemm_q(const int8_t* Xq, const float* x_scale, const int32_
   const int64_t wide_tiles = ((M + WideCfg::BM - 1) / WideCfg::BM) *
                              ((N + WideCfg::BN - 1) / WideCfg::BN);
   const int cus = device_cus();
-  if (wide_tiles > cus && wide_tiles <= (int64_t)cus * resident_per_cu<2, 2, 2, 4, 2>())
+  const int64_t wide_slots = (int64_t)cus * resident_per_cu<2, 2, 2, 4, 2>();
+  if (wide_tiles > cus && wide_tiles <= wide_slots && 4 * wide_tiles >= 3 * wide_slots)
     return launch_cfg<2, 2, 2, 4, 2>(Xq, x_scale, x_rowsum, M, K, N, packed, gamma, Y, epi,
                                      acc_out, static_cast<int*>(gemm_ws), s);
   if (plan_grid(plan_tiles<128, 128>(M, K, N, gemm_ws != nullptr)) <= 2 * cus)
