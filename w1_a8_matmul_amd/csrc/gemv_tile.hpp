@@ -87,12 +87,21 @@ __device__ __forceinline__ void load_gains(const float* __restrict__ g, int K,
   }
 }
 
+// Position of natural dword d of an int8 row in the field-transposed LDS
+// layout: within each 64-byte group, dword 4j + f moves to 4f + j.
+__device__ __forceinline__ int xs_ft_dword(int d) {
+  return (d & ~15) | ((d & 3) << 2) | ((d >> 2) & 3);
+}
+
 // Quantizes one row held in registers into xs[0..K); the scale and row sum
 // go to s_scale / s_rowsum.  All NT threads take part.  With NORM and
 // gain_on, subln first: the codes are those of u = x * g and the scale
 // carries the row's RMS factor (from the double sum of x^2; red_d holds
-// NT/64 doubles of LDS).
-template <int DT, int NT, int KCH, bool NORM = false>
+// NT/64 doubles of LDS).  With FT (field-transposed), the four dwords of
+// each 16-column group are spread across the four 16-byte quarters of
+// their 64-column group: natural dword 4j + f of a 64-byte group is stored
+// at dword 4f + j (xs_ft_dword).
+template <int DT, int NT, int KCH, bool NORM = false, bool FT = false>
 __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int8_t* xs,
                                              float* red_f, int* red_i, float* s_scale,
                                              int* s_rowsum,
@@ -147,7 +156,13 @@ __device__ __forceinline__ void quantize_row(const Chunk<DT> ch[KCH], int K, int
         else
           hi |= ((uint32_t)q & 0xffu) << (8 * (i - 4));
       }
-      *reinterpret_cast<uint2*>(xs + k) = make_uint2(lo, hi);
+      if constexpr (FT) {
+        const int d = k >> 2;  // even: the pair d, d + 1 shares its group of 16 columns
+        reinterpret_cast<uint32_t*>(xs)[xs_ft_dword(d)] = lo;
+        reinterpret_cast<uint32_t*>(xs)[xs_ft_dword(d + 1)] = hi;
+      } else {
+        *reinterpret_cast<uint2*>(xs + k) = make_uint2(lo, hi);
+      }
     }
   }
   sum = wave_sum(sum);

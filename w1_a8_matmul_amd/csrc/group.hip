@@ -38,13 +38,41 @@ constexpr int kSegTiles = kGroupSegTiles;
 
 // One 1 KiB block of a 16-row tile on the matrix cores.  Lane l loaded
 // row l%16 of the tile, columns 64q .. 64q+63 of the block (q = l/16), as
-// four words; word w holds the codes of columns 64q + 16w .. +15.  MFMA w
-// contracts, for every lane, those 16 columns of tile row l%16 (B) with the
-// same 16 columns of token row l%16 (A, 16 bytes from LDS): the four MFMAs
-// together cover the block's 256 columns for all 16 x 16 (token, row)
-// pairs.  Two accumulators halve the dependent chain.
-__device__ __forceinline__ void mfma_block(const uint4 w, const int8_t* xa, v4i& acc0,
-                                           v4i& acc1) {
+// four words; word j holds the codes of columns 64q + 16j .. +15, field f of
+// its byte b being column 64q + 16j + 4f + b.  MFMA f takes field f of all
+// four words, left in place (codes times 1, 4 or 16; field 3 shifted down
+// to times 1), so each operand costs one AND (two for field 3) instead of a
+// shift and an AND per field.  Its 16 activation bytes are columns
+// 64q + 16j + 4f .. +3 for j = 0..3, which the field-transposed LDS row
+// (xs_ft_dword) keeps as one 16-byte read at 16f.  The four MFMAs cover the
+// block's 256 columns for all 16 x 16 (token, row) pairs; acc4 and acc16
+// hold 4 and 16 times their fields' sums (exact multiples, well inside int32
+// for K <= 12288), so the tile's sum is acc1 + acc4 / 4 + acc16 / 16, taken
+// with arithmetic shifts at the tile's end.
+__device__ __forceinline__ void mfma_block(const uint4 w, const int8_t* xa, v4i& acc1,
+                                           v4i& acc4, v4i& acc16) {
+  auto operand = [&](uint32_t mask) {
+    return v4i{(int)(w.x & mask), (int)(w.y & mask), (int)(w.z & mask), (int)(w.w & mask)};
+  };
+  const v4i* a = reinterpret_cast<const v4i*>(xa);
+  acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], operand(kCodeMask), acc1, 0, 0, 0);
+  acc4 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[1], operand(kCodeMask << 2), acc4, 0, 0, 0);
+  acc16 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2], operand(kCodeMask << 4), acc16, 0, 0, 0);
+  const v4i b3 = v4i{(int)((w.x >> 6) & kCodeMask), (int)((w.y >> 6) & kCodeMask),
+                     (int)((w.z >> 6) & kCodeMask), (int)((w.w >> 6) & kCodeMask)};
+  acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[3], b3, acc1, 0, 0, 0);
+}
+
+// The same block with the activation row in natural order: MFMA j takes
+// word j, its four fields shifted down (dword f = field f, columns
+// 64q + 16j + 4f .. +3) against the 16 activation bytes at 16j; two
+// accumulators halve the dependent chain.  Seven VALU operations per word
+// against five, but fewer registers: the multi-row inline quantization
+// (two or three tokens) keeps three waves per SIMD with it, and drops to two
+// with the in-place fields (2B step at M = 2: 101.7-105.1 against
+// 104.5-106.5 us).
+__device__ __forceinline__ void mfma_block_shifted(const uint4 w, const int8_t* xa, v4i& acc0,
+                                                   v4i& acc1) {
   const uint32_t words[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -140,6 +168,9 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
   constexpr int kWaves = NT / kWave;
   constexpr int C = kChunk;
   constexpr int kBlockCols = B3 ? kB3TileCols : kTileCols;  // columns per 1 KiB block
+  // Field-transposed activation rows and the in-place field MFMAs, except
+  // for the base-3 layout and the multi-row inline quantization.
+  constexpr bool FT = !B3 && !MR;
   const int K = o.K;
   const int kblocks = B3 ? (K + kB3TileCols - 1) / kB3TileCols : K / kTileCols;
   const int nc = (kblocks + C - 1) / C;
@@ -199,7 +230,15 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
           const int i = b0 + u * kThreads + (int)threadIdx.x;
           if (i < n16) {
             const int m = i / row16, c = i - m * row16;
-            *reinterpret_cast<uint4*>(xs + m * xstride + c * 16) = v[u];
+            if constexpr (!FT) {
+              *reinterpret_cast<uint4*>(xs + m * xstride + c * 16) = v[u];
+            } else {  // field-transposed: dword 4c + t of the row goes to xs_ft_dword
+              uint32_t* row = reinterpret_cast<uint32_t*>(xs + m * xstride);
+              row[xs_ft_dword(4 * c)] = v[u].x;
+              row[xs_ft_dword(4 * c + 1)] = v[u].y;
+              row[xs_ft_dword(4 * c + 2)] = v[u].z;
+              row[xs_ft_dword(4 * c + 3)] = v[u].w;
+            }
           }
         }
       }
@@ -223,7 +262,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
     load_row<DT, kThreads, KCH>(o.X, 1, K, nx, M > 1);
     issue(bufA, 0, qi);
     auto quant = [&](const Chunk<DT>(&c)[KCH], int m) {
-      quantize_row<DT, kThreads, KCH, NORM>(c, K, xs + m * xstride, sm.red_f, sm.red_i, s_sx + m,
+      quantize_row<DT, kThreads, KCH, NORM, FT>(c, K, xs + m * xstride, sm.red_f, sm.red_i, s_sx + m,
                                             s_rs + m, &gn, gain_on, o.norm_eps, sm.red_d);
     };
     quant(ch, 0);
@@ -239,12 +278,12 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
     if constexpr (NORM) load_gains<kThreads, KCH>(o.norm_gain, K, gn);
     const bool gain_on = NORM && o.norm_gain != nullptr;
     issue(bufA, 0, qi);
-    quantize_row<DT, kThreads, KCH, NORM>(ch, K, xs, sm.red_f, sm.red_i, s_sx, s_rs, &gn,
+    quantize_row<DT, kThreads, KCH, NORM, FT>(ch, K, xs, sm.red_f, sm.red_i, s_sx, s_rs, &gn,
                                           gain_on, o.norm_eps, sm.red_d);
     for (int m = 1; m < M; ++m) {
       Chunk<DT> chm[KCH];
       load_row<DT, kThreads, KCH>(o.X, m, K, chm);
-      quantize_row<DT, kThreads, KCH, NORM>(chm, K, xs + m * xstride, sm.red_f, sm.red_i,
+      quantize_row<DT, kThreads, KCH, NORM, FT>(chm, K, xs + m * xstride, sm.red_f, sm.red_i,
                                             s_sx + m, s_rs + m, &gn, gain_on, o.norm_eps,
                                             sm.red_d);
     }
@@ -256,7 +295,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
 
   const float gamma = *o.gamma;
   const int8_t* xrow = xs + arow * xstride + q16 * (kBlockCols / 4);
-  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
+  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0}, acc2 = v4i{0, 0, 0, 0};
 
   // D layout: lane l holds tile row l%16 and tokens 4*(l/16) + r, r = 0..3.
   auto consume = [&](const uint4 (&buf)[C], int j, Cursor& q) {
@@ -265,11 +304,13 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
       const int b = min(q.c * C + i, kblocks - 1);  // past the end: zero codes, any x
       if constexpr (B3)
         mfma_block_b3(buf[i], xrow + b * kBlockCols, acc0, acc1);
+      else if constexpr (FT)
+        mfma_block(buf[i], xrow + b * kBlockCols, acc0, acc1, acc2);
       else
-        mfma_block(buf[i], xrow + b * kBlockCols, acc0, acc1);
+        mfma_block_shifted(buf[i], xrow + b * kBlockCols, acc0, acc1);
     }
     if (q.c == nc - 1) {
-      const v4i d = acc0 + acc1;
+      const v4i d = FT ? acc0 + (acc1 >> 2) + (acc2 >> 4) : acc0 + acc1;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = 4 * q16 + r;
@@ -279,6 +320,7 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
       }
       acc0 = v4i{0, 0, 0, 0};
       acc1 = v4i{0, 0, 0, 0};
+      acc2 = v4i{0, 0, 0, 0};
     }
     advance(q);
   };
