@@ -767,8 +767,9 @@ hipError_t launch_cfg(const int8_t* Xq, const float* sx, const int32_t* rs, int6
 // MFMAs (as 32x128 waves, one): 508-513 against 557-563 us, and the 2B step
 // at M = 64 248 against 250 us.  (4 waves of 64x128 in 64x512 tiles: 538
 // and 230 us.)  A 3-stage ring (48 KiB, three workgroups per CU) then
-// gains: 519-524 against 534-550 us, 2B step 225 against 251 us.  Above 64 tokens, the 128x256 tiles: 7B step at M = 512
-// 3157-3195 against 3382 us with 128x128 tiles.
+// gains: 519-524 against 534-550 us, 2B step 225 against 251 us.  Above 64
+// tokens, the 128x256 tiles: 7B step at M = 512 3157-3195 against 3382 us
+// with 128x128 tiles.
 using WideCfg = Tile<2, 2, 2, 4, 2>;
 using GroupSmallCfg = Tile<1, 4, 2, 2, 3>;
 constexpr int kSmallM = 64;

@@ -262,8 +262,9 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
     load_row<DT, kThreads, KCH>(o.X, 1, K, nx, M > 1);
     issue(bufA, 0, qi);
     auto quant = [&](const Chunk<DT>(&c)[KCH], int m) {
-      quantize_row<DT, kThreads, KCH, NORM, FT>(c, K, xs + m * xstride, sm.red_f, sm.red_i, s_sx + m,
-                                            s_rs + m, &gn, gain_on, o.norm_eps, sm.red_d);
+      quantize_row<DT, kThreads, KCH, NORM, FT>(c, K, xs + m * xstride, sm.red_f, sm.red_i,
+                                                s_sx + m, s_rs + m, &gn, gain_on, o.norm_eps,
+                                                sm.red_d);
     };
     quant(ch, 0);
     load_row<DT, kThreads, KCH>(o.X, 2, K, ch, M > 2);
@@ -279,13 +280,13 @@ __device__ __forceinline__ void run_segment(const GroupOp& o, int M, int first, 
     const bool gain_on = NORM && o.norm_gain != nullptr;
     issue(bufA, 0, qi);
     quantize_row<DT, kThreads, KCH, NORM, FT>(ch, K, xs, sm.red_f, sm.red_i, s_sx, s_rs, &gn,
-                                          gain_on, o.norm_eps, sm.red_d);
+                                              gain_on, o.norm_eps, sm.red_d);
     for (int m = 1; m < M; ++m) {
       Chunk<DT> chm[KCH];
       load_row<DT, kThreads, KCH>(o.X, m, K, chm);
       quantize_row<DT, kThreads, KCH, NORM, FT>(chm, K, xs + m * xstride, sm.red_f, sm.red_i,
-                                            s_sx + m, s_rs + m, &gn, gain_on, o.norm_eps,
-                                            sm.red_d);
+                                                s_sx + m, s_rs + m, &gn, gain_on, o.norm_eps,
+                                                sm.red_d);
     }
   } else {
     issue(bufA, 0, qi);
